@@ -1,0 +1,14 @@
+"""Seeded synthetic inputs for causal attention, shared by the tests and the benchmark.
+
+This module holds no attention arithmetic: it draws tensors, rounds them to the
+input dtype and lays out packed-document boundaries.  Both the fp64 oracle and
+the HIP path receive the arrays it returns.
+"""
+from .synth import (  # noqa: F401
+    CONFIGS,
+    AttnConfig,
+    round_to_bf16,
+    make_cu_seqlens,
+    make_inputs,
+    allowed_pair_count,
+)
