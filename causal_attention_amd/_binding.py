@@ -1,0 +1,253 @@
+"""ctypes binding of libcausal_attn.so (include/attn_api.h).
+
+Argument marshalling only: every function here checks that the torch tensors
+it is given match the C ABI's layout contract, passes their device pointers
+and the current HIP stream to the library, and raises on a non-zero status.
+All arithmetic runs in the library's HIP kernels; if the library is missing
+this module raises instead of computing anything itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libcausal_attn.so")
+HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "attn_api.h")
+
+ATTN_OK = 0
+ATTN_MASK_CAUSAL = 0
+ATTN_MASK_DOC_CAUSAL = 1
+ATTN_DTYPE_F32 = 0
+ATTN_DTYPE_BF16 = 1
+
+STATUS_NAMES = {
+    0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEAD_DIM",
+    -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_MASK", -6: "ATTN_ERR_SEQLENS", -7: "ATTN_ERR_HIP",
+    -8: "ATTN_ERR_UNIMPLEMENTED", -9: "ATTN_ERR_SCALE",
+}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+# argtypes of every exported function, in the header's order
+SIGNATURES = {
+    "attn_fwd": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
+    "attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
+    "attn_bwd_preprocess": [_P, _P, _P, _I, _I, _I, _I, _I, _P],
+    "attn_bwd_dkdv": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
+    "attn_bwd_dq": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
+    "attn_status_string": [_I],
+    "attn_abi_version": [],
+}
+
+_lib = None
+
+
+def header_functions(path: str = HEADER_PATH):
+    """Names of the functions declared in include/attn_api.h."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?(?:int|char|void)\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} not found: build the HIP library first "
+            "(python -m causal_attention_amd.build or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    for name, args in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "attn_status_string" else ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        raise AttnError(status, status_string(status))
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return ATTN_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return ATTN_DTYPE_F32
+    raise TypeError(f"unsupported input dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t, name, shape=None, dtype=None, device=None):
+    if t is None:
+        return None
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    del torch
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _mask_args(mask_mode, cu_seqlens, n_seqs, max_seqlen, device):
+    torch = _torch()
+    if mask_mode == ATTN_MASK_DOC_CAUSAL:
+        if cu_seqlens is None:
+            raise ValueError("packed-document mode needs cu_seqlens")
+        cu_ptr = _ptr(cu_seqlens, "cu_seqlens", dtype=torch.int32, device=device)
+        if n_seqs is None:
+            n_seqs = cu_seqlens.numel() - 1
+        if max_seqlen is None:
+            raise ValueError("packed-document mode needs max_seqlen (host integer)")
+        return cu_ptr, int(n_seqs), int(max_seqlen)
+    return None, 0, 0
+
+
+def _qkv_info(q, k, v):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, S, D]")
+    B, H, S, D = q.shape
+    for name, t in (("k", k), ("v", v)):
+        if tuple(t.shape) != (B, H, S, D) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    return B, H, S, D, _dtype_code(q)
+
+
+def attn_fwd(q, k, v, o, lse, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None, n_seqs=None,
+             max_seqlen=None, stream=None):
+    """Enqueue the forward: o [B,H,S,D] fp32 and lse [B,H,S] fp32 (or None)."""
+    torch = _torch()
+    lib = load_library()
+    B, H, S, D, dt = _qkv_info(q, k, v)
+    dev = q.device
+    cu, ns, ms = _mask_args(mask_mode, cu_seqlens, n_seqs, max_seqlen, dev)
+    _check(lib.attn_fwd(
+        _ptr(q, "q", device=dev), _ptr(k, "k", device=dev), _ptr(v, "v", device=dev),
+        _ptr(o, "o", (B, H, S, D), torch.float32, dev), _ptr(lse, "lse", (B, H, S), torch.float32, dev),
+        B, H, S, D, float(scale), int(mask_mode), cu, ns, ms, dt, _stream(stream)))
+
+
+def attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None,
+             n_seqs=None, max_seqlen=None, stream=None):
+    """Enqueue the backward: dq, dk, dv [B,H,S,D] fp32; delta [B,H,S] fp32 workspace."""
+    torch = _torch()
+    lib = load_library()
+    B, H, S, D, dt = _qkv_info(q, k, v)
+    dev = q.device
+    cu, ns, ms = _mask_args(mask_mode, cu_seqlens, n_seqs, max_seqlen, dev)
+    f32 = torch.float32
+    _check(lib.attn_bwd(
+        _ptr(q, "q", device=dev), _ptr(k, "k", device=dev), _ptr(v, "v", device=dev),
+        _ptr(o, "o", (B, H, S, D), f32, dev), _ptr(dO, "dO", (B, H, S, D), q.dtype, dev),
+        _ptr(lse, "lse", (B, H, S), f32, dev), _ptr(dq, "dq", (B, H, S, D), f32, dev),
+        _ptr(dk, "dk", (B, H, S, D), f32, dev), _ptr(dv, "dv", (B, H, S, D), f32, dev),
+        _ptr(delta, "delta", (B, H, S), f32, dev),
+        B, H, S, D, float(scale), int(mask_mode), cu, ns, ms, dt, _stream(stream)))
+
+
+def attn_bwd_preprocess(o, dO, delta, stream=None):
+    torch = _torch()
+    lib = load_library()
+    B, H, S, D = dO.shape
+    dev = dO.device
+    _check(lib.attn_bwd_preprocess(
+        _ptr(o, "o", (B, H, S, D), torch.float32, dev), _ptr(dO, "dO", device=dev),
+        _ptr(delta, "delta", (B, H, S), torch.float32, dev), B, H, S, D, _dtype_code(dO), _stream(stream)))
+
+
+def attn_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None,
+                  n_seqs=None, max_seqlen=None, stream=None):
+    torch = _torch()
+    lib = load_library()
+    B, H, S, D, dt = _qkv_info(q, k, v)
+    dev = q.device
+    cu, ns, ms = _mask_args(mask_mode, cu_seqlens, n_seqs, max_seqlen, dev)
+    f32 = torch.float32
+    _check(lib.attn_bwd_dkdv(
+        _ptr(q, "q", device=dev), _ptr(k, "k", device=dev), _ptr(v, "v", device=dev),
+        _ptr(dO, "dO", (B, H, S, D), q.dtype, dev), _ptr(lse, "lse", (B, H, S), f32, dev),
+        _ptr(delta, "delta", (B, H, S), f32, dev), _ptr(dk, "dk", (B, H, S, D), f32, dev),
+        _ptr(dv, "dv", (B, H, S, D), f32, dev),
+        B, H, S, D, float(scale), int(mask_mode), cu, ns, ms, dt, _stream(stream)))
+
+
+def attn_bwd_dq(q, k, v, dO, lse, delta, dq, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None,
+                n_seqs=None, max_seqlen=None, stream=None):
+    torch = _torch()
+    lib = load_library()
+    B, H, S, D, dt = _qkv_info(q, k, v)
+    dev = q.device
+    cu, ns, ms = _mask_args(mask_mode, cu_seqlens, n_seqs, max_seqlen, dev)
+    f32 = torch.float32
+    _check(lib.attn_bwd_dq(
+        _ptr(q, "q", device=dev), _ptr(k, "k", device=dev), _ptr(v, "v", device=dev),
+        _ptr(dO, "dO", (B, H, S, D), q.dtype, dev), _ptr(lse, "lse", (B, H, S), f32, dev),
+        _ptr(delta, "delta", (B, H, S), f32, dev), _ptr(dq, "dq", (B, H, S, D), f32, dev),
+        B, H, S, D, float(scale), int(mask_mode), cu, ns, ms, dt, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Allocating conveniences (torch supplies the device memory).
+
+def forward(q, k, v, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None, max_seqlen=None, stream=None):
+    """Returns (o, lse) as new fp32 device tensors."""
+    torch = _torch()
+    B, H, S, D = q.shape
+    o = torch.empty((B, H, S, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    attn_fwd(q, k, v, o, lse, scale, mask_mode, cu_seqlens, None, max_seqlen, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, dO, lse, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None, max_seqlen=None,
+             stream=None):
+    """Returns (dq, dk, dv, delta) as new fp32 device tensors."""
+    torch = _torch()
+    B, H, S, D = q.shape
+    dq = torch.empty((B, H, S, D), dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode, cu_seqlens, None, max_seqlen, stream)
+    return dq, dk, dv, delta

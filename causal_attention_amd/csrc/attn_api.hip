@@ -1,0 +1,174 @@
+// attn_api.hip - the C ABI (include/attn_api.h): argument checks and launches.
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime, then enqueues the kernels on the caller's stream and returns.
+// Nothing here allocates, frees, copies or synchronises.
+#include <cmath>
+#include <cstdint>
+
+#include "attn_api.h"
+#include "attn_launch.h"
+
+namespace {
+
+constexpr int kAbiVersion = 100;  // 1.00
+
+int check_common(int B, int H, int S, int D, int dtype) {
+  if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  if (D != 32 && D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (B < 1 || H < 1 || S < 1) return ATTN_ERR_SHAPE;
+  const int64_t elems = (int64_t)B * H * S * D;
+  if (elems >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+int check_mask(int B, int H, int S, int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen) {
+  if (mask_mode == ATTN_MASK_CAUSAL) return ATTN_OK;
+  if (mask_mode != ATTN_MASK_DOC_CAUSAL) return ATTN_ERR_MASK;
+  if (cu_seqlens == nullptr) return ATTN_ERR_NULL;
+  if (B != 1 || n_seqs < 1 || n_seqs > S || n_seqs > 65535 || H > 65535) return ATTN_ERR_SEQLENS;
+  if (max_seqlen < 1 || max_seqlen > S) return ATTN_ERR_SEQLENS;
+  return ATTN_OK;
+}
+
+int check_scale(float scale) {
+  if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_SCALE;
+  return ATTN_OK;
+}
+
+attn::Args make_args(int B, int H, int S, int D, float scale, int mask_mode, const int32_t *cu_seqlens,
+                     int n_seqs, int max_seqlen, int dtype, void *stream) {
+  attn::Args a{};
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.D = D;
+  a.scale = scale;
+  a.doc = mask_mode == ATTN_MASK_DOC_CAUSAL;
+  a.cu_seqlens = cu_seqlens;
+  a.n_seqs = n_seqs;
+  a.max_seqlen = max_seqlen;
+  a.bf16 = dtype == ATTN_DTYPE_BF16;
+  a.stream = static_cast<hipStream_t>(stream);
+  return a;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return kAbiVersion; }
+
+const char *attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "B, H or S out of range (each >= 1, B*H*S*D < 2^31)";
+    case ATTN_ERR_HEAD_DIM: return "head dimension D must be 32, 64 or 128";
+    case ATTN_ERR_DTYPE: return "unknown input dtype (ATTN_DTYPE_F32 or ATTN_DTYPE_BF16)";
+    case ATTN_ERR_MASK: return "unknown mask mode (ATTN_MASK_CAUSAL or ATTN_MASK_DOC_CAUSAL)";
+    case ATTN_ERR_SEQLENS: return "packed-document mode needs B == 1, 1 <= n_seqs <= S and 1 <= max_seqlen <= S";
+    case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case ATTN_ERR_UNIMPLEMENTED: return "not implemented in this build";
+    case ATTN_ERR_SCALE: return "scale must be finite and > 0";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int S, int D,
+             float scale, int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype,
+             void *stream) {
+  int st = check_common(B, H, S, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+  if ((st = check_mask(B, H, S, mask_mode, cu_seqlens, n_seqs, max_seqlen)) != ATTN_OK) return st;
+  if ((st = check_scale(scale)) != ATTN_OK) return st;
+  attn::Args a = make_args(B, H, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  return to_status(attn::launch_fwd(a));
+}
+
+int attn_bwd_preprocess(const float *o, const void *dO, float *delta, int B, int H, int S, int D, int dtype,
+                        void *stream) {
+  int st = check_common(B, H, S, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (!o || !dO || !delta) return ATTN_ERR_NULL;
+  attn::Args a = make_args(B, H, S, D, 1.f, ATTN_MASK_CAUSAL, nullptr, 0, 0, dtype, stream);
+  a.o_in = o;
+  a.dO = dO;
+  a.delta = delta;
+  return to_status(attn::launch_bwd_preprocess(a));
+}
+
+int attn_bwd_dkdv(const void *q, const void *k, const void *v, const void *dO, const float *lse,
+                  const float *delta, float *dk, float *dv, int B, int H, int S, int D, float scale, int mask_mode,
+                  const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype, void *stream) {
+  int st = check_common(B, H, S, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (!q || !k || !v || !dO || !lse || !delta || !dk || !dv) return ATTN_ERR_NULL;
+  if ((st = check_mask(B, H, S, mask_mode, cu_seqlens, n_seqs, max_seqlen)) != ATTN_OK) return st;
+  if ((st = check_scale(scale)) != ATTN_OK) return st;
+  attn::Args a = make_args(B, H, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dO = dO;
+  a.lse_in = lse;
+  a.delta_in = delta;
+  a.dk = dk;
+  a.dv = dv;
+  return to_status(attn::launch_bwd_dkdv(a));
+}
+
+int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dO, const float *lse, const float *delta,
+                float *dq, int B, int H, int S, int D, float scale, int mask_mode, const int32_t *cu_seqlens,
+                int n_seqs, int max_seqlen, int dtype, void *stream) {
+  int st = check_common(B, H, S, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (!q || !k || !v || !dO || !lse || !delta || !dq) return ATTN_ERR_NULL;
+  if ((st = check_mask(B, H, S, mask_mode, cu_seqlens, n_seqs, max_seqlen)) != ATTN_OK) return st;
+  if ((st = check_scale(scale)) != ATTN_OK) return st;
+  attn::Args a = make_args(B, H, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dO = dO;
+  a.lse_in = lse;
+  a.delta_in = delta;
+  a.dq = dq;
+  return to_status(attn::launch_bwd_dq(a));
+}
+
+int attn_bwd(const void *q, const void *k, const void *v, const float *o, const void *dO, const float *lse,
+             float *dq, float *dk, float *dv, float *delta, int B, int H, int S, int D, float scale, int mask_mode,
+             const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype, void *stream) {
+  int st = check_common(B, H, S, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL;
+  if ((st = check_mask(B, H, S, mask_mode, cu_seqlens, n_seqs, max_seqlen)) != ATTN_OK) return st;
+  if ((st = check_scale(scale)) != ATTN_OK) return st;
+  attn::Args a = make_args(B, H, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dO = dO;
+  a.o_in = o;
+  a.lse_in = lse;
+  a.delta = delta;
+  a.delta_in = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  hipError_t e = attn::launch_bwd_preprocess(a);
+  if (e == hipSuccess) e = attn::launch_bwd_dkdv(a);
+  if (e == hipSuccess) e = attn::launch_bwd_dq(a);
+  return to_status(e);
+}
+
+}  // extern "C"

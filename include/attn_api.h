@@ -1,0 +1,141 @@
+/*
+ * attn_api.h - C ABI of the fused causal scaled-dot-product attention library
+ * (libcausal_attn.so), forward and backward, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For every batch b and head h, with queries and keys the
+ * same sequence of S tokens and head dimension D:
+ *
+ *   S_ij   = scale * sum_d Q_id K_jd           (ARK: multi-head SDPA attention)
+ *   S_ij   = -inf unless key j is allowed      (ARK: causal mask fused into the SDPA)
+ *   P      = softmax over j of S (per row i)
+ *   O      = P V,  LSE_i = ln sum_j exp(S_ij)  (natural log)
+ *
+ * and, given the upstream gradient dO, the analytic backward
+ *
+ *   Delta_i = sum_d dO_id O_id,  dP = dO V^T,  dS = P o (dP - Delta)
+ *   dQ = scale * dS K,  dK = scale * dS^T Q,  dV = P^T dO
+ *
+ * computed flash-attention style (Forge, "What this is" and "Acknowledgements":
+ * forward and backward after FlashAttention-2): the forward keeps a running
+ * row maximum and sum and stores only O and LSE; the backward recomputes P from
+ * LSE tile by tile.  No S x S matrix is ever stored.
+ *
+ * Masks.
+ *   ATTN_MASK_CAUSAL:     key j allowed for query i iff j <= i.
+ *   ATTN_MASK_DOC_CAUSAL: packed documents (Cort33x, "Preserving context in
+ *     the data"): the sequence is the concatenation of n_seqs documents with
+ *     boundaries cu_seqlens[0] = 0 < cu_seqlens[1] < ... < cu_seqlens[n_seqs] = S;
+ *     key j allowed for query i iff j <= i and both lie in the same document.
+ *
+ * Layout.  Q, K, V, dO, O, dQ, dK, dV are contiguous [B, H, S, D] row-major
+ * (D fastest); LSE and Delta are contiguous [B, H, S].  In DOC_CAUSAL mode
+ * B must be 1.  Q, K, V and dO share one input dtype (ATTN_DTYPE_*); O, LSE,
+ * Delta, dQ, dK and dV are always float32.
+ *
+ * Ownership.  Every pointer except where noted is a DEVICE pointer on the
+ * current HIP device, allocated and owned by the caller.  The library never
+ * allocates, frees, copies between host and device or synchronises; it keeps
+ * no state between calls and is safe to call from several threads.
+ * Outputs are fully overwritten (no accumulation, no need to clear them first).
+ *
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls
+ * return after enqueueing; results are valid once the stream has completed.
+ *
+ * Errors.  Arguments are validated before any HIP call; an invalid call
+ * returns a negative attn_status and touches no memory.  A failed kernel
+ * launch returns ATTN_ERR_HIP.  The library never aborts and never throws.
+ * The contents of device cu_seqlens are NOT validated (that would need a
+ * synchronisation); a malformed array gives unspecified results.
+ *
+ * Supported: D in {32, 64, 128}; S >= 1; B, H >= 1; B*H*S*D < 2^31;
+ * scale finite and > 0.
+ */
+#ifndef CAUSAL_ATTN_API_H
+#define CAUSAL_ATTN_API_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,          /* a required pointer is NULL                       */
+  ATTN_ERR_SHAPE = -2,         /* B, H or S out of range, or sizes overflow        */
+  ATTN_ERR_HEAD_DIM = -3,      /* D not in {32, 64, 128}                           */
+  ATTN_ERR_DTYPE = -4,         /* unknown input dtype                              */
+  ATTN_ERR_MASK = -5,          /* unknown mask mode                                */
+  ATTN_ERR_SEQLENS = -6,       /* DOC_CAUSAL with B != 1, n_seqs < 1, bad max_seqlen */
+  ATTN_ERR_HIP = -7,           /* a HIP runtime call or kernel launch failed       */
+  ATTN_ERR_UNIMPLEMENTED = -8, /* valid request this build does not implement      */
+  ATTN_ERR_SCALE = -9          /* scale not finite or not > 0                      */
+} attn_status;
+
+enum { ATTN_MASK_CAUSAL = 0, ATTN_MASK_DOC_CAUSAL = 1 };
+enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 };
+
+/*
+ * Forward.  Reads q, k, v [B,H,S,D] (dtype), writes o [B,H,S,D] float32 and,
+ * unless lse is NULL, lse [B,H,S] float32 (natural-log logsumexp of each
+ * row's scaled, masked scores; the backward needs it).
+ * cu_seqlens: device int32 [n_seqs+1], used only in DOC_CAUSAL mode (may be
+ * NULL otherwise); n_seqs and max_seqlen (the longest document, 1..S) are
+ * host integers used to size the launch, ignored in CAUSAL mode.
+ */
+int attn_fwd(const void *q, const void *k, const void *v, float *o, float *lse,
+             int B, int H, int S, int D, float scale, int mask_mode,
+             const int32_t *cu_seqlens, int n_seqs, int max_seqlen,
+             int dtype, void *stream);
+
+/*
+ * Backward.  Reads q, k, v, dO (dtype), o and lse (float32, from attn_fwd
+ * with the same arguments) and writes dq, dk, dv [B,H,S,D] float32.
+ * delta: caller-owned float32 workspace of B*H*S elements; on return it holds
+ * Delta_i = sum_d dO_id O_id.  Runs the three stages below in order on
+ * `stream`.
+ */
+int attn_bwd(const void *q, const void *k, const void *v, const float *o,
+             const void *dO, const float *lse, float *dq, float *dk, float *dv,
+             float *delta, int B, int H, int S, int D, float scale, int mask_mode,
+             const int32_t *cu_seqlens, int n_seqs, int max_seqlen,
+             int dtype, void *stream);
+
+/*
+ * The backward's stages, exported separately so that callers (and timing
+ * harnesses) can schedule or measure them one by one.  attn_bwd is exactly
+ * attn_bwd_preprocess, then attn_bwd_dkdv, then attn_bwd_dq; the last two
+ * both need only the first and may run in either order.
+ *
+ * attn_bwd_preprocess: delta[B*H*S] = rowsum(dO o O).  S, D, dtype as above.
+ * attn_bwd_dkdv: dk, dv from q, k, v, dO, lse, delta (loops over query tiles
+ *   for each key tile).
+ * attn_bwd_dq: dq from q, k, v, dO, lse, delta (loops over key tiles for
+ *   each query tile).
+ */
+int attn_bwd_preprocess(const float *o, const void *dO, float *delta,
+                        int B, int H, int S, int D, int dtype, void *stream);
+
+int attn_bwd_dkdv(const void *q, const void *k, const void *v, const void *dO,
+                  const float *lse, const float *delta, float *dk, float *dv,
+                  int B, int H, int S, int D, float scale, int mask_mode,
+                  const int32_t *cu_seqlens, int n_seqs, int max_seqlen,
+                  int dtype, void *stream);
+
+int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dO,
+                const float *lse, const float *delta, float *dq,
+                int B, int H, int S, int D, float scale, int mask_mode,
+                const int32_t *cu_seqlens, int n_seqs, int max_seqlen,
+                int dtype, void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *attn_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CAUSAL_ATTN_API_H */

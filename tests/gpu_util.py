@@ -1,0 +1,100 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, run the HIP path through
+the C ABI, compare against the fp64 oracle with the stated tolerances."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import causal_attention_amd as ca
+from oracle import attention_bwd_ref
+
+# Tolerances: fp32 inputs, max-abs 1e-4 on every output; bf16 inputs, max-abs
+# 2e-2 and relative Frobenius error 1e-2 per tensor (O, dQ, dK, dV), LSE 1e-3.
+TOL = {
+    "f32": dict(max_abs=1e-4, rel_fro=None, lse=1e-4),
+    "bf16": dict(max_abs=2e-2, rel_fro=1e-2, lse=1e-3),
+}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(x):
+    import torch
+    dt = torch.bfloat16 if x["dtype"] == "bf16" else torch.float32
+    dev = {n: torch.from_numpy(np.ascontiguousarray(x[n])).to("cuda").to(dt).contiguous()
+           for n in ("q", "k", "v", "do")}
+    cu = x.get("cu_seqlens")
+    if cu is not None:
+        dev["cu"] = torch.from_numpy(np.asarray(cu, dtype=np.int32)).to("cuda")
+        dev["max_seqlen"] = int(np.diff(cu).max())
+    else:
+        dev["cu"] = None
+        dev["max_seqlen"] = None
+    return dev
+
+
+def run_hip(x, dev=None, poison=True, stream=None):
+    """Forward + backward on the GPU.  Outputs are NaN-poisoned first, so an
+    element the kernels fail to write shows up as NaN.  Returns torch tensors."""
+    import torch
+    if dev is None:
+        dev = to_device(x)
+    B, H, S, D = x["B"], x["H"], x["S"], x["D"]
+    fill = float("nan") if poison else 0.0
+    f32 = dict(dtype=torch.float32, device="cuda")
+    out = {n: torch.full((B, H, S, D), fill, **f32) for n in ("o", "dq", "dk", "dv")}
+    out["lse"] = torch.full((B, H, S), fill, **f32)
+    out["delta"] = torch.full((B, H, S), fill, **f32)
+    mode = x["mask_mode"]
+    ca.attn_fwd(dev["q"], dev["k"], dev["v"], out["o"], out["lse"], x["scale"], mode, dev["cu"], None,
+                dev["max_seqlen"], stream)
+    ca.attn_bwd(dev["q"], dev["k"], dev["v"], out["o"], dev["do"], out["lse"], out["dq"], out["dk"], out["dv"],
+                out["delta"], x["scale"], mode, dev["cu"], None, dev["max_seqlen"], stream)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle(x, heads=None):
+    args = [x[n].astype(np.float64) for n in ("q", "k", "v", "do")]
+    return attention_bwd_ref(*args, x["scale"], x["mask_mode"], x.get("cu_seqlens"), heads=heads)
+
+
+def errors(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    max_abs = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    denom = float(np.linalg.norm(ref))
+    rel_fro = float(np.linalg.norm(got - ref) / denom) if denom > 0 else float(np.linalg.norm(got - ref))
+    return max_abs, rel_fro
+
+
+def compare(out, ref, dtype, heads=None, names=("o", "lse", "dq", "dk", "dv", "delta"), tag="",
+            max_abs_scale=1.0):
+    """Assert the GPU outputs match the oracle on the given heads (all if None)."""
+    tol = TOL[dtype]
+    report = {}
+    for name in names:
+        g = out[name].detach().cpu().numpy().astype(np.float64)
+        r = ref[name]
+        if heads is not None:
+            g = np.stack([g[b, h] for b, h in heads])
+            r = np.stack([r[b, h] for b, h in heads])
+        assert np.all(np.isfinite(g)), f"{tag} {name}: non-finite outputs (unwritten or overflow)"
+        ma, rf = errors(g, r)
+        report[name] = (ma, rf)
+        if name in ("lse",):
+            assert ma <= tol["lse"], f"{tag} {name}: max-abs {ma:.3e} > {tol['lse']}"
+        elif name == "delta":
+            # Delta is an intermediate: bounded by |dO| |O| accuracy, checked loosely
+            assert ma <= 10 * tol["max_abs"], f"{tag} {name}: max-abs {ma:.3e}"
+        else:
+            lim = tol["max_abs"] * max_abs_scale
+            assert ma <= lim, f"{tag} {name}: max-abs {ma:.3e} > {lim}"
+            if tol["rel_fro"] is not None:
+                assert rf <= tol["rel_fro"], f"{tag} {name}: rel-Frobenius {rf:.3e} > {tol['rel_fro']}"
+    log(f"{tag} " + " ".join(f"{n}:{m:.2e}/{f:.1e}" for n, (m, f) in report.items()))
+    return report

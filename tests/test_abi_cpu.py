@@ -1,0 +1,143 @@
+"""The C-ABI library without a GPU: it loads, exports what the header declares, and
+rejects invalid arguments before making any HIP call."""
+import ctypes
+import re
+
+import pytest
+
+import causal_attention_amd as ca
+from causal_attention_amd import _binding
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ca.load_library()
+
+
+def test_exports_every_header_function(lib):
+    names = ca.header_functions()
+    assert set(names) == set(_binding.SIGNATURES), names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_header_status_codes_match_binding():
+    with open(_binding.HEADER_PATH) as f:
+        text = f.read()
+    codes = dict((name, int(val)) for name, val in re.findall(r"(ATTN_(?:OK|ERR_\w+))\s*=\s*(-?\d+)", text))
+    assert {v: k for k, v in codes.items()} == _binding.STATUS_NAMES
+
+
+def test_abi_version(lib):
+    assert lib.attn_abi_version() == 100
+
+
+def test_status_strings(lib):
+    for code in list(_binding.STATUS_NAMES) + [-100, 7]:
+        s = lib.attn_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.attn_status_string(-3) == b"head dimension D must be 32, 64 or 128"
+
+
+def _fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, S=64, D=64, scale=0.125, mask=0,
+             cu=None, n=0, mx=0, dtype=1, stream=None)
+    a.update(kw)
+    return lib.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["S"], a["D"], a["scale"],
+                        a["mask"], a["cu"], a["n"], a["mx"], a["dtype"], a["stream"])
+
+
+def _bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, delta=FAKE,
+             B=1, H=2, S=64, D=64, scale=0.125, mask=0, cu=None, n=0, mx=0, dtype=1, stream=None)
+    a.update(kw)
+    return lib.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                        a["delta"], a["B"], a["H"], a["S"], a["D"], a["scale"], a["mask"], a["cu"], a["n"],
+                        a["mx"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
+    (dict(D=48), -3), (dict(D=256), -3), (dict(D=0), -3),
+    (dict(dtype=2), -4), (dict(dtype=-1), -4),
+    (dict(mask=2), -5), (dict(mask=-1), -5),
+    (dict(mask=1, cu=None, n=1, mx=64), -1),
+    (dict(mask=1, cu=FAKE, n=1, mx=64, B=2), -6),
+    (dict(mask=1, cu=FAKE, n=0, mx=64), -6),
+    (dict(mask=1, cu=FAKE, n=65, mx=64), -6),
+    (dict(mask=1, cu=FAKE, n=2, mx=0), -6),
+    (dict(mask=1, cu=FAKE, n=2, mx=65), -6),
+    (dict(S=0), -2), (dict(S=-5), -2), (dict(B=0), -2), (dict(H=0), -2),
+    (dict(B=1024, H=1024, S=2048), -2),
+    (dict(scale=float("nan")), -9), (dict(scale=float("inf")), -9), (dict(scale=0.0), -9),
+    (dict(scale=-0.1), -9),
+])
+def test_fwd_rejects_invalid_arguments(lib, kw, code):
+    assert _fwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(do=None), -1), (dict(lse=None), -1), (dict(delta=None), -1), (dict(dq=None), -1),
+    (dict(dk=None), -1), (dict(dv=None), -1), (dict(o=None), -1),
+    (dict(D=16), -3), (dict(dtype=5), -4), (dict(mask=3), -5),
+    (dict(mask=1, cu=FAKE, n=1, mx=64, B=3), -6), (dict(S=0), -2), (dict(scale=float("nan")), -9),
+])
+def test_bwd_rejects_invalid_arguments(lib, kw, code):
+    assert _bwd(lib, **kw) == code
+
+
+def test_stage_entry_points_reject_invalid_arguments(lib):
+    assert lib.attn_bwd_preprocess(FAKE, FAKE, None, 1, 1, 64, 64, 1, None) == -1
+    assert lib.attn_bwd_preprocess(FAKE, FAKE, FAKE, 1, 1, 64, 40, 1, None) == -3
+    assert lib.attn_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 64, 0.1, 0,
+                             None, 0, 0, 1, None) == -1
+    assert lib.attn_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 0.1, 1,
+                             None, 0, 0, 1, None) == -1
+    assert lib.attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 0.1, 0,
+                           None, 0, 0, 7, None) == -4
+    assert lib.attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, -1.0, 0,
+                           None, 0, 0, 1, None) == -9
+
+
+def test_no_device_reports_hip_error(lib):
+    """A valid call with no GPU present fails with ATTN_ERR_HIP instead of aborting."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _fwd(lib) == -7
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 16, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ca.attn_fwd(q, q, q, torch.zeros(1, 1, 16, 32), torch.zeros(1, 1, 16), 0.1)
+
+
+def test_binding_rejects_unsupported_dtype():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 16, 32, dtype=torch.float16)
+    with pytest.raises(TypeError):
+        ca.attn_fwd(q, q, q, None, None, 0.1)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="build the HIP library"):
+        _binding._lib, saved = None, _binding._lib
+        try:
+            _binding.load_library(str(tmp_path / "nope.so"))
+        finally:
+            _binding._lib = saved
+
+
+def test_signatures_cover_argument_counts():
+    """argtypes lengths equal the parameter counts in the header."""
+    with open(_binding.HEADER_PATH) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    for name, args in _binding.SIGNATURES.items():
+        m = re.search(name + r"\s*\(([^)]*)\)", text)
+        params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
+        assert len(params) == len(args), name
+    assert ctypes.sizeof(ctypes.c_int) == 4

@@ -1,0 +1,190 @@
+"""GPU parity: the HIP kernels through the C ABI against the fp64 oracle.
+
+Every workload (tiny fp32, 12M-class ctx 512, 237M-class ctx 1024, long context
+8192, packed documents) on several seeds, plus edge shapes (ragged tails, one
+row, one head, head dims 32/64/128, both input dtypes), packed-document edge
+cases, large logits, NaN propagation and NaN-poisoned outputs.
+Tolerances: fp32 inputs max-abs 1e-4; bf16 inputs max-abs 2e-2 and relative
+Frobenius 1e-2 per output tensor, LSE 1e-3 (tests/gpu_util.py).
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import MASK_CAUSAL, MASK_DOC_CAUSAL, attention_dq_rows_ref, attention_fwd_rows_ref
+from tests.gpu_util import compare, log, oracle, run_hip, to_device
+from workload import CONFIGS, AttnConfig, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import causal_attention_amd as ca
+    ca.load_library()
+
+
+FULL_CASES = [("tiny_f32", s) for s in (1, 11, 12, 13)] + \
+             [("lm12m_ctx512", s) for s in (2, 11, 12, 13)] + \
+             [("lm237m_ctx1024", s) for s in (3, 11, 12, 13)]
+
+
+@pytest.mark.parametrize("cfg,seed", FULL_CASES)
+def test_parity_full_oracle(cfg, seed):
+    """Every element of every output against the full fp64 oracle."""
+    c = CONFIGS[cfg]
+    log(f"[parity] {cfg} seed={seed} B{c.B} H{c.H} S{c.S} D{c.D} {c.dtype}")
+    x = make_inputs(c, seed)
+    out = run_hip(x)
+    ref = oracle(x)
+    compare(out, ref, c.dtype, tag=f"{cfg}/{seed}")
+
+
+SAMPLED_CASES = [("long_ctx8192", s) for s in (4, 11, 12)] + [("packed_docs8192", s) for s in (5, 11, 12)]
+
+
+@pytest.mark.parametrize("cfg,seed", SAMPLED_CASES)
+def test_parity_full_size_sampled_heads(cfg, seed):
+    """Full-size workloads: two whole heads against the oracle, plus sampled rows
+    of O, LSE and dQ in every head (each row computed on its own)."""
+    c = CONFIGS[cfg]
+    log(f"[parity] {cfg} seed={seed} B{c.B} H{c.H} S{c.S} D{c.D} {c.dtype} (sampled heads)")
+    x = make_inputs(c, seed)
+    out = run_hip(x)
+    rng = np.random.default_rng(seed)
+    heads = [(0, int(rng.integers(0, c.H))), (0, c.H - 1)]
+    ref = oracle(x, heads=heads)
+    compare(out, ref, c.dtype, heads=heads, tag=f"{cfg}/{seed}")
+    o = out["o"].cpu().numpy()
+    lse = out["lse"].cpu().numpy()
+    dq = out["dq"].cpu().numpy()
+    cu = x["cu_seqlens"]
+    for h in range(c.H):
+        rows = sorted(set([0, c.S - 1] + [int(r) for r in rng.integers(0, c.S, 4)]))
+        ro, rl = attention_fwd_rows_ref(x["q"], x["k"], x["v"], x["scale"], 0, h, rows, c.mask_mode, cu)
+        assert np.max(np.abs(o[0, h, rows] - ro)) <= 2e-2
+        assert np.max(np.abs(lse[0, h, rows] - rl)) <= 1e-3
+        rq = attention_dq_rows_ref(x["q"], x["k"], x["v"], x["do"], x["scale"], 0, h, rows[:3], c.mask_mode, cu)
+        assert np.max(np.abs(dq[0, h, rows[:3]] - rq)) <= 2e-2
+
+
+def _shape_cfg(dtype, D, mask_mode=MASK_CAUSAL, qkv_scale=1.0):
+    return AttnConfig("edge", B=1, H=1, S=1, D=D, dtype=dtype, qkv_scale=qkv_scale, mask_mode=mask_mode)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("S", [1, 17, 100, 1000])
+def test_edge_sequence_lengths(dtype, D, S):
+    """Ragged tails and tiny sequences with B*H = 1."""
+    log(f"[edge] S={S} D={D} {dtype}")
+    x = make_inputs(_shape_cfg(dtype, D), 100 + S + D, shape=(1, 1, S, D))
+    compare(run_hip(x), oracle(x), dtype, tag=f"edge S{S} D{D} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,H,S,D", [(2, 3, 130, 64), (3, 2, 257, 32), (1, 2, 383, 128)])
+def test_multi_head_ragged(dtype, B, H, S, D):
+    log(f"[edge] B{B} H{H} S{S} D{D} {dtype}")
+    x = make_inputs(_shape_cfg(dtype, D), 7 * S + D, shape=(B, H, S, D))
+    compare(run_hip(x), oracle(x), dtype, tag=f"B{B}H{H}S{S}D{D} {dtype}")
+
+
+def _doc_inputs(dtype, D, cu, H=2, seed=0):
+    cu = np.asarray(cu, dtype=np.int32)
+    S = int(cu[-1])
+    x = make_inputs(_shape_cfg(dtype, D), seed, shape=(1, H, S, D))
+    x["cu_seqlens"] = cu
+    x["mask_mode"] = MASK_DOC_CAUSAL
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_documents_with_length_one_and_ragged(dtype, D):
+    cu = [0, 1, 2, 50, 51, 180, 181, 300, 429, 430]
+    log(f"[doc] cu={cu} D={D} {dtype}")
+    x = _doc_inputs(dtype, D, cu, seed=D)
+    compare(run_hip(x), oracle(x), dtype, tag=f"doc D{D} {dtype}")
+
+
+@pytest.mark.parametrize("seed", [21, 22])
+def test_packed_small_random_documents(seed):
+    """Packed mode at a size the oracle checks fully: 1000 tokens, lengths in [1, 300]."""
+    from workload import make_cu_seqlens
+    cu = make_cu_seqlens(1000, 1, 300, seed)
+    log(f"[doc] random cu ({len(cu) - 1} docs) seed={seed}")
+    x = _doc_inputs("bf16", 64, cu, H=4, seed=seed)
+    compare(run_hip(x), oracle(x), "bf16", tag=f"doc random {seed}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_single_document_equals_causal_bitwise(dtype):
+    S = 300
+    log(f"[doc] single document vs causal {dtype}")
+    x = make_inputs(_shape_cfg(dtype, 64), 31, shape=(1, 3, S, 64))
+    a = run_hip(x)
+    y = dict(x)
+    y["cu_seqlens"] = np.array([0, S], dtype=np.int32)
+    y["mask_mode"] = MASK_DOC_CAUSAL
+    b = run_hip(y)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert bool((a[n] == b[n]).all()), n
+
+
+def test_large_logits():
+    """Q and K scaled by 4: scores with std ~32 stress the running-max rescaling."""
+    c = AttnConfig("big", B=2, H=2, S=512, D=64, dtype="bf16", qkv_scale=1.0)
+    x = make_inputs(c, 41, shape=(2, 2, 512, 64))
+    from workload import round_to_bf16
+    x["q"] = round_to_bf16(x["q"] * 4.0)
+    x["k"] = round_to_bf16(x["k"] * 4.0)
+    log("[stress] large logits")
+    out = run_hip(x)
+    ref = oracle(x)
+    compare(out, ref, "bf16", names=("o", "lse", "dv"), tag="large logits")
+    # dQ and dK carry the 4x factor of K and Q: same relative accuracy, scaled absolute bound
+    compare(out, ref, "bf16", names=("dq", "dk"), tag="large logits grads", max_abs_scale=4.0)
+
+
+def test_nan_row_reaches_only_its_outputs():
+    import torch
+    x = make_inputs(CONFIGS["lm12m_ctx512"], 51, shape=(1, 2, 256, 64))
+    dev = to_device(x)
+    i = 77
+    dev["q"][0, 1, i, 5] = float("nan")
+    log("[nan] NaN in one query row")
+    out = run_hip(x, dev=dev)
+    o = out["o"].cpu().numpy()
+    lse = out["lse"].cpu().numpy()
+    assert np.all(np.isnan(o[0, 1, i])) and np.isnan(lse[0, 1, i])
+    mask = np.ones(256, bool)
+    mask[i] = False
+    assert np.all(np.isfinite(o[0, 1, mask])) and np.all(np.isfinite(o[0, 0]))
+    ref = oracle(x)
+    assert np.max(np.abs(o[0, 1, mask] - ref["o"][0, 1, mask])) <= 2e-2
+    del torch
+
+
+def test_lse_may_be_null():
+    import torch
+    import causal_attention_amd as ca
+    x = make_inputs(CONFIGS["lm12m_ctx512"], 61, shape=(1, 2, 200, 64))
+    dev = to_device(x)
+    o1, lse = ca.forward(dev["q"], dev["k"], dev["v"], x["scale"])
+    o2 = torch.full_like(o1, float("nan"))
+    ca.attn_fwd(dev["q"], dev["k"], dev["v"], o2, None, x["scale"])
+    torch.cuda.synchronize()
+    assert bool((o1 == o2).all())
+
+
+def test_scale_is_honoured():
+    """A non-default temperature reaches the kernels (checked against the oracle)."""
+    x = make_inputs(CONFIGS["lm12m_ctx512"], 71, shape=(1, 2, 160, 64))
+    x["scale"] = 0.3
+    compare(run_hip(x), oracle(x), "bf16", tag="scale 0.3")
+    assert not math.isclose(x["scale"], 1 / 8)
