@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Throughput of fused causal attention, forward + backward, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole path on resident inputs: attn_fwd (forward
+with LSE) then attn_bwd (Delta preprocess, dK/dV, dQ).  Throughput counts the
+causal FLOPs actually allowed by the mask: 4*D per allowed (query, key) pair
+forward and 10*D backward (the five products of the FlashAttention-2
+accounting), divided by the measured time.  One JSON line is printed.
+
+Besides the headline workload the line carries:
+  by_workload   the same measurement at the other full-size workloads
+                (context 512, 8192 and packed documents), fewer steps;
+  kernels       per-kernel mean duration from HIP events on the launch stream;
+  roofline      the dominant kernel against its roofline;
+  cpu_baseline  the fp64 oracle timed on this host's cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+from workload import CONFIGS, allowed_pair_count, make_inputs  # noqa: E402
+
+METRIC = "causal attention fwd+bwd TFLOPS and % bf16 MFMA peak at ctx 512/1024/8192"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 flop/CU/clk (dense)
+PEAK_FP32_TFLOPS = 157.3    # fp32 matrix/vector peak used for fp32 inputs
+PEAK_HBM_GBS = 8000.0
+HEADLINE = "lm237m_ctx1024"
+SEEDS = {"tiny_f32": 1, "lm12m_ctx512": 2, "lm237m_ctx1024": 3, "long_ctx8192": 4, "packed_docs8192": 5}
+# algorithmic flops per allowed pair, per kernel (times D)
+KERNEL_FLOPS_PER_PAIR = {"fwd": 4, "dkdv": 8, "dq": 2}
+KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=HEADLINE, choices=sorted(CONFIGS))
+    p.add_argument("--kernel-reps", type=int, default=50, help="repetitions for per-kernel event timing")
+    p.add_argument("--no-others", action="store_true", help="skip the other full-size workloads")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time for the oracle sample")
+    return p.parse_args()
+
+
+class Workload:
+    """Resident device inputs and outputs of one workload."""
+
+    def __init__(self, name):
+        import torch
+        import causal_attention_amd as ca
+        self.ca = ca
+        self.name = name
+        self.cfg = cfg = CONFIGS[name]
+        x = make_inputs(cfg, SEEDS[name])
+        self.x = x
+        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        d = {n: torch.from_numpy(x[n]).to("cuda").to(dt).contiguous() for n in ("q", "k", "v", "do")}
+        self.q, self.k, self.v, self.do = d["q"], d["k"], d["v"], d["do"]
+        B, H, S, D = x["B"], x["H"], x["S"], x["D"]
+        f32 = dict(dtype=torch.float32, device="cuda")
+        self.o = torch.empty((B, H, S, D), **f32)
+        self.dq = torch.empty_like(self.o)
+        self.dk = torch.empty_like(self.o)
+        self.dv = torch.empty_like(self.o)
+        self.lse = torch.empty((B, H, S), **f32)
+        self.delta = torch.empty((B, H, S), **f32)
+        cu = x["cu_seqlens"]
+        if cu is not None:
+            self.cu = torch.from_numpy(cu).to("cuda")
+            self.max_seqlen = int(np.diff(cu).max())
+        else:
+            self.cu, self.max_seqlen = None, None
+        self.pairs = allowed_pair_count(S, B, H, cu)
+        self.flops_fwd = 4 * D * self.pairs
+        self.flops_bwd = 10 * D * self.pairs
+        self.stream = torch.cuda.current_stream()
+        self.sargs = dict(mask_mode=cfg.mask_mode, cu_seqlens=self.cu, max_seqlen=self.max_seqlen,
+                          stream=self.stream)
+
+    def fwd(self):
+        self.ca.attn_fwd(self.q, self.k, self.v, self.o, self.lse, self.x["scale"], **self.sargs)
+
+    def bwd(self):
+        self.ca.attn_bwd(self.q, self.k, self.v, self.o, self.do, self.lse, self.dq, self.dk, self.dv,
+                         self.delta, self.x["scale"], **self.sargs)
+
+    def pre(self):
+        self.ca.attn_bwd_preprocess(self.o, self.do, self.delta, stream=self.stream)
+
+    def dkdv(self):
+        self.ca.attn_bwd_dkdv(self.q, self.k, self.v, self.do, self.lse, self.delta, self.dk, self.dv,
+                              self.x["scale"], **self.sargs)
+
+    def dqk(self):
+        self.ca.attn_bwd_dq(self.q, self.k, self.v, self.do, self.lse, self.delta, self.dq,
+                            self.x["scale"], **self.sargs)
+
+    def step(self):
+        self.fwd()
+        self.bwd()
+
+    def timed_steps(self, steps, warmup):
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    def kernel_times(self, reps):
+        """Mean duration of each kernel (ms) from HIP events recorded on the launch stream."""
+        import torch
+        stages = [("fwd", self.fwd), ("pre", self.pre), ("dkdv", self.dkdv), ("dq", self.dqk)]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(reps)]
+        for _ in range(3):
+            self.step()
+        torch.cuda.synchronize()
+        for r in range(reps):
+            ev[r][0].record(self.stream)
+            for i, (_, fn) in enumerate(stages):
+                fn()
+                ev[r][i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        out = {}
+        for i, (name, _) in enumerate(stages):
+            ts = sorted(ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps))
+            out[name] = {"mean_ms": float(np.mean(ts)), "median_ms": float(np.median(ts))}
+        return out
+
+    def preprocess_bytes(self):
+        B, H, S, D = self.x["B"], self.x["H"], self.x["S"], self.x["D"]
+        in_bytes = 2 if self.cfg.dtype == "bf16" else 4
+        return B * H * S * (D * (in_bytes + 4) + 4)
+
+
+def sources_digest():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "causal_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("sources_digest") != sources_digest():
+        return None
+    ent = rec.get("kernels", {}).get(workload, {}).get(kernel)
+    return None if ent is None else ent.get("bytes_per_launch")
+
+
+def roofline(w, times):
+    """The dominant kernel (most time per step) against its roofline."""
+    peak = PEAK_BF16_TFLOPS if w.cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    dom = max(times, key=lambda k: times[k]["mean_ms"])
+    t = times[dom]["mean_ms"] * 1e-3
+    if dom == "pre":
+        achieved = w.preprocess_bytes() / t / 1e9
+        r = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        achieved = KERNEL_FLOPS_PER_PAIR[dom] * w.x["D"] * w.pairs / t / 1e12
+        r = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s"}
+    r["frac"] = r["achieved"] / r["peak"]
+    r["traffic"] = measured_traffic(dom, w.name)
+    r["kernel"] = dom
+    return r
+
+
+def cpu_baseline(w, seconds):
+    """The fp64 oracle (as it stands) on whole heads of the same workload, until about
+    `seconds` of host time are spent; reported in the same unit as the GPU value."""
+    from oracle import attention_bwd_ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                      default=1)
+    except Exception:  # threadpoolctl missing or no BLAS info
+        threads = os.cpu_count() or 1
+    x = w.x
+    B, H, S, D = x["B"], x["H"], x["S"], x["D"]
+    args = [x[n].astype(np.float64) for n in ("q", "k", "v", "do")]
+    cu = x["cu_seqlens"]
+    per_head_pairs = allowed_pair_count(S, 1, 1, cu)
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    done = 0
+    t0 = time.perf_counter()
+    # whole heads, cycling through the workload until the time budget is spent
+    while time.perf_counter() - t0 < seconds:
+        bh = heads[done % len(heads)]
+        attention_bwd_ref(*args, x["scale"], x["mask_mode"], cu, heads=[bh])
+        done += 1
+    dt = time.perf_counter() - t0
+    flops = 14 * D * per_head_pairs * done
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"fwd+bwd of {done} heads (of {len(heads)}, cycled) of B{B} H{H} S{S} D{D}, {dt:.1f} s"}
+
+
+def measure(name, steps, warmup, reps):
+    w = Workload(name)
+    sec = w.timed_steps(steps, warmup)
+    total = w.flops_fwd + w.flops_bwd
+    tflops = total / sec / 1e12
+    times = w.kernel_times(reps)
+    peak = PEAK_BF16_TFLOPS if w.cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    ms_fwd = times["fwd"]["mean_ms"]
+    ms_bwd = sum(times[k]["mean_ms"] for k in ("pre", "dkdv", "dq"))
+    summary = {
+        "tflops": tflops, "pct_peak": 100.0 * tflops / peak, "ms_per_step": sec * 1e3,
+        "fwd_tflops": w.flops_fwd / (ms_fwd * 1e-3) / 1e12,
+        "bwd_tflops": w.flops_bwd / (ms_bwd * 1e-3) / 1e12,
+        "kernels_ms": {k: round(v["mean_ms"], 5) for k, v in times.items()},
+        "pairs": w.pairs,
+    }
+    return w, sec, times, summary
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported in this build "
+              "(attention shards by batch and head with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import causal_attention_amd as ca
+    ca.load_library()
+
+    log(f"[bench] workload {a.workload}: warmup {a.warmup}, steps {a.steps}")
+    w, sec, times, summary = measure(a.workload, a.steps, a.warmup, a.kernel_reps)
+    log(f"[bench] {a.workload}: {summary['tflops']:.1f} TFLOPS ({summary['pct_peak']:.1f}% of peak), "
+        f"{sec * 1e3:.4f} ms/step, kernels {summary['kernels_ms']}")
+    by_workload = {a.workload: summary}
+    if not a.no_others:
+        for name in ("lm12m_ctx512", "long_ctx8192", "packed_docs8192", "lm237m_ctx1024"):
+            if name == a.workload:
+                continue
+            _, _, _, s = measure(name, max(10, a.steps // 4), max(3, a.warmup // 2), max(10, a.kernel_reps // 2))
+            by_workload[name] = s
+            log(f"[bench] {name}: {s['tflops']:.1f} TFLOPS ({s['pct_peak']:.1f}% of peak), "
+                f"kernels {s['kernels_ms']}")
+    rl = roofline(w, times)
+    log(f"[bench] roofline: {rl}")
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host ...")
+        cpu = cpu_baseline(w, a.cpu_seconds)
+        log(f"[bench] cpu baseline: {cpu}")
+    cfg = w.cfg
+    line = {
+        "metric": METRIC,
+        "value": summary["tflops"],
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": sec * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "S": cfg.S, "D": cfg.D,
+                   "mask": "packed_documents" if cfg.mask_mode else "causal",
+                   "outputs": "fp32", "parallelism": "single GPU"},
+        "pct_peak": summary["pct_peak"],
+        "fwd_tflops": summary["fwd_tflops"],
+        "bwd_tflops": summary["bwd_tflops"],
+        "kernels": {k: v["mean_ms"] for k, v in times.items()},
+        "roofline": rl,
+        "cpu_baseline": cpu,
+        "by_workload": by_workload,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
