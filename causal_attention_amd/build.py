@@ -29,6 +29,8 @@ HIPCC_FLAGS = [
     "-shared",
     "-Wall",
     "-Wno-unused-result",
+    # matrix-core accumulators in VGPRs: the softmax reads them directly
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     # keep the compiler from forming packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

@@ -19,6 +19,8 @@ int check_common(int B, int H, int S, int D, int dtype) {
   if (B < 1 || H < 1 || S < 1) return ATTN_ERR_SHAPE;
   const int64_t elems = (int64_t)B * H * S * D;
   if (elems >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+  // one head's fp32 output must be addressable with 32-bit byte offsets
+  if ((int64_t)S * D * 4 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
 

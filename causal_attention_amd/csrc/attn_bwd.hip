@@ -99,14 +99,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   if (!t.valid) return;
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWaveSize;
+  const int wave = wave_id();
   const int lane = tid % kWaveSize;
   const int hh = lane / 32;
   const int c = lane % 32;
   const size_t base = (size_t)t.head * S * D;
   const size_t rbase = (size_t)t.head * S;
-  const T *qh = q + base;
-  const T *doh = dO + base;
+  const GBuf gq(q + base, (uint32_t)(t.seg_end * D * sizeof(T)));
+  const GBuf gdo(dO + base, (uint32_t)(t.seg_end * D * sizeof(T)));
+  const GBuf gk(k + base, (uint32_t)(t.r_end * D * sizeof(T)));
+  const GBuf gv(v + base, (uint32_t)(t.r_end * D * sizeof(T)));
+  const GBuf glse(lse + rbase, (uint32_t)(t.seg_end * sizeof(float)));
+  const GBuf gdel(delta + rbase, (uint32_t)(t.seg_end * sizeof(float)));
 
   const int w0 = t.r_start + wave * 32 * KBW;  // first key of this wave
   const bool wave_active = w0 < t.r_end;
@@ -114,14 +118,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 
   frag kf[KBW][KB], vf[KBW][KB];
 #pragma unroll
-  for (int kw = 0; kw < KBW; ++kw) {
-    const int key = w0 + 32 * kw + c;
+  for (int kw = 0; kw < KBW; ++kw)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      kf[kw][kb] = global_frag<T>(k + base + (size_t)key * D + 16 * kb + 8 * hh, key < t.r_end);
-      vf[kw][kb] = global_frag<T>(v + base + (size_t)key * D + 16 * kb + 8 * hh, key < t.r_end);
+      kf[kw][kb] = global_frag<T, D>(gk, w0 + 32 * kw + c, 16 * kb + 8 * hh);
+      vf[kw][kb] = global_frag<T, D>(gv, w0 + 32 * kw + c, 16 * kb + 8 * hh);
     }
-  }
 
   f32x16 dkacc[KBW][DB], dvacc[KBW][DB];
 #pragma unroll
@@ -132,45 +134,26 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
       dvacc[kw][db] = f32x16{};
     }
 
-  const int q_lo = t.r_start;   // the first query that sees any of these keys
+  const int q_lo = t.r_start;  // the first query that sees any of these keys
   const int q_hi = t.seg_end;
   const int ntile = (q_hi - q_lo + BMQ - 1) / BMQ;
 
+  // Per-row statistics of the next query tile: LSE (to base 2) and Delta.
+  float lval = 0.f, dval = 0.f;
+  // Every thread loads (rows past the end read 0); threads tid < BMQ publish.
+  auto load_stats = [&](int q0) {
+    const int row = q0 + tid % BMQ;
+    const float lv = glse.load4((uint32_t)row * 4);
+    dval = gdel.load4((uint32_t)row * 4);
+    lval = row < q_hi ? lv * kLog2e : INFINITY;
+  };
+
   Loader lq, ldo;
-  float lval = INFINITY, dval = 0.f;
-  lq.load(qh, q_lo, q_hi, tid);
-  ldo.load(doh, q_lo, q_hi, tid);
-  if (tid < BMQ && q_lo + tid < q_hi) {
-    lval = lse[rbase + q_lo + tid] * kLog2e;
-    dval = delta[rbase + q_lo + tid];
-  }
+  lq.load(gq, q_lo, tid);
+  ldo.load(gdo, q_lo, tid);
+  load_stats(q_lo);
 
-  for (int it = 0; it < ntile; ++it) {
-    const int q0 = q_lo + it * BMQ;
-    __syncthreads();
-    lq.store_rm(sQ, tid);
-    lq.store_tr(sQt, tid);
-    ldo.store_rm(sdO, tid);
-    ldo.store_tr(sdOt, tid);
-    if (tid < BMQ) {
-      sL[tid] = lval;
-      sD[tid] = dval;
-    }
-    __syncthreads();
-    if (it + 1 < ntile) {
-      const int qn = q0 + BMQ;
-      lq.load(qh, qn, q_hi, tid);
-      ldo.load(doh, qn, q_hi, tid);
-      lval = INFINITY;
-      dval = 0.f;
-      if (tid < BMQ && qn + tid < q_hi) {
-        lval = lse[rbase + qn + tid] * kLog2e;
-        dval = delta[rbase + qn + tid];
-      }
-    }
-    if (!wave_active || q0 + BMQ - 1 < w0) continue;  // every query precedes every key here
-    const bool need_mask = q0 < wave_last;
-
+  auto tile = [&]<bool MASK>(int q0) {
     // S and dP as [query][key] blocks: lane c owns key w0 + 32*kw + c.
     f32x16 sacc[QB][KBW], pacc[QB][KBW];
 #pragma unroll
@@ -194,8 +177,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
       }
     }
 
-    // P = exp2(S * c2 - LSE2), dS = P (dP - Delta); pack both as B operands
-    // whose slots run over queries.
+    // P = exp2(S * c2 - LSE2), dS = P (dP - Delta); packed as B operands whose
+    // slots run over queries.
     frag pf[KBW][PB], sf[KBW][PB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -210,10 +193,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
         const int key = w0 + 32 * kw + c;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(sacc[qb][kw][r] * c2 - lq4[r / 4][r % 4]);
-          if (need_mask) {
+          float p = fast_exp2(__builtin_fmaf(sacc[qb][kw][r], c2, -lq4[r / 4][r % 4]));
+          if constexpr (MASK) {
             const int qi = q0 + qb * 32 + 8 * (r / 4) + 4 * hh + (r % 4);
-            if (qi < key) p = 0.f;
+            p = qi < key ? 0.f : p;
           }
           sacc[qb][kw][r] = p;
           pacc[qb][kw][r] = p * (pacc[qb][kw][r] - dq4[r / 4][r % 4]);
@@ -239,28 +222,51 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
         }
       }
     }
+  };
+
+  for (int it = 0; it < ntile; ++it) {
+    const int q0 = q_lo + it * BMQ;
+    __syncthreads();
+    lq.store_rm(sQ, tid);
+    lq.store_tr(sQt, tid);
+    ldo.store_rm(sdO, tid);
+    ldo.store_tr(sdOt, tid);
+    if (tid < BMQ) {
+      sL[tid] = lval;
+      sD[tid] = dval;
+    }
+    __syncthreads();
+    if (it + 1 < ntile) {
+      lq.load(gq, q0 + BMQ, tid);
+      ldo.load(gdo, q0 + BMQ, tid);
+      load_stats(q0 + BMQ);
+    }
+    if (!wave_active || q0 + BMQ - 1 < w0) continue;  // every query precedes every key here
+    if (q0 < wave_last)
+      tile.template operator()<true>(q0);
+    else
+      tile.template operator()<false>(q0);
   }
 
   if (!wave_active) return;
+  const GBuf gdk(dk + base, (uint32_t)(t.r_end * D * sizeof(float)));
+  const GBuf gdv(dv + base, (uint32_t)(t.r_end * D * sizeof(float)));
 #pragma unroll
   for (int kw = 0; kw < KBW; ++kw) {
     const int key = w0 + 32 * kw + c;
-    if (key < t.r_end) {
-      float *dkrow = dk + base + (size_t)key * D;
-      float *dvrow = dv + base + (size_t)key * D;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 a4, b4;
+      for (int g = 0; g < 4; ++g) {
+        f32x4 a4, b4;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            a4[i] = dkacc[kw][db][4 * g + i] * scale;
-            b4[i] = dvacc[kw][db][4 * g + i];
-          }
-          *reinterpret_cast<f32x4 *>(dkrow + db * 32 + 8 * g + 4 * hh) = a4;
-          *reinterpret_cast<f32x4 *>(dvrow + db * 32 + 8 * g + 4 * hh) = b4;
+        for (int i = 0; i < 4; ++i) {
+          a4[i] = dkacc[kw][db][4 * g + i] * scale;
+          b4[i] = dvacc[kw][db][4 * g + i];
         }
+        const uint32_t off = (uint32_t)(key * D + db * 32 + 8 * g + 4 * hh) * sizeof(float);
+        gdk.store16(a4, off);
+        gdv.store16(b4, off);
       }
     }
   }
@@ -295,14 +301,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   if (!t.valid) return;
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWaveSize;
+  const int wave = wave_id();
   const int lane = tid % kWaveSize;
   const int hh = lane / 32;
   const int c = lane % 32;
   const size_t base = (size_t)t.head * S * D;
   const size_t rbase = (size_t)t.head * S;
-  const T *kh = k + base;
-  const T *vh = v + base;
+  const GBuf gq(q + base, (uint32_t)(t.r_end * D * sizeof(T)));
+  const GBuf gdo(dO + base, (uint32_t)(t.r_end * D * sizeof(T)));
+  const GBuf gk(k + base, (uint32_t)(t.seg_end * D * sizeof(T)));
+  const GBuf gv(v + base, (uint32_t)(t.seg_end * D * sizeof(T)));
+  const GBuf glse(lse + rbase, (uint32_t)(t.r_end * sizeof(float)));
+  const GBuf gdel(delta + rbase, (uint32_t)(t.r_end * sizeof(float)));
 
   const int w0 = t.r_start + wave * 32 * QB;
   const bool wave_active = w0 < t.r_end;
@@ -313,14 +323,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = w0 + 32 * qb + c;
-    const bool ok = row < t.r_end;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      qf[qb][kb] = global_frag<T>(q + base + (size_t)row * D + 16 * kb + 8 * hh, ok);
-      df[qb][kb] = global_frag<T>(dO + base + (size_t)row * D + 16 * kb + 8 * hh, ok);
+      qf[qb][kb] = global_frag<T, D>(gq, row, 16 * kb + 8 * hh);
+      df[qb][kb] = global_frag<T, D>(gdo, row, 16 * kb + 8 * hh);
     }
-    l2[qb] = ok ? lse[rbase + row] * kLog2e : INFINITY;
-    dl[qb] = ok ? delta[rbase + row] : 0.f;
+    const float lv = glse.load4((uint32_t)row * 4);
+    dl[qb] = gdel.load4((uint32_t)row * 4);
+    l2[qb] = row < t.r_end ? lv * kLog2e : INFINITY;
   }
 
   f32x16 dqacc[QB][DB];
@@ -334,23 +344,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const int ntile = (kv_hi - kv_lo + BN - 1) / BN;
 
   Loader lk, lv;
-  lk.load(kh, kv_lo, t.seg_end, tid);
-  lv.load(vh, kv_lo, t.seg_end, tid);
+  lk.load(gk, kv_lo, tid);
+  lv.load(gv, kv_lo, tid);
 
-  for (int it = 0; it < ntile; ++it) {
-    const int k0 = kv_lo + it * BN;
-    __syncthreads();
-    lk.store_rm(sK, tid);
-    lk.store_tr(sKt, tid);
-    lv.store_rm(sV, tid);
-    __syncthreads();
-    if (it + 1 < ntile) {
-      lk.load(kh, k0 + BN, t.seg_end, tid);
-      lv.load(vh, k0 + BN, t.seg_end, tid);
-    }
-    if (!wave_active || k0 > wave_last) continue;
-    const bool need_mask = (k0 + BN - 1 > w0) || (k0 + BN > t.seg_end);
-
+  auto tile = [&]<bool MASK>(int k0) {
     // S^T = K Q^T and dP^T = V dO^T : rows are keys, lanes are queries.
     f32x16 sacc[QB][NB], pacc[QB][NB];
 #pragma unroll
@@ -382,10 +379,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
       for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(sacc[qb][nb][r] * c2 - l2[qb]);
-          if (need_mask) {
+          float p = fast_exp2(__builtin_fmaf(sacc[qb][nb][r], c2, -l2[qb]));
+          if constexpr (MASK) {
             const int key = k0 + 32 * nb + 8 * (r / 4) + 4 * hh + (r % 4);
-            if (key > qi || key >= t.seg_end) p = 0.f;
+            p = (key > qi || key >= t.seg_end) ? 0.f : p;
           }
           pacc[qb][nb][r] = p * (pacc[qb][nb][r] - dl[qb]);
         }
@@ -404,23 +401,39 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
         for (int qb = 0; qb < QB; ++qb) E::mma(dqacc[qb][db], a, sf[qb][j]);
       }
     }
+  };
+
+  for (int it = 0; it < ntile; ++it) {
+    const int k0 = kv_lo + it * BN;
+    __syncthreads();
+    lk.store_rm(sK, tid);
+    lk.store_tr(sKt, tid);
+    lv.store_rm(sV, tid);
+    __syncthreads();
+    if (it + 1 < ntile) {
+      lk.load(gk, k0 + BN, tid);
+      lv.load(gv, k0 + BN, tid);
+    }
+    if (!wave_active || k0 > wave_last) continue;
+    if ((k0 + BN - 1 > w0) || (k0 + BN > t.seg_end))
+      tile.template operator()<true>(k0);
+    else
+      tile.template operator()<false>(k0);
   }
 
   if (!wave_active) return;
+  const GBuf gdq(dq + base, (uint32_t)(t.r_end * D * sizeof(float)));
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qi = w0 + 32 * qb + c;
-    if (qi < t.r_end) {
-      float *row = dq + base + (size_t)qi * D;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 a4;
+      for (int g = 0; g < 4; ++g) {
+        f32x4 a4;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) a4[i] = dqacc[qb][db][4 * g + i] * scale;
-          *reinterpret_cast<f32x4 *>(row + db * 32 + 8 * g + 4 * hh) = a4;
-        }
+        for (int i = 0; i < 4; ++i) a4[i] = dqacc[qb][db][4 * g + i] * scale;
+        gdq.store16(a4, (uint32_t)(qi * D + db * 32 + 8 * g + 4 * hh) * sizeof(float));
       }
     }
   }

@@ -32,6 +32,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaveSize = 64;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -82,12 +83,49 @@ __device__ __forceinline__ typename Elem<T>::frag lds_frag(const T *p) {
   return *reinterpret_cast<const typename Elem<T>::frag *>(p);
 }
 
-// Load an 8-slot fragment from global memory, or zeros when !valid.
-template <typename T>
-__device__ __forceinline__ typename Elem<T>::frag global_frag(const T *p, bool valid) {
-  typename Elem<T>::frag f = {};
-  if (valid) f = *reinterpret_cast<const typename Elem<T>::frag *>(p);
-  return f;
+// ---------------------------------------------------------------------------
+// Global memory through buffer resources.  A resource covers `nbytes` from
+// `base`; loads past the end return zeros and stores past the end are
+// dropped by the hardware range check, so ragged tiles need no branches (and
+// the compiler can track outstanding loads exactly).  All offsets are
+// per-lane byte offsets (voffset), so the range check applies to them.
+struct GBuf {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ GBuf(const void *base, uint32_t nbytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)nbytes, 0x00020000)) {}
+  __device__ __forceinline__ u32x4 load16(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  }
+  __device__ __forceinline__ float load4(uint32_t off) const {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  }
+  __device__ __forceinline__ void store16(const f32x4 &v, uint32_t off) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+  }
+  __device__ __forceinline__ void store4(float v, uint32_t off) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+  }
+};
+
+// An 8-slot fragment of row `row`, columns [col, col + 8), of a row-major
+// [*, D] array behind `g` (zeros past the resource's end).
+template <typename T, int D>
+__device__ __forceinline__ typename Elem<T>::frag global_frag(const GBuf &g, int row, int col) {
+  using frag = typename Elem<T>::frag;
+  const uint32_t off = (uint32_t)(row * D + col) * sizeof(T);
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(frag, g.load16(off));
+  } else {
+    const u32x4 a = g.load16(off);
+    const u32x4 b = g.load16(off + 16);
+    u32x8 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[i] = a[i];
+      w[4 + i] = b[i];
+    }
+    return __builtin_bit_cast(frag, w);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -104,12 +142,12 @@ template <typename T, int R, int D> struct TileGeom {
   static constexpr int kSizeTR = D * kLdTR;
 };
 
-// Cooperative copy of rows [r0, r0 + R) of a row-major [*, D] array into LDS,
-// zero-filling rows >= r_end.  Each thread moves 16-byte chunks of two
-// adjacent rows (2p, 2p+1); a wave's load instruction covers whole rows, so
-// global reads are fully coalesced.  Split into a global->register phase
-// and a register->LDS phase so the next tile can be fetched while the
-// current one is in use.
+// Cooperative copy of rows [r0, r0 + R) of a row-major [*, D] array into LDS;
+// rows past the buffer resource's end read as zeros.  Each thread moves
+// 16-byte chunks of two adjacent rows (2p, 2p+1); a wave's load instruction
+// covers whole rows, so global reads are fully coalesced.  Split into a
+// global->register phase and a register->LDS phase so the next tile can be
+// fetched while the current one is in use.
 template <typename T, int R, int D, int NT> struct TileLoader {
   static constexpr int kVec = 16 / sizeof(T);      // elements per chunk
   static constexpr int kCPR = D / kVec;            // chunks per row
@@ -118,22 +156,22 @@ template <typename T, int R, int D, int NT> struct TileLoader {
   static_assert(D % kVec == 0, "D must be a multiple of the chunk");
   static_assert(NT % kCPR == 0, "thread count must cover whole rows");
   static_assert(R % 16 == 0, "tile rows must be a multiple of 16");
+  // every thread has rows in every pass (no guard needed)
+  static constexpr bool kExact = kPasses * kPairsPerPass * 2 == R;
   using G = TileGeom<T, R, D>;
 
   u32x4 regs[kPasses][2];
 
-  __device__ __forceinline__ void load(const T *g, int r0, int r_end, int tid) {
+  __device__ __forceinline__ void load(const GBuf &g, int r0, int tid) {
     const int c = tid % kCPR;
     const int p = tid / kCPR;
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps) {
       const int lr = 2 * (ps * kPairsPerPass + p);
+      if (kExact || lr < R) {
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int r = r0 + lr + e;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (lr < R && r < r_end) v = *reinterpret_cast<const u32x4 *>(g + (size_t)r * D + c * kVec);
-        regs[ps][e] = v;
+        for (int e = 0; e < 2; ++e)
+          regs[ps][e] = g.load16((uint32_t)((r0 + lr + e) * D + c * kVec) * sizeof(T));
       }
     }
   }
@@ -144,7 +182,7 @@ template <typename T, int R, int D, int NT> struct TileLoader {
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps) {
       const int lr = 2 * (ps * kPairsPerPass + p);
-      if (lr < R) {
+      if (kExact || lr < R) {
         *reinterpret_cast<u32x4 *>(rm + lr * G::kLdRM + c * kVec) = regs[ps][0];
         *reinterpret_cast<u32x4 *>(rm + (lr + 1) * G::kLdRM + c * kVec) = regs[ps][1];
       }
@@ -159,7 +197,7 @@ template <typename T, int R, int D, int NT> struct TileLoader {
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps) {
       const int lr = 2 * (ps * kPairsPerPass + p);
-      if (lr < R) {
+      if (kExact || lr < R) {
         const int col = perm16(lr);
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -189,6 +227,9 @@ __device__ __forceinline__ float swap_halves(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize); }
 
 // ---------------------------------------------------------------------------
 // Work decomposition.  A "row tile" is BM consecutive rows of one head that one

@@ -45,14 +45,15 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T *__restrict__ q, 
   if (!t.valid) return;
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWaveSize;
+  const int wave = wave_id();
   const int lane = tid % kWaveSize;
   const int hh = lane / 32;
   const int c = lane % 32;
   const size_t base = (size_t)t.head * S * D;
-  const T *qh = q + base;
-  const T *kh = k + base;
-  const T *vh = v + base;
+  // Resources end at the last valid row (queries) or key of the segment.
+  const GBuf gq(q + base, (uint32_t)(t.r_end * D * sizeof(T)));
+  const GBuf gk(k + base, (uint32_t)(t.seg_end * D * sizeof(T)));
+  const GBuf gv(v + base, (uint32_t)(t.seg_end * D * sizeof(T)));
 
   const int w0 = t.r_start + wave * 32 * QB;  // first query of this wave
   const bool wave_active = w0 < t.r_end;
@@ -60,15 +61,12 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T *__restrict__ q, 
 
   frag qf[QB][KB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = w0 + 32 * qb + c;
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      qf[qb][kb] = global_frag<T>(qh + (size_t)row * D + 16 * kb + 8 * hh, row < t.r_end);
-  }
+    for (int kb = 0; kb < KB; ++kb) qf[qb][kb] = global_frag<T, D>(gq, w0 + 32 * qb + c, 16 * kb + 8 * hh);
 
   f32x16 oacc[QB][DB];
-  float m[QB], l[QB];
+  float m[QB], l[QB];  // running max (scaled, base 2) and this lane-half's partial sum
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m[qb] = -INFINITY;
@@ -82,22 +80,12 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T *__restrict__ q, 
   const int ntile = (kv_hi - kv_lo + BN - 1) / BN;
 
   Loader lk, lv;
-  lk.load(kh, kv_lo, t.seg_end, tid);
-  lv.load(vh, kv_lo, t.seg_end, tid);
+  lk.load(gk, kv_lo, tid);
+  lv.load(gv, kv_lo, tid);
 
-  for (int it = 0; it < ntile; ++it) {
-    const int k0 = kv_lo + it * BN;
-    __syncthreads();  // every wave is done with the previous tile
-    lk.store_rm(sK, tid);
-    lv.store_tr(sVt, tid);
-    __syncthreads();
-    if (it + 1 < ntile) {
-      lk.load(kh, k0 + BN, t.seg_end, tid);
-      lv.load(vh, k0 + BN, t.seg_end, tid);
-    }
-    if (!wave_active || k0 > wave_last) continue;  // tile entirely above this wave's diagonal
-    const bool need_mask = (k0 + BN - 1 > w0) || (k0 + BN > t.seg_end);
-
+  // One key tile for this wave.  MASK selects the diagonal / segment-end
+  // variant; interior tiles take the branch-free path.
+  auto tile = [&]<bool MASK>(int k0) {
     // S^T = K Q^T : rows are keys, columns (lanes) are queries.
     f32x16 sacc[QB][NB];
 #pragma unroll
@@ -114,7 +102,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T *__restrict__ q, 
       }
     }
 
-    // Online softmax, base 2.
+    // Online softmax in base 2: the maximum is taken on raw scores and the
+    // scale folded into one multiply-add before each exp2.
     frag pf[QB][PB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -124,17 +113,15 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T *__restrict__ q, 
       for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float s = sacc[qb][nb][r] * c2;
-          if (need_mask) {
+          if constexpr (MASK) {
             const int key = k0 + 32 * nb + 8 * (r / 4) + 4 * hh + (r % 4);
-            if (key > qi || key >= t.seg_end) s = -INFINITY;
+            sacc[qb][nb][r] = (key > qi || key >= t.seg_end) ? -INFINITY : sacc[qb][nb][r];
           }
-          sacc[qb][nb][r] = s;
-          mx = fmaxf(mx, s);
+          mx = fmaxf(mx, sacc[qb][nb][r]);
         }
       }
       mx = fmaxf(mx, swap_halves(mx));
-      const float mnew = fmaxf(m[qb], mx);
+      const float mnew = fmaxf(m[qb], mx * c2);
       const float alpha = fast_exp2(m[qb] - mnew);
       m[qb] = mnew;
       float psum = 0.f;
@@ -142,7 +129,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T *__restrict__ q, 
       for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(sacc[qb][nb][r] - mnew);
+          const float p = fast_exp2(__builtin_fmaf(sacc[qb][nb][r], c2, -mnew));
           sacc[qb][nb][r] = p;
           psum += p;
         }
@@ -164,28 +151,43 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T *__restrict__ q, 
         for (int qb = 0; qb < QB; ++qb) E::mma(oacc[qb][db], a, pf[qb][j]);
       }
     }
+  };
+
+  for (int it = 0; it < ntile; ++it) {
+    const int k0 = kv_lo + it * BN;
+    __syncthreads();  // every wave is done with the previous tile
+    lk.store_rm(sK, tid);
+    lv.store_tr(sVt, tid);
+    __syncthreads();
+    if (it + 1 < ntile) {
+      lk.load(gk, k0 + BN, tid);
+      lv.load(gv, k0 + BN, tid);
+    }
+    if (!wave_active || k0 > wave_last) continue;  // tile entirely above this wave's diagonal
+    if ((k0 + BN - 1 > w0) || (k0 + BN > t.seg_end))
+      tile.template operator()<true>(k0);
+    else
+      tile.template operator()<false>(k0);
   }
 
   if (!wave_active) return;
+  const GBuf go(o + base, (uint32_t)(t.r_end * D * sizeof(float)));
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qi = w0 + 32 * qb + c;
     const float lt = l[qb] + swap_halves(l[qb]);
-    if (qi < t.r_end) {
-      const float inv = 1.0f / lt;
-      float *orow = o + base + (size_t)qi * D;
+    const float inv = 1.0f / lt;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 val;
+      for (int g = 0; g < 4; ++g) {
+        f32x4 val;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) val[i] = oacc[qb][db][4 * g + i] * inv;
-          *reinterpret_cast<f32x4 *>(orow + db * 32 + 8 * g + 4 * hh) = val;
-        }
+        for (int i = 0; i < 4; ++i) val[i] = oacc[qb][db][4 * g + i] * inv;
+        go.store16(val, (uint32_t)(qi * D + db * 32 + 8 * g + 4 * hh) * sizeof(float));
       }
-      if (lse != nullptr && hh == 0) lse[(size_t)t.head * S + qi] = (m[qb] + __log2f(lt)) * kLn2;
     }
+    if (lse != nullptr && hh == 0 && qi < t.r_end) lse[(size_t)t.head * S + qi] = (m[qb] + __log2f(lt)) * kLn2;
   }
 }
 

@@ -48,7 +48,7 @@
  * synchronisation); a malformed array gives unspecified results.
  *
  * Supported: D in {32, 64, 128}; S >= 1; B, H >= 1; B*H*S*D < 2^31;
- * scale finite and > 0.
+ * S*D < 2^29 (one head's fp32 output under 2 GiB); scale finite and > 0.
  */
 #ifndef CAUSAL_ATTN_API_H
 #define CAUSAL_ATTN_API_H
