@@ -15,12 +15,12 @@
 // own registers ("accum" order, attn_device.h), so P and dS feed the next
 // product without leaving registers.
 //   dK/dV: a lane owns one key.  S and dP are computed as [query][key]
-//          blocks (Q and dO rows staged row-major in LDS against K and V held
-//          in registers), then dV^T += dO^T P and dK^T += Q^T dS with Q and
-//          dO also staged transposed.
+//          blocks (Q and dO row fragments from LDS against K and V held in
+//          registers), then dV^T += dO^T P and dK^T += Q^T dS with Q and dO
+//          read from the same LDS tiles through the transposing load.
 //   dQ:    a lane owns one query.  S^T and dP^T are [key][query] blocks (K
 //          and V rows from LDS against Q and dO in registers), then
-//          dQ^T += K^T dS^T with K also staged transposed.
+//          dQ^T += K^T dS^T with K read transposed from the same tile.
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -84,13 +84,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   constexpr int PB = BMQ / 16;       // k-blocks over the queries of a tile
   using E = Elem<T>;
   using frag = typename E::frag;
-  using G = TileGeom<T, BMQ, D>;
+  constexpr int LD = RowStride<T, D>::kPadded;  // read both as rows and transposed
   using Loader = TileLoader<T, BMQ, D, NT>;
 
-  __shared__ __attribute__((aligned(16))) T sQ[G::kSizeRM];
-  __shared__ __attribute__((aligned(16))) T sQt[G::kSizeTR];
-  __shared__ __attribute__((aligned(16))) T sdO[G::kSizeRM];
-  __shared__ __attribute__((aligned(16))) T sdOt[G::kSizeTR];
+  __shared__ __attribute__((aligned(16))) T sQ[BMQ * LD];
+  __shared__ __attribute__((aligned(16))) T sdO[BMQ * LD];
   __shared__ __attribute__((aligned(16))) float sL[BMQ];  // LSE * log2(e); +inf past the end
   __shared__ __attribute__((aligned(16))) float sD[BMQ];  // Delta; 0 past the end
 
@@ -153,6 +151,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   ldo.load(gdo, q_lo, tid);
   load_stats(q_lo);
 
+  const TrRead<T, LD> trq(sQ, lane);
+  const TrRead<T, LD> trdo(sdO, lane);
+
   auto tile = [&]<bool MASK>(int q0) {
     // S and dP as [query][key] blocks: lane c owns key w0 + 32*kw + c.
     f32x16 sacc[QB][KBW], pacc[QB][KBW];
@@ -167,8 +168,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const frag aq = lds_frag<T>(sQ + (qb * 32 + c) * G::kLdRM + 16 * kb + 8 * hh);
-        const frag ad = lds_frag<T>(sdO + (qb * 32 + c) * G::kLdRM + 16 * kb + 8 * hh);
+        const frag aq = lds_frag<T>(sQ + (qb * 32 + c) * LD + 16 * kb + 8 * hh);
+        const frag ad = lds_frag<T>(sdO + (qb * 32 + c) * LD + 16 * kb + 8 * hh);
 #pragma unroll
         for (int kw = 0; kw < KBW; ++kw) {
           E::mma(sacc[qb][kw], aq, kf[kw][kb]);
@@ -213,8 +214,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int j = 0; j < PB; ++j) {
-        const frag ad = lds_frag<T>(sdOt + (db * 32 + c) * G::kLdTR + 16 * j + 8 * hh);
-        const frag aq = lds_frag<T>(sQt + (db * 32 + c) * G::kLdTR + 16 * j + 8 * hh);
+        const frag ad = trdo(16 * j, 32 * db);
+        const frag aq = trq(16 * j, 32 * db);
 #pragma unroll
         for (int kw = 0; kw < KBW; ++kw) {
           E::mma(dvacc[kw][db], ad, pf[kw][j]);
@@ -227,10 +228,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   for (int it = 0; it < ntile; ++it) {
     const int q0 = q_lo + it * BMQ;
     __syncthreads();
-    lq.store_rm(sQ, tid);
-    lq.store_tr(sQt, tid);
-    ldo.store_rm(sdO, tid);
-    ldo.store_tr(sdOt, tid);
+    lq.template store<LD>(sQ, tid);
+    ldo.template store<LD>(sdO, tid);
     if (tid < BMQ) {
       sL[tid] = lval;
       sD[tid] = dval;
@@ -289,12 +288,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   constexpr int PB = BN / 16;
   using E = Elem<T>;
   using frag = typename E::frag;
-  using G = TileGeom<T, BN, D>;
+  constexpr int LD = RowStride<T, D>::kPadded;
   using Loader = TileLoader<T, BN, D, NT>;
 
-  __shared__ __attribute__((aligned(16))) T sK[G::kSizeRM];
-  __shared__ __attribute__((aligned(16))) T sKt[G::kSizeTR];
-  __shared__ __attribute__((aligned(16))) T sV[G::kSizeRM];
+  __shared__ __attribute__((aligned(16))) T sK[BN * LD];
+  __shared__ __attribute__((aligned(16))) T sV[BN * LD];
 
   const RowTile t = DOC ? doc_tile(cu, blockIdx.x, gridDim.x, blockIdx.y, blockIdx.z, BM, true)
                         : causal_tile(blockIdx.x, gridDim.x, ntiles, BM, S, true);
@@ -347,6 +345,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   lk.load(gk, kv_lo, tid);
   lv.load(gv, kv_lo, tid);
 
+  const TrRead<T, LD> trk(sK, lane);
+
   auto tile = [&]<bool MASK>(int k0) {
     // S^T = K Q^T and dP^T = V dO^T : rows are keys, lanes are queries.
     f32x16 sacc[QB][NB], pacc[QB][NB];
@@ -361,8 +361,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const frag ak = lds_frag<T>(sK + (nb * 32 + c) * G::kLdRM + 16 * kb + 8 * hh);
-        const frag av = lds_frag<T>(sV + (nb * 32 + c) * G::kLdRM + 16 * kb + 8 * hh);
+        const frag ak = lds_frag<T>(sK + (nb * 32 + c) * LD + 16 * kb + 8 * hh);
+        const frag av = lds_frag<T>(sV + (nb * 32 + c) * LD + 16 * kb + 8 * hh);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           E::mma(sacc[qb][nb], ak, qf[qb][kb]);
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int j = 0; j < PB; ++j) {
-        const frag a = lds_frag<T>(sKt + (db * 32 + c) * G::kLdTR + 16 * j + 8 * hh);
+        const frag a = trk(16 * j, 32 * db);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) E::mma(dqacc[qb][db], a, sf[qb][j]);
       }
@@ -406,9 +406,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   for (int it = 0; it < ntile; ++it) {
     const int k0 = kv_lo + it * BN;
     __syncthreads();
-    lk.store_rm(sK, tid);
-    lk.store_tr(sKt, tid);
-    lv.store_rm(sV, tid);
+    lk.template store<LD>(sK, tid);
+    lv.template store<LD>(sV, tid);
     __syncthreads();
     if (it + 1 < ntile) {
       lk.load(gk, k0 + BN, tid);
@@ -442,11 +441,23 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 // Launchers.
 
+#ifndef ATTN_DKDV_KBW
+#define ATTN_DKDV_KBW 1
+#endif
+#ifndef ATTN_DKDV_BMQ
+#define ATTN_DKDV_BMQ 64
+#endif
+#ifndef ATTN_DQ_QB
+#define ATTN_DQ_QB 1
+#endif
+#ifndef ATTN_DQ_BN
+#define ATTN_DQ_BN 64
+#endif
 template <typename T, int D> struct BwdCfg {
-  static constexpr int KBW = 1;                                      // key blocks per wave (dK/dV)
-  static constexpr int BMQ = (D == 128 || sizeof(T) == 4) ? 32 : 64; // query tile (dK/dV)
-  static constexpr int QB = 1;                                       // query blocks per wave (dQ)
-  static constexpr int BN = 64;                                      // key tile (dQ)
+  static constexpr int KBW = (D == 128 || sizeof(T) == 4) ? 1 : ATTN_DKDV_KBW;  // key blocks per wave (dK/dV)
+  static constexpr int BMQ = (D == 128 || sizeof(T) == 4) ? 32 : ATTN_DKDV_BMQ;  // query tile (dK/dV)
+  static constexpr int QB = ATTN_DQ_QB;                                         // query blocks per wave (dQ)
+  static constexpr int BN = ATTN_DQ_BN;                                         // key tile (dQ)
 };
 
 template <typename T, int D>

@@ -14,10 +14,10 @@
 //   accum     slot (h, s) of k-block kb  <->  k = 16*kb + 8*(s/4) + 4*h + s%4
 // The "accum" order is exactly how a 32x32 result (e.g. P^T, dS) already sits
 // in a lane's registers 8*kb .. 8*kb+7, so a result can feed the next
-// contraction as its B operand with no data movement at all.  Operands staged
-// in LDS for that contraction are stored with their row index permuted to
-// match (swap bits 2 and 3 within each 16-row group), so each lane still reads
-// its 8 slots with one 16-byte LDS load.
+// contraction as its B operand with no data movement at all.  An operand that
+// must match it (the A operand of a product reducing over the rows of a
+// row-major LDS tile) is read with the transposing LDS load, which delivers
+// those rows in the same order (TrRead below).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,6 +27,8 @@ namespace attn {
 
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
@@ -55,6 +57,14 @@ template <> struct Elem<bf16> {
     for (int s = 0; s < 8; ++s) f[s] = (bf16)acc[8 * j + s];
     return f;
   }
+  // pack() and add the eight fp32 values to `sum` (round-to-nearest-even is
+  // unbiased, so normalising the rounded weights by the fp32 sum adds only
+  // random error far below the rounding of the weights themselves).
+  __device__ __forceinline__ static frag pack_sum(const f32x16 &acc, int j, float &sum) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) sum += acc[8 * j + s];
+    return pack(acc, j);
+  }
 };
 
 template <> struct Elem<float> {
@@ -70,18 +80,72 @@ template <> struct Elem<float> {
     for (int s = 0; s < 8; ++s) f[s] = acc[8 * j + s];
     return f;
   }
+  __device__ __forceinline__ static frag pack_sum(const f32x16 &acc, int j, float &sum) {
+    frag f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      f[s] = acc[8 * j + s];
+      sum += f[s];
+    }
+    return f;
+  }
 };
-
-// Row permutation of the "accum" order: swap bits 2 and 3 of the row index.
-__device__ __forceinline__ constexpr int perm16(int r) {
-  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
 
 // Load an 8-slot fragment from LDS (16- or 32-byte aligned).
 template <typename T>
 __device__ __forceinline__ typename Elem<T>::frag lds_frag(const T *p) {
   return *reinterpret_cast<const typename Elem<T>::frag *>(p);
 }
+
+// Fragment of the TRANSPOSE of a row-major LDS tile (row stride LD elements),
+// in "accum" slot order: lane (h, c) receives
+//     slot s = tile[row0 + 8*(s/4) + 4*h + s%4][col0 + c],
+// i.e. the A operand of a product that reduces over the tile's rows.
+// bf16: two ds_read_b64_tr_b16.  Within each group of 16 lanes that
+// instruction hands output lane 4a+b, slot k, element b of the 8 bytes
+// addressed by source lane a+4k; so source lane i of group g addresses row
+// (row0 + 4*h + i/4) at column (col0 + 16*(g%2) + 4*(i%4)), and the second
+// read the rows 8 further down.
+// fp32: eight ds_read_b32 (no transposing read exists for 32-bit data).
+template <typename T, int LD> struct TrRead;
+
+template <int LD> struct TrRead<bf16, LD> {
+  using frag = bf16x8;
+  const bf16 *base;  // this lane's source address for row0 = col0 = 0
+  __device__ __forceinline__ TrRead(const bf16 *tile, int lane) {
+    const int g = lane / 16, i = lane % 16, h = g / 2;
+    base = tile + (4 * h + i / 4) * LD + 16 * (g % 2) + 4 * (i % 4);
+  }
+  __device__ __forceinline__ frag operator()(int row0, int col0) const {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const bf16 *p = base + row0 * LD + col0;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 8 * LD));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = a[k];
+      v[4 + k] = b[k];
+    }
+    return __builtin_bit_cast(frag, v);
+  }
+};
+
+template <int LD> struct TrRead<float, LD> {
+  using frag = f32x8;
+  const float *base;
+  __device__ __forceinline__ TrRead(const float *tile, int lane) {
+    base = tile + 4 * (lane / 32) * LD + lane % 32;
+  }
+  __device__ __forceinline__ frag operator()(int row0, int col0) const {
+    const float *p = base + row0 * LD + col0;
+    frag f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) f[s] = p[(8 * (s / 4) + s % 4) * LD];
+    return f;
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Global memory through buffer resources.  A resource covers `nbytes` from
@@ -129,96 +193,130 @@ __device__ __forceinline__ typename Elem<T>::frag global_frag(const GBuf &g, int
 }
 
 // ---------------------------------------------------------------------------
-// LDS tile geometry for a block of R rows x D columns of T.
-//   RM (row-major):  element (r, d) at r * ld_rm + d,           ld_rm = D + pad
-//   TR (transposed): element (r, d) at d * ld_tr + perm16(r),   ld_tr = R + pad
-// The 16-byte row padding keeps 16-byte fragment loads of consecutive rows on
-// distinct LDS banks.
-template <typename T, int R, int D> struct TileGeom {
-  static constexpr int kPad = 16 / sizeof(T);
-  static constexpr int kLdRM = D + kPad;
-  static constexpr int kLdTR = R + kPad;
-  static constexpr int kSizeRM = R * kLdRM;  // elements
-  static constexpr int kSizeTR = D * kLdTR;
+// LDS row strides.  Tiles read as row fragments (16 bytes per lane, lanes on
+// consecutive rows) are padded by 16 bytes per row, which spreads consecutive
+// rows over distinct LDS banks; tiles read only through the transposing load
+// stay unpadded, the stride it reads fastest at.
+template <typename T, int D> struct RowStride {
+  static constexpr int kPadded = D + 16 / sizeof(T);
+  static constexpr int kTrOnly = sizeof(T) == 2 ? D : D + 4;
 };
 
-// Cooperative copy of rows [r0, r0 + R) of a row-major [*, D] array into LDS;
-// rows past the buffer resource's end read as zeros.  Each thread moves
-// 16-byte chunks of two adjacent rows (2p, 2p+1); a wave's load instruction
-// covers whole rows, so global reads are fully coalesced.  Split into a
+// Cooperative copy of rows [r0, r0 + R) of a row-major [*, D] array into a
+// row-major LDS tile with row stride LD; rows past the buffer resource's end
+// read as zeros.  Thread `tid` moves 16-byte chunks idx = tid + NT * pass
+// (row idx / CPR, chunk idx % CPR), so each wave's load instruction covers
+// whole consecutive rows and global reads are fully coalesced.  Split into a
 // global->register phase and a register->LDS phase so the next tile can be
 // fetched while the current one is in use.
 template <typename T, int R, int D, int NT> struct TileLoader {
-  static constexpr int kVec = 16 / sizeof(T);      // elements per chunk
-  static constexpr int kCPR = D / kVec;            // chunks per row
-  static constexpr int kPairsPerPass = NT / kCPR;  // row pairs per pass
-  static constexpr int kPasses = (R / 2 + kPairsPerPass - 1) / kPairsPerPass;
+  static constexpr int kVec = 16 / sizeof(T);          // elements per chunk
+  static constexpr int kCPR = D / kVec;                // chunks per row
+  static constexpr int kChunks = R * kCPR;
+  static constexpr int kPasses = (kChunks + NT - 1) / NT;
+  static constexpr bool kFull = kChunks % NT == 0;     // every thread busy in every pass
   static_assert(D % kVec == 0, "D must be a multiple of the chunk");
-  static_assert(NT % kCPR == 0, "thread count must cover whole rows");
-  static_assert(R % 16 == 0, "tile rows must be a multiple of 16");
-  // every thread has rows in every pass (no guard needed)
-  static constexpr bool kExact = kPasses * kPairsPerPass * 2 == R;
-  using G = TileGeom<T, R, D>;
+  static_assert(kFull || (kChunks < NT && kChunks % kWaveSize == 0),
+                "a partial pass must end on a wave boundary");
 
-  u32x4 regs[kPasses][2];
+  u32x4 regs[kPasses];
+
+  // Threads past the tile in a partial pass sit out; the test is per wave.
+  __device__ __forceinline__ static bool busy(int tid) {
+    return kFull || __builtin_amdgcn_readfirstlane(tid / kWaveSize) * kWaveSize < kChunks;
+  }
 
   __device__ __forceinline__ void load(const GBuf &g, int r0, int tid) {
-    const int c = tid % kCPR;
-    const int p = tid / kCPR;
+    if (!busy(tid)) return;
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps) {
-      const int lr = 2 * (ps * kPairsPerPass + p);
-      if (kExact || lr < R) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          regs[ps][e] = g.load16((uint32_t)((r0 + lr + e) * D + c * kVec) * sizeof(T));
-      }
+      const int idx = tid + NT * ps;
+      regs[ps] = g.load16((uint32_t)((r0 + idx / kCPR) * D + (idx % kCPR) * kVec) * sizeof(T));
     }
   }
 
-  __device__ __forceinline__ void store_rm(T *rm, int tid) const {
-    const int c = tid % kCPR;
-    const int p = tid / kCPR;
+  template <int LD>
+  __device__ __forceinline__ void store(T *dst, int tid) const {
+    if (!busy(tid)) return;
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps) {
-      const int lr = 2 * (ps * kPairsPerPass + p);
-      if (kExact || lr < R) {
-        *reinterpret_cast<u32x4 *>(rm + lr * G::kLdRM + c * kVec) = regs[ps][0];
-        *reinterpret_cast<u32x4 *>(rm + (lr + 1) * G::kLdRM + c * kVec) = regs[ps][1];
-      }
-    }
-  }
-
-  // Transposed store: rows lr and lr+1 land side by side (perm16 keeps bit 0),
-  // so each column element pair is one 32-bit (bf16) or 64-bit (fp32) write.
-  __device__ __forceinline__ void store_tr(T *tr, int tid) const {
-    const int c = tid % kCPR;
-    const int p = tid / kCPR;
-#pragma unroll
-    for (int ps = 0; ps < kPasses; ++ps) {
-      const int lr = 2 * (ps * kPairsPerPass + p);
-      if (kExact || lr < R) {
-        const int col = perm16(lr);
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-          for (int i = 0; i < kVec; ++i) {
-            const uint32_t a = (regs[ps][0][i / 2] >> (16 * (i & 1))) & 0xffffu;
-            const uint32_t b = (regs[ps][1][i / 2] >> (16 * (i & 1))) & 0xffffu;
-            *reinterpret_cast<uint32_t *>(tr + (c * kVec + i) * G::kLdTR + col) = a | (b << 16);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < kVec; ++i) {
-            uint2 w;
-            w.x = regs[ps][0][i];
-            w.y = regs[ps][1][i];
-            *reinterpret_cast<uint2 *>(tr + (c * kVec + i) * G::kLdTR + col) = w;
-          }
-        }
-      }
+      const int idx = tid + NT * ps;
+      *reinterpret_cast<u32x4 *>(dst + (idx / kCPR) * LD + (idx % kCPR) * kVec) = regs[ps];
     }
   }
 };
+
+// ---------------------------------------------------------------------------
+// Direct global->LDS tile copies (buffer_load ... lds).  Each wave instruction
+// writes 64 lanes x 16 bytes to 1 KB of consecutive LDS; the global chunk each
+// lane fetches is free, which places rows without padding.  Rows past the
+// buffer resource's end arrive as zeros.  No VGPRs hold the data in flight,
+// so tiles can be requested several iterations before they are used; the
+// caller waits with wait_vmcnt (each wave counts its own copies) and then
+// crosses a workgroup barrier before reading.
+//
+// Tiles read as row fragments are XOR-swizzled: 16-byte chunk c of row r is
+// stored at chunk c ^ (r & SW), which puts the 16-byte reads of consecutive
+// rows on distinct LDS banks without padding.
+template <typename T, int R, int D, int NT, bool SWIZZLE> struct DmaTile {
+  static constexpr int kVec = 16 / sizeof(T);                 // elements per chunk
+  static constexpr int kCPR = D / kVec;                        // chunks per row
+  static constexpr int kSW = SWIZZLE ? (kCPR < 8 ? kCPR : 8) - 1 : 0;
+  static constexpr int kBlocks = R * kCPR / kWaveSize;         // 1 KB blocks per tile
+  static constexpr int kPerWave = kBlocks / (NT / kWaveSize);  // copy instructions per wave
+  static_assert(R * kCPR % NT == 0, "tile must split evenly over the waves");
+
+  __device__ __forceinline__ static void issue(const GBuf &g, T *tile, int r0, int wave, int lane) {
+    typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int blk = wave * kPerWave + i;
+      const int p = blk * kWaveSize + lane;
+      const uint32_t row = (uint32_t)p / kCPR;
+      const uint32_t col = ((uint32_t)(p % kCPR) * kVec) ^ ((row & kSW) * kVec);  // swizzled chunk, in elements
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          g.r, (lds_void *)(tile + blk * (1024 / sizeof(T))), 16,
+          (((uint32_t)r0 + row) * D + col) * (uint32_t)sizeof(T), 0, 0, 0);
+    }
+  }
+};
+
+// Row fragment of a swizzled tile: 8 slots of row `row` starting at column
+// 8*(2*kb + hh) (natural slot order), for lanes whose row index is `row`.
+template <typename T, int D, int SW>
+__device__ __forceinline__ typename Elem<T>::frag swz_frag(const T *tile, int row, int chunk0) {
+  using frag = typename Elem<T>::frag;
+  constexpr int kVec = 16 / sizeof(T);
+  // (chunk ^ s) * kVec == (chunk * kVec) ^ (s * kVec): kVec is a power of two
+  const int sw = (row & SW) * kVec;
+  const int rbase = row * D;
+  if constexpr (sizeof(T) == 2) {
+    return *reinterpret_cast<const frag *>(tile + rbase + ((chunk0 * kVec) ^ sw));
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(tile + rbase + ((chunk0 * kVec) ^ sw));
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(tile + rbase + (((chunk0 + 1) * kVec) ^ sw));
+    frag f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = a[i];
+      f[4 + i] = b[i];
+    }
+    return f;
+  }
+}
+
+// Wait until at most N of this wave's vector-memory operations (including
+// direct-to-LDS copies) are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every copy in flight); LDS visibility of the copies a wave waited
+// for is what the barrier publishes.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
 // Cross-half reductions (lanes c and c + 32 hold the two halves of a column).

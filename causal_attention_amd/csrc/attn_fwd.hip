@@ -2,23 +2,37 @@
 //
 // Flash-attention forward (Forge, "What this is": fused forward written after
 // FlashAttention-2, "Acknowledgements"): one workgroup owns BM query rows of
-// one head and streams the key/value tiles up to its causal diagonal (keys of
-// its document only, in packed mode), keeping per row a running maximum m,
-// a running sum l and the unnormalised output; after the last tile
-// O = acc / l and LSE = m + ln l.  Scores never leave registers.
+// one head and streams key/value tiles up to its causal diagonal (keys of its
+// document only, in packed mode), keeping per row a reference maximum m, a
+// running sum l and the unnormalised output; after the last tile O = acc / l
+// and LSE = m + ln l.  Scores never leave registers.
 //
-// gfx950 mapping.  Each wave computes S^T = K Q^T for its 32*QB queries, so a
-// lane owns one query (column) and holds that query's scores against 16 keys
-// per 32-key block in its own registers: the row maximum and sum are in-lane
-// except for one exchange between the two wave halves, and P^T is already
-// the B operand of O^T += V^T P^T (the "accum" slot order, attn_device.h).
-// K is staged row-major and V transposed in LDS; the next tile's global
-// loads are in flight while the current tile is computed.  Softmax runs in
-// base 2 with scale * log2(e) folded into one multiply.
+// gfx950 mapping.
+//  * Each wave computes S^T = K Q^T for its 32*QB queries, so a lane owns one
+//    query and holds that query's scores in its own registers; P^T is then
+//    already the B operand of O^T += V^T P^T ("accum" slot order,
+//    attn_device.h).  K is read from LDS as (swizzled) row fragments; V is
+//    stored row-major and read through the transposing LDS load.
+//  * Software pipeline per wave: while the softmax of tile j runs on the
+//    vector ALUs, the matrix cores compute the scores of tile j+1 and the
+//    P V product of tile j-1.
+//  * K and V tiles arrive by direct global->LDS copies into 3-slot rings,
+//    requested two iterations before use, with one barrier per tile.
+//  * No per-tile maximum: p = exp2(s * c2 - m) uses the reference maximum m
+//    of earlier tiles (c2 = scale * log2 e).  The first tile, and any tile
+//    whose exponentials could overflow (a row sum above 2^64 or not finite,
+//    voted across the wave), take the exact path: true row maximum, rescale
+//    of the running output and sum (an out-of-range tile's scores are
+//    recomputed from its key tile, still in LDS, so the exponentials can
+//    overwrite the scores in place).
+//  * P is rounded to the input type (round to nearest even) for the P V
+//    product; the row sum adds the fp32 values.
 #include "attn_device.h"
 #include "attn_launch.h"
 
 namespace attn {
+
+constexpr float kRescaleLimit = 1.8446744e19f;  // 2^64: larger row sums take the exact path
 
 template <typename T, int D, int QB, int BN, bool DOC>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
@@ -32,13 +46,16 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T *__restrict__ q, 
   constexpr int DB = D / 32;        // 32-row blocks of O^T
   constexpr int NB = BN / 32;       // 32-key blocks per tile
   constexpr int PB = BN / 16;       // k-blocks over the keys of a tile
+  constexpr int NS = 3;             // LDS ring slots for K and for V
   using E = Elem<T>;
   using frag = typename E::frag;
-  using G = TileGeom<T, BN, D>;
-  using Loader = TileLoader<T, BN, D, NT>;
+  using KTile = DmaTile<T, BN, D, NT, true>;   // read as row fragments: swizzled
+  using VTile = DmaTile<T, BN, D, NT, false>;  // read through the transposing load
+  constexpr int IPW = KTile::kPerWave;         // copy instructions per wave per tile
+  static_assert(VTile::kPerWave == IPW, "K and V tiles have the same shape");
 
-  __shared__ __attribute__((aligned(16))) T sK[G::kSizeRM];
-  __shared__ __attribute__((aligned(16))) T sVt[G::kSizeTR];
+  __shared__ __attribute__((aligned(1024))) T sK[NS][BN * D];
+  __shared__ __attribute__((aligned(1024))) T sV[NS][BN * D];
 
   const RowTile t = DOC ? doc_tile(cu, blockIdx.x, gridDim.x, blockIdx.y, blockIdx.z, BM, true)
                         : causal_tile(blockIdx.x, gridDim.x, ntiles, BM, S, true);
@@ -50,7 +67,6 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T *__restrict__ q, 
   const int hh = lane / 32;
   const int c = lane % 32;
   const size_t base = (size_t)t.head * S * D;
-  // Resources end at the last valid row (queries) or key of the segment.
   const GBuf gq(q + base, (uint32_t)(t.r_end * D * sizeof(T)));
   const GBuf gk(k + base, (uint32_t)(t.seg_end * D * sizeof(T)));
   const GBuf gv(v + base, (uint32_t)(t.seg_end * D * sizeof(T)));
@@ -58,6 +74,20 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T *__restrict__ q, 
   const int w0 = t.r_start + wave * 32 * QB;  // first query of this wave
   const bool wave_active = w0 < t.r_end;
   const int wave_last = min(w0 + 32 * QB, t.r_end) - 1;
+  const int kv_lo = t.seg_start;
+  const int kv_hi = min(t.r_end, t.seg_end);  // one past the last key any row here can see
+  const int ntile = (kv_hi - kv_lo + BN - 1) / BN;
+  const int jw = wave_active ? (wave_last - kv_lo) / BN + 1 : 0;  // tiles this wave needs
+
+  // Tiles past the end are still requested (they arrive as zeros into slots
+  // nobody reads), so every iteration issues the same number of copies and
+  // one fixed wait count covers the tiles an iteration needs.
+  auto issue_k = [&](int tile) { KTile::issue(gk, sK[tile % NS], kv_lo + tile * BN, wave, lane); };
+  auto issue_v = [&](int tile) { VTile::issue(gv, sV[tile % NS], kv_lo + tile * BN, wave, lane); };
+  issue_k(0);
+  issue_k(1);
+  issue_k(2);
+  issue_v(0);
 
   frag qf[QB][KB];
 #pragma unroll
@@ -66,7 +96,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T *__restrict__ q, 
     for (int kb = 0; kb < KB; ++kb) qf[qb][kb] = global_frag<T, D>(gq, w0 + 32 * qb + c, 16 * kb + 8 * hh);
 
   f32x16 oacc[QB][DB];
-  float m[QB], l[QB];  // running max (scaled, base 2) and this lane-half's partial sum
+  float m[QB], l[QB];  // reference max (scaled, base 2) and this lane-half's partial sum
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m[qb] = -INFINITY;
@@ -75,19 +105,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T *__restrict__ q, 
     for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x16{};
   }
 
-  const int kv_lo = t.seg_start;
-  const int kv_hi = min(t.r_end, t.seg_end);  // one past the last key any row here can see
-  const int ntile = (kv_hi - kv_lo + BN - 1) / BN;
-
-  Loader lk, lv;
-  lk.load(gk, kv_lo, tid);
-  lv.load(gv, kv_lo, tid);
-
-  // One key tile for this wave.  MASK selects the diagonal / segment-end
-  // variant; interior tiles take the branch-free path.
-  auto tile = [&]<bool MASK>(int k0) {
-    // S^T = K Q^T : rows are keys, columns (lanes) are queries.
-    f32x16 sacc[QB][NB];
+  // S^T of the key tile in ring slot `b`.
+  auto scores = [&](int b, f32x16 (&sacc)[QB][NB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -96,79 +115,163 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T *__restrict__ q, 
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const frag a = lds_frag<T>(sK + (nb * 32 + c) * G::kLdRM + 16 * kb + 8 * hh);
+        const frag a = swz_frag<T, D, KTile::kSW>(sK[b], nb * 32 + c, (16 * kb + 8 * hh) / KTile::kVec);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) E::mma(sacc[qb][nb], a, qf[qb][kb]);
       }
     }
+  };
 
-    // Online softmax in base 2: the maximum is taken on raw scores and the
-    // scale folded into one multiply-add before each exp2.
-    frag pf[QB][PB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int qi = w0 + 32 * qb + c;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if constexpr (MASK) {
-            const int key = k0 + 32 * nb + 8 * (r / 4) + 4 * hh + (r % 4);
-            sacc[qb][nb][r] = (key > qi || key >= t.seg_end) ? -INFINITY : sacc[qb][nb][r];
-          }
-          mx = fmaxf(mx, sacc[qb][nb][r]);
-        }
-      }
-      mx = fmaxf(mx, swap_halves(mx));
-      const float mnew = fmaxf(m[qb], mx * c2);
-      const float alpha = fast_exp2(m[qb] - mnew);
-      m[qb] = mnew;
-      float psum = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(sacc[qb][nb][r], c2, -mnew));
-          sacc[qb][nb][r] = p;
-          psum += p;
-        }
-      }
-      l[qb] = l[qb] * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
-#pragma unroll
-      for (int j = 0; j < PB; ++j) pf[qb][j] = E::pack(sacc[qb][j / 2], j % 2);
-    }
-
-    // O^T += V^T P^T : rows are head dims, columns (lanes) are queries.
+  // O^T += V^T P^T for the value tile in ring slot `b`.
+  auto pv = [&](int b, const frag (&pf)[QB][PB]) {
+    const TrRead<T, D> vr(sV[b], lane);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int j = 0; j < PB; ++j) {
-        const frag a = lds_frag<T>(sVt + (db * 32 + c) * G::kLdTR + 16 * j + 8 * hh);
+        const frag a = vr(16 * j, 32 * db);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) E::mma(oacc[qb][db], a, pf[qb][j]);
       }
     }
   };
 
-  for (int it = 0; it < ntile; ++it) {
-    const int k0 = kv_lo + it * BN;
-    __syncthreads();  // every wave is done with the previous tile
-    lk.store_rm(sK, tid);
-    lv.store_tr(sVt, tid);
-    __syncthreads();
-    if (it + 1 < ntile) {
-      lk.load(gk, k0 + BN, tid);
-      lv.load(gv, k0 + BN, tid);
+  auto apply_mask = [&](f32x16 (&sacc)[QB][NB], int k0) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qi = w0 + 32 * qb + c;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * nb + 8 * (r / 4) + 4 * hh + (r % 4);
+          sacc[qb][nb][r] = (key > qi || key >= t.seg_end) ? -INFINITY : sacc[qb][nb][r];
+        }
     }
-    if (!wave_active || k0 > wave_last) continue;  // tile entirely above this wave's diagonal
-    if ((k0 + BN - 1 > w0) || (k0 + BN > t.seg_end))
-      tile.template operator()<true>(k0);
-    else
-      tile.template operator()<false>(k0);
+  };
+
+  // Exponentials against the reference max, in place, then rounded and
+  // summed.  True when every row of the wave stayed in range.
+  auto softmax_fast = [&](f32x16 (&sacc)[QB][NB], frag (&pf)[QB][PB], float (&psum)[QB]) {
+    bool bad = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[qb][nb][r] = fast_exp2(__builtin_fmaf(sacc[qb][nb][r], c2, -m[qb]));
+      psum[qb] = 0.f;
+#pragma unroll
+      for (int j = 0; j < PB; ++j) pf[qb][j] = E::pack_sum(sacc[qb][j / 2], j % 2, psum[qb]);
+      bad = bad || !(psum[qb] <= kRescaleLimit);
+    }
+    return __builtin_amdgcn_ballot_w64(bad) == 0;
+  };
+
+  // Exact path: true row maximum, rescale of the running output and sum.
+  // Works in place on raw scores.
+  auto softmax_exact = [&](f32x16 (&sacc)[QB][NB], frag (&pf)[QB][PB], float (&psum)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][nb][r]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float mnew = fmaxf(m[qb], mx * c2);
+      const float alpha = fast_exp2(m[qb] - mnew);
+      m[qb] = mnew;
+      l[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[qb][nb][r] = fast_exp2(__builtin_fmaf(sacc[qb][nb][r], c2, -mnew));
+      psum[qb] = 0.f;
+#pragma unroll
+      for (int j = 0; j < PB; ++j) pf[qb][j] = E::pack_sum(sacc[qb][j / 2], j % 2, psum[qb]);
+    }
+  };
+
+  auto needs_mask = [&](int k0) { return (k0 + BN - 1 > w0) || (k0 + BN > t.seg_end); };
+
+  // Prologue: scores of tile 0 (this wave's copies of K0 done, then everyone's).
+  wait_vmcnt<3 * IPW>();
+  wg_barrier();
+  f32x16 snext[QB][NB];
+  if (jw > 0) {
+    scores(0, snext);
+    if (needs_mask(kv_lo)) apply_mask(snext, kv_lo);
   }
+
+  frag pprev[QB][PB];
+  bool have_prev = false;
+  for (int j = 0; j < ntile; ++j) {
+    const int k0 = kv_lo + j * BN;
+    // K(j+1) and V(j-1) were requested two iterations ago: wait for this
+    // wave's copies, then for everyone's.  The barrier also retires every
+    // read of K(j) and V(j-2), whose slots the next copies overwrite.
+    wait_vmcnt<2 * IPW>();
+    wg_barrier();
+    issue_k(j + 3);
+    issue_v(j + 1);
+
+    f32x16 scur[QB][NB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) scur[qb][nb] = snext[qb][nb];
+    const bool cur_active = j < jw;
+    const bool next_active = j + 1 < jw;
+    const bool next_mask = needs_mask(k0 + BN);
+    frag pcur[QB][PB];
+    float psum[QB];
+
+    // Scores of tile j again, from its key slot (rewritten only by the copy
+    // issued at the next iteration), for the exact path after an
+    // out-of-range fast pass.
+    auto redo_exact = [&]() {
+      scores(j % NS, scur);
+      if (needs_mask(k0)) apply_mask(scur, k0);
+      softmax_exact(scur, pcur, psum);
+    };
+    if (cur_active && next_active && have_prev && !next_mask) {
+      // Steady state: scores of tile j+1 and P V of tile j-1 on the matrix
+      // cores while the exponentials of tile j run.
+      scores((j + 1) % NS, snext);
+      pv((j + NS - 1) % NS, pprev);
+      if (!softmax_fast(scur, pcur, psum)) redo_exact();
+    } else {
+      if (have_prev) pv((j + NS - 1) % NS, pprev);
+      if (next_active) {
+        scores((j + 1) % NS, snext);
+        if (next_mask) apply_mask(snext, k0 + BN);
+      }
+      if (cur_active) {
+        if (m[0] == -INFINITY)
+          softmax_exact(scur, pcur, psum);
+        else if (!softmax_fast(scur, pcur, psum))
+          redo_exact();
+      }
+    }
+    if (cur_active) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        l[qb] += psum[qb];
+#pragma unroll
+        for (int jj = 0; jj < PB; ++jj) pprev[qb][jj] = pcur[qb][jj];
+      }
+    }
+    have_prev = cur_active;
+  }
+  if (have_prev) {
+    wait_vmcnt<2 * IPW>();  // V(ntile-1) was requested in the last iteration but one
+    wg_barrier();
+    pv((ntile - 1) % NS, pprev);
+  }
+  wait_vmcnt<0>();  // no copy may land in LDS after the workgroup retires
 
   if (!wave_active) return;
   const GBuf go(o + base, (uint32_t)(t.r_end * D * sizeof(float)));
@@ -192,9 +295,17 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T *__restrict__ q, 
 }
 
 // Tile shape per (dtype, D): queries per wave (32 * QB) and keys per tile (BN).
+// Two query blocks per wave would halve the LDS traffic per matrix-core step,
+// but with two score tiles live in the pipeline they leave one wave per SIMD;
+// measured slower at context 1024.
 template <typename T, int D> struct FwdCfg {
+#ifdef ATTN_FWD_QB
+  static constexpr int QB = ATTN_FWD_QB;
+  static constexpr int BN = ATTN_FWD_BN;
+#else
   static constexpr int QB = 1;
-  static constexpr int BN = 64;
+  static constexpr int BN = (sizeof(T) == 4 && D == 128) ? 32 : 64;  // LDS: 3-slot K and V rings
+#endif
 };
 
 template <typename T, int D, bool DOC>

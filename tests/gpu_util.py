@@ -73,8 +73,12 @@ def errors(got, ref):
 
 
 def compare(out, ref, dtype, heads=None, names=("o", "lse", "dq", "dk", "dv", "delta"), tag="",
-            max_abs_scale=1.0):
-    """Assert the GPU outputs match the oracle on the given heads (all if None)."""
+            rel_to_max=None):
+    """Assert the GPU outputs match the oracle on the given heads (all if None).
+
+    rel_to_max: if given, the max-abs bound of O/dQ/dK/dV is rel_to_max * max|ref|
+    instead of the fixed absolute bound (for inputs far outside the workloads'
+    scale, where bf16 rounding error grows with the magnitudes)."""
     tol = TOL[dtype]
     report = {}
     for name in names:
@@ -92,7 +96,7 @@ def compare(out, ref, dtype, heads=None, names=("o", "lse", "dq", "dk", "dv", "d
             # Delta is an intermediate: bounded by |dO| |O| accuracy, checked loosely
             assert ma <= 10 * tol["max_abs"], f"{tag} {name}: max-abs {ma:.3e}"
         else:
-            lim = tol["max_abs"] * max_abs_scale
+            lim = tol["max_abs"] if rel_to_max is None else rel_to_max * float(np.max(np.abs(r)))
             assert ma <= lim, f"{tag} {name}: max-abs {ma:.3e} > {lim}"
             if tol["rel_fro"] is not None:
                 assert rf <= tol["rel_fro"], f"{tag} {name}: rel-Frobenius {rf:.3e} > {tol['rel_fro']}"

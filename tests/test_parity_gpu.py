@@ -147,8 +147,10 @@ def test_large_logits():
     out = run_hip(x)
     ref = oracle(x)
     compare(out, ref, "bf16", names=("o", "lse", "dv"), tag="large logits")
-    # dQ and dK carry the 4x factor of K and Q: same relative accuracy, scaled absolute bound
-    compare(out, ref, "bf16", names=("dq", "dk"), tag="large logits grads", max_abs_scale=4.0)
+    # dS is rounded to bf16 before dS K and dS^T Q; with Q and K four times larger
+    # |dP|, |K| and |Q| grow with them, so the gradients' absolute error scales with
+    # their magnitude: bound it relative to max|ref| (plus relative Frobenius 1e-2).
+    compare(out, ref, "bf16", names=("dq", "dk"), tag="large logits grads", rel_to_max=2.0 ** -6)
 
 
 def test_nan_row_reaches_only_its_outputs():
