@@ -58,6 +58,12 @@ def parse():
     p.add_argument("--no-others", action="store_true", help="skip the other full-size workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time for the oracle sample")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="also run a plain fp32 elementwise kernel (negation) over MIB MiB, a known number of "
+                        "HBM bytes, to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; csv output) of "
+                        "'bench.py --no-others --copy-calibration MIB' into profiles/traffic.json")
     return p.parse_args()
 
 
@@ -177,6 +183,74 @@ def measured_traffic(kernel, workload):
     return None if ent is None else ent.get("bytes_per_launch")
 
 
+KERNEL_NAMES = {"attn_fwd_kernel": "fwd", "attn_bwd_preprocess_kernel": "pre",
+                "attn_bwd_dkdv_kernel": "dkdv", "attn_bwd_dq_kernel": "dq", "neg_kernel": "copy"}
+
+
+def copy_calibration(mib):
+    """A plain elementwise kernel of known HBM traffic: reads and writes mib MiB."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def _counter_rows(directory):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {directory}")
+    for path in files:
+        with open(path, newline="") as f:
+            yield from csv.DictReader(f)
+
+
+def _per_dispatch_kib(directory, counter):
+    """Mean counter value (KiB) per dispatch, for each kernel this bench launches."""
+    acc = {}
+    for row in _counter_rows(directory):
+        if row["Counter_Name"] != counter:
+            continue
+        name = next((v for k, v in KERNEL_NAMES.items() if k in row["Kernel_Name"]), None)
+        if name is None:
+            continue
+        d = acc.setdefault(name, {})
+        d[row["Dispatch_Id"]] = d.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in acc.items()}
+
+
+def write_traffic(fetch_dir, write_dir, workload, mib):
+    """HBM bytes per launch of each kernel: FETCH_SIZE + WRITE_SIZE (KiB per dispatch),
+    each divided by what the same counter reads for the calibration kernel relative to
+    its known traffic (mib MiB read, mib MiB written)."""
+    fetch = _per_dispatch_kib(fetch_dir, "FETCH_SIZE")
+    write = _per_dispatch_kib(write_dir, "WRITE_SIZE")
+    if "copy" not in fetch or "copy" not in write:
+        raise SystemExit("calibration kernel not found in the counter data")
+    known_kib = mib * 1024.0
+    f_fetch = fetch["copy"] / known_kib
+    f_write = write["copy"] / known_kib
+    kernels = {}
+    for k in ("fwd", "pre", "dkdv", "dq"):
+        if k in fetch and k in write:
+            fb = fetch[k] * 1024 / f_fetch
+            wb = write[k] * 1024 / f_write
+            kernels[k] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb,
+                          "raw_fetch_kib": fetch[k], "raw_write_kib": write[k]}
+    rec = {"sources_digest": sources_digest(), "calibration": {
+        "kernel": "torch.neg over fp32", "mib": mib, "fetch_factor": f_fetch, "write_factor": f_write},
+        "kernels": {workload: kernels}}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
 def roofline(w, times):
     """The dominant kernel (most time per step) against its roofline."""
     peak = PEAK_BF16_TFLOPS if w.cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -244,6 +318,10 @@ def measure(name, steps, warmup, reps):
 
 def main():
     a = parse()
+    if a.write_traffic:
+        rec = write_traffic(*a.write_traffic, a.workload, a.copy_calibration or 256)
+        print(json.dumps(rec, indent=1))
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported in this build "
               "(attention shards by batch and head with no communication; see the design notes)",
@@ -302,6 +380,8 @@ def main():
         "by_workload": by_workload,
     }
     print(json.dumps(line), flush=True)
+    if a.copy_calibration:
+        copy_calibration(a.copy_calibration)
 
 
 if __name__ == "__main__":

@@ -34,12 +34,11 @@ namespace attn {
 
 constexpr float kRescaleLimit = 1.8446744e19f;  // 2^64: larger row sums take the exact path
 
-template <typename T, int D, int QB, int BN, bool DOC>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
+template <typename T, int D, int NW, int QB, int BN, bool DOC>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                        const T *__restrict__ v, float *__restrict__ o,
                                                        float *__restrict__ lse, int S, float c2,
                                                        const int32_t *__restrict__ cu, int ntiles) {
-  constexpr int NW = 4;
   constexpr int NT = NW * kWaveSize;
   constexpr int BM = NW * 32 * QB;  // query rows per workgroup
   constexpr int KB = D / 16;        // k-blocks over the head dimension
@@ -294,15 +293,19 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T *__restrict__ q, 
   }
 }
 
-// Tile shape per (dtype, D): queries per wave (32 * QB) and keys per tile (BN).
-// Two query blocks per wave would halve the LDS traffic per matrix-core step,
-// but with two score tiles live in the pipeline they leave one wave per SIMD;
-// measured slower at context 1024.
+// Tile shape per (dtype, D): waves per workgroup (NW), queries per wave (32 * QB)
+// and keys per tile (BN).  Two query blocks per wave would halve the LDS traffic
+// per matrix-core step, but with two score tiles live in the pipeline they leave
+// one wave per SIMD; eight waves sharing one K/V ring (two per SIMD) halve the
+// copy traffic per CU but give half as many workgroups.  Both measured slower at
+// context 1024 than four waves with one query block each.
 template <typename T, int D> struct FwdCfg {
 #ifdef ATTN_FWD_QB
+  static constexpr int NW = (sizeof(T) == 2 && D == 64) ? ATTN_FWD_NW : 4;
   static constexpr int QB = ATTN_FWD_QB;
-  static constexpr int BN = ATTN_FWD_BN;
+  static constexpr int BN = D == 32 ? 64 : (sizeof(T) == 4 && D == 128) ? 32 : ATTN_FWD_BN;
 #else
+  static constexpr int NW = 4;
   static constexpr int QB = 1;
   static constexpr int BN = (sizeof(T) == 4 && D == 128) ? 32 : 64;  // LDS: 3-slot K and V rings
 #endif
@@ -312,9 +315,10 @@ template <typename T, int D, bool DOC>
 static hipError_t launch_fwd_t(const Args &a) {
   constexpr int QB = FwdCfg<T, D>::QB;
   constexpr int BN = FwdCfg<T, D>::BN;
-  constexpr int BM = 4 * 32 * QB;
+  constexpr int NW = FwdCfg<T, D>::NW;
+  constexpr int BM = NW * 32 * QB;
   const float c2 = a.scale * kLog2e;
-  dim3 block(256);
+  dim3 block(NW * 64);
   dim3 grid;
   int ntiles;
   if (DOC) {
@@ -324,7 +328,7 @@ static hipError_t launch_fwd_t(const Args &a) {
     ntiles = (a.S + BM - 1) / BM;
     grid = dim3(ntiles * a.B * a.H);
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, QB, BN, DOC>), grid, block, 0, a.stream,
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW, QB, BN, DOC>), grid, block, 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
                      a.o, a.lse, a.S, c2, a.cu_seqlens, ntiles);
   return hipGetLastError();
