@@ -37,6 +37,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaveSize = 64;
+
+// Pointers into LDS carry their address space explicitly: the compiler then
+// keeps track of which LDS object an access touches, and waits for an
+// in-flight direct-to-LDS copy only when a read can overlap its destination.
+template <typename T> using lds_t = __attribute__((address_space(3))) T;
+template <typename T> __device__ __forceinline__ lds_t<T> *lds_cast(T *p) { return (lds_t<T> *)p; }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -96,6 +102,10 @@ template <typename T>
 __device__ __forceinline__ typename Elem<T>::frag lds_frag(const T *p) {
   return *reinterpret_cast<const typename Elem<T>::frag *>(p);
 }
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::frag lds_frag(const lds_t<T> *p) {
+  return *(const lds_t<typename Elem<T>::frag> *)p;
+}
 
 // Fragment of the TRANSPOSE of a row-major LDS tile (row stride LD elements),
 // in "accum" slot order: lane (h, c) receives
@@ -111,16 +121,24 @@ template <typename T, int LD> struct TrRead;
 
 template <int LD> struct TrRead<bf16, LD> {
   using frag = bf16x8;
-  const bf16 *base;  // this lane's source address for row0 = col0 = 0
-  __device__ __forceinline__ TrRead(const bf16 *tile, int lane) {
+  const lds_t<bf16> *base;   // this lane's source address for row0 = col0 = 0
+  const lds_t<bf16> *base8;  // ... and for the rows 8 further down
+  __device__ __forceinline__ TrRead(const lds_t<bf16> *tile, int lane) {
     const int g = lane / 16, i = lane % 16, h = g / 2;
-    base = tile + (4 * h + i / 4) * LD + 16 * (g % 2) + 4 * (i % 4);
+    const int off = (4 * h + i / 4) * LD + 16 * (g % 2) + 4 * (i % 4);
+    // The second read's offset is kept opaque to constant folding: folded
+    // into an immediate, the compiler loses track of which LDS object the
+    // read belongs to and waits for every direct-to-LDS copy in flight.
+    int off8 = off + 8 * LD;
+    asm volatile("" : "+v"(off8));
+    base = tile + off;
+    base8 = tile + off8;
   }
+  __device__ __forceinline__ TrRead(const bf16 *tile, int lane) : TrRead(lds_cast(const_cast<bf16 *>(tile)), lane) {}
   __device__ __forceinline__ frag operator()(int row0, int col0) const {
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const bf16 *p = base + row0 * LD + col0;
-    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
-    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 8 * LD));
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + row0 * LD + col0));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base8 + row0 * LD + col0));
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     s16x8 v;
 #pragma unroll
@@ -134,12 +152,13 @@ template <int LD> struct TrRead<bf16, LD> {
 
 template <int LD> struct TrRead<float, LD> {
   using frag = f32x8;
-  const float *base;
-  __device__ __forceinline__ TrRead(const float *tile, int lane) {
+  const lds_t<float> *base;
+  __device__ __forceinline__ TrRead(const lds_t<float> *tile, int lane) {
     base = tile + 4 * (lane / 32) * LD + lane % 32;
   }
+  __device__ __forceinline__ TrRead(const float *tile, int lane) : TrRead(lds_cast(const_cast<float *>(tile)), lane) {}
   __device__ __forceinline__ frag operator()(int row0, int col0) const {
-    const float *p = base + row0 * LD + col0;
+    const lds_t<float> *p = base + row0 * LD + col0;
     frag f;
 #pragma unroll
     for (int s = 0; s < 8; ++s) f[s] = p[(8 * (s / 4) + s % 4) * LD];
@@ -266,7 +285,7 @@ template <typename T, int R, int D, int NT, bool SWIZZLE> struct DmaTile {
   static constexpr int kPerWave = kBlocks / (NT / kWaveSize);  // copy instructions per wave
   static_assert(R * kCPR % NT == 0, "tile must split evenly over the waves");
 
-  __device__ __forceinline__ static void issue(const GBuf &g, T *tile, int r0, int wave, int lane) {
+  __device__ __forceinline__ static void issue(const GBuf &g, lds_t<T> *tile, int r0, int wave, int lane) {
     typedef __attribute__((address_space(3))) void lds_void;
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
@@ -284,17 +303,17 @@ template <typename T, int R, int D, int NT, bool SWIZZLE> struct DmaTile {
 // Row fragment of a swizzled tile: 8 slots of row `row` starting at column
 // 8*(2*kb + hh) (natural slot order), for lanes whose row index is `row`.
 template <typename T, int D, int SW>
-__device__ __forceinline__ typename Elem<T>::frag swz_frag(const T *tile, int row, int chunk0) {
+__device__ __forceinline__ typename Elem<T>::frag swz_frag(const lds_t<T> *tile, int row, int chunk0) {
   using frag = typename Elem<T>::frag;
   constexpr int kVec = 16 / sizeof(T);
   // (chunk ^ s) * kVec == (chunk * kVec) ^ (s * kVec): kVec is a power of two
   const int sw = (row & SW) * kVec;
   const int rbase = row * D;
   if constexpr (sizeof(T) == 2) {
-    return *reinterpret_cast<const frag *>(tile + rbase + ((chunk0 * kVec) ^ sw));
+    return *(const lds_t<frag> *)(tile + rbase + ((chunk0 * kVec) ^ sw));
   } else {
-    const f32x4 a = *reinterpret_cast<const f32x4 *>(tile + rbase + ((chunk0 * kVec) ^ sw));
-    const f32x4 b = *reinterpret_cast<const f32x4 *>(tile + rbase + (((chunk0 + 1) * kVec) ^ sw));
+    const f32x4 a = *(const lds_t<f32x4> *)(tile + rbase + ((chunk0 * kVec) ^ sw));
+    const f32x4 b = *(const lds_t<f32x4> *)(tile + rbase + (((chunk0 + 1) * kVec) ^ sw));
     frag f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

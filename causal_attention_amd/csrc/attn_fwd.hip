@@ -34,27 +34,29 @@ namespace attn {
 
 constexpr float kRescaleLimit = 1.8446744e19f;  // 2^64: larger row sums take the exact path
 
-template <typename T, int D, int NW, int QB, int BN, bool DOC>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                                                       const T *__restrict__ v, float *__restrict__ o,
-                                                       float *__restrict__ lse, int S, float c2,
-                                                       const int32_t *__restrict__ cu, int ntiles) {
+template <typename T, int D, int NW, int BN, int MINB, bool DOC>
+__global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                                 const T *__restrict__ v, float *__restrict__ o,
+                                                                 float *__restrict__ lse, int S, float c2,
+                                                                 const int32_t *__restrict__ cu, int ntiles) {
   constexpr int NT = NW * kWaveSize;
-  constexpr int BM = NW * 32 * QB;  // query rows per workgroup
-  constexpr int KB = D / 16;        // k-blocks over the head dimension
-  constexpr int DB = D / 32;        // 32-row blocks of O^T
-  constexpr int NB = BN / 32;       // 32-key blocks per tile
-  constexpr int PB = BN / 16;       // k-blocks over the keys of a tile
-  constexpr int NS = 3;             // LDS ring slots for K and for V
+  constexpr int BM = NW * 32;  // query rows per workgroup
+  constexpr int KB = D / 16;   // k-blocks over the head dimension
+  constexpr int DB = D / 32;   // 32-row blocks of O^T
+  constexpr int NB = BN / 32;  // 32-key blocks per tile
+  constexpr int PB = BN / 16;  // k-blocks over the keys of a tile
   using E = Elem<T>;
   using frag = typename E::frag;
   using KTile = DmaTile<T, BN, D, NT, true>;   // read as row fragments: swizzled
   using VTile = DmaTile<T, BN, D, NT, false>;  // read through the transposing load
-  constexpr int IPW = KTile::kPerWave;         // copy instructions per wave per tile
-  static_assert(VTile::kPerWave == IPW, "K and V tiles have the same shape");
 
-  __shared__ __attribute__((aligned(1024))) T sK[NS][BN * D];
-  __shared__ __attribute__((aligned(1024))) T sV[NS][BN * D];
+  // Two ring slots for K and for V, each its own LDS object: the slot an
+  // access touches is known at compile time (the loop is unrolled by two),
+  // so reading one slot never waits for the copy in flight into the other.
+  __shared__ __attribute__((aligned(1024))) T sK0[BN * D];
+  __shared__ __attribute__((aligned(1024))) T sK1[BN * D];
+  __shared__ __attribute__((aligned(1024))) T sV0[BN * D];
+  __shared__ __attribute__((aligned(1024))) T sV1[BN * D];
 
   const RowTile t = DOC ? doc_tile(cu, blockIdx.x, gridDim.x, blockIdx.y, blockIdx.z, BM, true)
                         : causal_tile(blockIdx.x, gridDim.x, ntiles, BM, S, true);
@@ -70,253 +72,175 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const T *__restrict__
   const GBuf gk(k + base, (uint32_t)(t.seg_end * D * sizeof(T)));
   const GBuf gv(v + base, (uint32_t)(t.seg_end * D * sizeof(T)));
 
-  const int w0 = t.r_start + wave * 32 * QB;  // first query of this wave
+  const int w0 = t.r_start + wave * 32;  // first query of this wave
   const bool wave_active = w0 < t.r_end;
-  const int wave_last = min(w0 + 32 * QB, t.r_end) - 1;
+  const int wave_last = min(w0 + 32, t.r_end) - 1;
   const int kv_lo = t.seg_start;
   const int kv_hi = min(t.r_end, t.seg_end);  // one past the last key any row here can see
   const int ntile = (kv_hi - kv_lo + BN - 1) / BN;
   const int jw = wave_active ? (wave_last - kv_lo) / BN + 1 : 0;  // tiles this wave needs
 
-  // Tiles past the end are still requested (they arrive as zeros into slots
-  // nobody reads), so every iteration issues the same number of copies and
-  // one fixed wait count covers the tiles an iteration needs.
-  auto issue_k = [&](int tile) { KTile::issue(gk, sK[tile % NS], kv_lo + tile * BN, wave, lane); };
-  auto issue_v = [&](int tile) { VTile::issue(gv, sV[tile % NS], kv_lo + tile * BN, wave, lane); };
-  issue_k(0);
-  issue_k(1);
-  issue_k(2);
-  issue_v(0);
+  auto kslot = [&]<int P>() { return lds_cast(P == 0 ? sK0 : sK1); };
+  auto vslot = [&]<int P>() { return lds_cast(P == 0 ? sV0 : sV1); };
+  auto issue = [&]<int P>(int tile) {
+    KTile::issue(gk, kslot.template operator()<P>(), kv_lo + tile * BN, wave, lane);
+    VTile::issue(gv, vslot.template operator()<P>(), kv_lo + tile * BN, wave, lane);
+  };
+  issue.template operator()<0>(0);
 
-  frag qf[QB][KB];
+  frag qf[KB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) qf[qb][kb] = global_frag<T, D>(gq, w0 + 32 * qb + c, 16 * kb + 8 * hh);
+  for (int kb = 0; kb < KB; ++kb) qf[kb] = global_frag<T, D>(gq, w0 + c, 16 * kb + 8 * hh);
 
-  f32x16 oacc[QB][DB];
-  float m[QB], l[QB];  // reference max (scaled, base 2) and this lane-half's partial sum
+  f32x16 oacc[DB];
+  float m = -INFINITY;  // reference max (scaled, base 2)
+  float l = 0.f;        // this lane-half's partial row sum
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY;
-    l[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x16{};
-  }
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
 
-  // S^T of the key tile in ring slot `b`.
-  auto scores = [&](int b, f32x16 (&sacc)[QB][NB]) {
+  // S^T = K Q^T for the key tile in `ks`.
+  auto scores = [&](const lds_t<T> *ks, f32x16 (&sacc)[NB]) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int nb = 0; nb < NB; ++nb) sacc[nb] = f32x16{};
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sacc[qb][nb] = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const frag a = swz_frag<T, D, KTile::kSW>(sK[b], nb * 32 + c, (16 * kb + 8 * hh) / KTile::kVec);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) E::mma(sacc[qb][nb], a, qf[qb][kb]);
+        const frag a = swz_frag<T, D, KTile::kSW>(ks, nb * 32 + c, (16 * kb + 8 * hh) / KTile::kVec);
+        E::mma(sacc[nb], a, qf[kb]);
       }
-    }
   };
 
-  // O^T += V^T P^T for the value tile in ring slot `b`.
-  auto pv = [&](int b, const frag (&pf)[QB][PB]) {
-    const TrRead<T, D> vr(sV[b], lane);
+  // O^T += V^T P^T for the value tile in `vs`.
+  auto pv = [&](const lds_t<T> *vs, const frag (&pf)[PB]) {
+    const TrRead<T, D> vr(vs, lane);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int j = 0; j < PB; ++j) {
-        const frag a = vr(16 * j, 32 * db);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) E::mma(oacc[qb][db], a, pf[qb][j]);
-      }
-    }
+      for (int j = 0; j < PB; ++j) E::mma(oacc[db], vr(16 * j, 32 * db), pf[j]);
   };
 
-  auto apply_mask = [&](f32x16 (&sacc)[QB][NB], int k0) {
+  auto apply_mask = [&](f32x16 (&sacc)[NB], int k0) {
+    const int qi = w0 + c;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int qi = w0 + 32 * qb + c;
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * nb + 8 * (r / 4) + 4 * hh + (r % 4);
-          sacc[qb][nb][r] = (key > qi || key >= t.seg_end) ? -INFINITY : sacc[qb][nb][r];
-        }
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 32 * nb + 8 * (r / 4) + 4 * hh + (r % 4);
+        sacc[nb][r] = (key > qi || key >= t.seg_end) ? -INFINITY : sacc[nb][r];
+      }
   };
 
   // Exponentials against the reference max, in place, then rounded and
   // summed.  True when every row of the wave stayed in range.
-  auto softmax_fast = [&](f32x16 (&sacc)[QB][NB], frag (&pf)[QB][PB], float (&psum)[QB]) {
-    bool bad = false;
+  auto softmax_fast = [&](f32x16 (&sacc)[NB], frag (&pf)[PB], float &psum) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int r = 0; r < 16; ++r) sacc[nb][r] = fast_exp2(__builtin_fmaf(sacc[nb][r], c2, -m));
+    psum = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[qb][nb][r] = fast_exp2(__builtin_fmaf(sacc[qb][nb][r], c2, -m[qb]));
-      psum[qb] = 0.f;
-#pragma unroll
-      for (int j = 0; j < PB; ++j) pf[qb][j] = E::pack_sum(sacc[qb][j / 2], j % 2, psum[qb]);
-      bad = bad || !(psum[qb] <= kRescaleLimit);
-    }
-    return __builtin_amdgcn_ballot_w64(bad) == 0;
+    for (int j = 0; j < PB; ++j) pf[j] = E::pack_sum(sacc[j / 2], j % 2, psum);
+    return __builtin_amdgcn_ballot_w64(!(psum <= kRescaleLimit)) == 0;
   };
 
   // Exact path: true row maximum, rescale of the running output and sum.
-  // Works in place on raw scores.
-  auto softmax_exact = [&](f32x16 (&sacc)[QB][NB], frag (&pf)[QB][PB], float (&psum)[QB]) {
+  auto softmax_exact = [&](f32x16 (&sacc)[NB], frag (&pf)[PB], float &psum) {
+    float mx = -INFINITY;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
+    mx = fmaxf(mx, swap_halves(mx));
+    const float mnew = fmaxf(m, mx * c2);
+    const float alpha = fast_exp2(m - mnew);
+    m = mnew;
+    l *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][nb][r]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float mnew = fmaxf(m[qb], mx * c2);
-      const float alpha = fast_exp2(m[qb] - mnew);
-      m[qb] = mnew;
-      l[qb] *= alpha;
+    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int r = 0; r < 16; ++r) sacc[nb][r] = fast_exp2(__builtin_fmaf(sacc[nb][r], c2, -mnew));
+    psum = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[qb][nb][r] = fast_exp2(__builtin_fmaf(sacc[qb][nb][r], c2, -mnew));
-      psum[qb] = 0.f;
-#pragma unroll
-      for (int j = 0; j < PB; ++j) pf[qb][j] = E::pack_sum(sacc[qb][j / 2], j % 2, psum[qb]);
-    }
+    for (int j = 0; j < PB; ++j) pf[j] = E::pack_sum(sacc[j / 2], j % 2, psum);
   };
 
-  auto needs_mask = [&](int k0) { return (k0 + BN - 1 > w0) || (k0 + BN > t.seg_end); };
-
-  // Prologue: scores of tile 0 (this wave's copies of K0 done, then everyone's).
-  wait_vmcnt<3 * IPW>();
-  wg_barrier();
-  f32x16 snext[QB][NB];
-  if (jw > 0) {
-    scores(0, snext);
-    if (needs_mask(kv_lo)) apply_mask(snext, kv_lo);
-  }
-
-  frag pprev[QB][PB];
-  bool have_prev = false;
-  for (int j = 0; j < ntile; ++j) {
+  // One key tile in ring slot P: wait for its copies (issued one iteration
+  // ago; this wave's own, then everyone's), request the next tile into the
+  // other slot (the barrier also retires every read of that slot), then
+  // scores, softmax and P V.
+  auto step = [&]<int P>(int j) {
+    wait_vmcnt<0>();
+    wg_barrier();
+    if (j + 1 < ntile) issue.template operator()<1 - P>(j + 1);
+    if (j >= jw) return;
     const int k0 = kv_lo + j * BN;
-    // K(j+1) and V(j-1) were requested two iterations ago: wait for this
-    // wave's copies, then for everyone's.  The barrier also retires every
-    // read of K(j) and V(j-2), whose slots the next copies overwrite.
-    wait_vmcnt<2 * IPW>();
-    wg_barrier();
-    issue_k(j + 3);
-    issue_v(j + 1);
-
-    f32x16 scur[QB][NB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) scur[qb][nb] = snext[qb][nb];
-    const bool cur_active = j < jw;
-    const bool next_active = j + 1 < jw;
-    const bool next_mask = needs_mask(k0 + BN);
-    frag pcur[QB][PB];
-    float psum[QB];
-
-    // Scores of tile j again, from its key slot (rewritten only by the copy
-    // issued at the next iteration), for the exact path after an
-    // out-of-range fast pass.
-    auto redo_exact = [&]() {
-      scores(j % NS, scur);
-      if (needs_mask(k0)) apply_mask(scur, k0);
-      softmax_exact(scur, pcur, psum);
-    };
-    if (cur_active && next_active && have_prev && !next_mask) {
-      // Steady state: scores of tile j+1 and P V of tile j-1 on the matrix
-      // cores while the exponentials of tile j run.
-      scores((j + 1) % NS, snext);
-      pv((j + NS - 1) % NS, pprev);
-      if (!softmax_fast(scur, pcur, psum)) redo_exact();
-    } else {
-      if (have_prev) pv((j + NS - 1) % NS, pprev);
-      if (next_active) {
-        scores((j + 1) % NS, snext);
-        if (next_mask) apply_mask(snext, k0 + BN);
-      }
-      if (cur_active) {
-        if (m[0] == -INFINITY)
-          softmax_exact(scur, pcur, psum);
-        else if (!softmax_fast(scur, pcur, psum))
-          redo_exact();
-      }
+    const bool masked = (k0 + BN - 1 > w0) || (k0 + BN > t.seg_end);
+    const lds_t<T> *ks = kslot.template operator()<P>();
+    f32x16 sacc[NB];
+    frag pf[PB];
+    float psum;
+    scores(ks, sacc);
+    if (masked) apply_mask(sacc, k0);
+    if (m == -INFINITY) {
+      softmax_exact(sacc, pf, psum);
+    } else if (!softmax_fast(sacc, pf, psum)) {
+      // a row sum left the safe range: recompute the scores from the key
+      // tile (still in its slot) and take the exact path
+      scores(ks, sacc);
+      if (masked) apply_mask(sacc, k0);
+      softmax_exact(sacc, pf, psum);
     }
-    if (cur_active) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        l[qb] += psum[qb];
-#pragma unroll
-        for (int jj = 0; jj < PB; ++jj) pprev[qb][jj] = pcur[qb][jj];
-      }
-    }
-    have_prev = cur_active;
+    l += psum;
+    pv(vslot.template operator()<P>(), pf);
+  };
+
+  for (int j = 0; j < ntile; j += 2) {
+    step.template operator()<0>(j);
+    if (j + 1 < ntile) step.template operator()<1>(j + 1);
   }
-  if (have_prev) {
-    wait_vmcnt<2 * IPW>();  // V(ntile-1) was requested in the last iteration but one
-    wg_barrier();
-    pv((ntile - 1) % NS, pprev);
-  }
-  wait_vmcnt<0>();  // no copy may land in LDS after the workgroup retires
 
   if (!wave_active) return;
   const GBuf go(o + base, (uint32_t)(t.r_end * D * sizeof(float)));
+  const int qi = w0 + c;
+  const float lt = l + swap_halves(l);
+  const float inv = 1.0f / lt;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = w0 + 32 * qb + c;
-    const float lt = l[qb] + swap_halves(l[qb]);
-    const float inv = 1.0f / lt;
+  for (int db = 0; db < DB; ++db) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int g = 0; g < 4; ++g) {
+      f32x4 val;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 val;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) val[i] = oacc[qb][db][4 * g + i] * inv;
-        go.store16(val, (uint32_t)(qi * D + db * 32 + 8 * g + 4 * hh) * sizeof(float));
-      }
+      for (int i = 0; i < 4; ++i) val[i] = oacc[db][4 * g + i] * inv;
+      go.store16(val, (uint32_t)(qi * D + db * 32 + 8 * g + 4 * hh) * sizeof(float));
     }
-    if (lse != nullptr && hh == 0 && qi < t.r_end) lse[(size_t)t.head * S + qi] = (m[qb] + __log2f(lt)) * kLn2;
   }
+  if (lse != nullptr && hh == 0 && qi < t.r_end) lse[(size_t)t.head * S + qi] = (m + __log2f(lt)) * kLn2;
 }
 
-// Tile shape per (dtype, D): waves per workgroup (NW), queries per wave (32 * QB)
-// and keys per tile (BN).  Two query blocks per wave would halve the LDS traffic
-// per matrix-core step, but with two score tiles live in the pipeline they leave
-// one wave per SIMD; eight waves sharing one K/V ring (two per SIMD) halve the
-// copy traffic per CU but give half as many workgroups.  Both measured slower at
-// context 1024 than four waves with one query block each.
+// Tile shape per (dtype, D): waves per workgroup (NW, 32 queries each), keys
+// per tile (BN) and the minimum number of workgroups per CU the register
+// allocation must allow (MINB).
 template <typename T, int D> struct FwdCfg {
-#ifdef ATTN_FWD_QB
-  static constexpr int NW = (sizeof(T) == 2 && D == 64) ? ATTN_FWD_NW : 4;
-  static constexpr int QB = ATTN_FWD_QB;
-  static constexpr int BN = D == 32 ? 64 : (sizeof(T) == 4 && D == 128) ? 32 : ATTN_FWD_BN;
+#ifdef ATTN_FWD_BN
+  static constexpr int NW = ATTN_FWD_NW;
+  static constexpr int BN = (sizeof(T) == 4 && D == 128) ? 32 : ATTN_FWD_BN;
+  static constexpr int MINB = ATTN_FWD_MINB;
 #else
   static constexpr int NW = 4;
-  static constexpr int QB = 1;
-  static constexpr int BN = (sizeof(T) == 4 && D == 128) ? 32 : 64;  // LDS: 3-slot K and V rings
+  static constexpr int BN = (sizeof(T) == 4 && D == 128) ? 32 : 64;
+  static constexpr int MINB = 1;
 #endif
 };
 
 template <typename T, int D, bool DOC>
 static hipError_t launch_fwd_t(const Args &a) {
-  constexpr int QB = FwdCfg<T, D>::QB;
   constexpr int BN = FwdCfg<T, D>::BN;
   constexpr int NW = FwdCfg<T, D>::NW;
-  constexpr int BM = NW * 32 * QB;
+  constexpr int MINB = FwdCfg<T, D>::MINB;
+  constexpr int BM = NW * 32;
   const float c2 = a.scale * kLog2e;
   dim3 block(NW * 64);
   dim3 grid;
@@ -328,7 +252,7 @@ static hipError_t launch_fwd_t(const Args &a) {
     ntiles = (a.S + BM - 1) / BM;
     grid = dim3(ntiles * a.B * a.H);
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW, QB, BN, DOC>), grid, block, 0, a.stream,
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW, BN, MINB, DOC>), grid, block, 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
                      a.o, a.lse, a.S, c2, a.cu_seqlens, ntiles);
   return hipGetLastError();
