@@ -67,30 +67,35 @@ __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const float *_
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.  A workgroup owns BN = 4 * 32 * KBW keys of one head and loops over
-// query tiles of BMQ rows from its first key to the end of the sequence (or
-// document).
-template <typename T, int D, int KBW, int BMQ, bool DOC>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+// dK, dV.  A workgroup owns BN = 128 keys of one head (32 per wave) and loops
+// over query tiles of BMQ rows from its first key to the end of the sequence
+// (or document).  Q and dO tiles, with their LSE and Delta, arrive by direct
+// global->LDS copies into two ring slots (separate LDS objects, loop unrolled
+// by two) one iteration ahead; Q and dO are read both as row fragments and,
+// through the transposing load, as Q^T and dO^T.
+template <typename T, int D, int BMQ, int MINB, bool DOC>
+__global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, float *__restrict__ dk,
     float *__restrict__ dv, int S, float c2, float scale, const int32_t *__restrict__ cu, int ntiles) {
   constexpr int NW = 4;
   constexpr int NT = NW * kWaveSize;
-  constexpr int BN = NW * 32 * KBW;  // keys per workgroup
+  constexpr int BN = NW * 32;  // keys per workgroup
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
-  constexpr int QB = BMQ / 32;       // 32-query blocks per tile
-  constexpr int PB = BMQ / 16;       // k-blocks over the queries of a tile
+  constexpr int QB = BMQ / 32;  // 32-query blocks per tile
   using E = Elem<T>;
   using frag = typename E::frag;
-  constexpr int LD = RowStride<T, D>::kPadded;  // read both as rows and transposed
-  using Loader = TileLoader<T, BMQ, D, NT>;
+  using QTile = DmaTile<T, BMQ, D, NT, true>;
 
-  __shared__ __attribute__((aligned(16))) T sQ[BMQ * LD];
-  __shared__ __attribute__((aligned(16))) T sdO[BMQ * LD];
-  __shared__ __attribute__((aligned(16))) float sL[BMQ];  // LSE * log2(e); +inf past the end
-  __shared__ __attribute__((aligned(16))) float sD[BMQ];  // Delta; 0 past the end
+  __shared__ __attribute__((aligned(1024))) T sQ0[BMQ * D];
+  __shared__ __attribute__((aligned(1024))) T sQ1[BMQ * D];
+  __shared__ __attribute__((aligned(1024))) T sO0[BMQ * D];  // dO
+  __shared__ __attribute__((aligned(1024))) T sO1[BMQ * D];
+  __shared__ __attribute__((aligned(256))) float sL0[64];    // LSE (natural log)
+  __shared__ __attribute__((aligned(256))) float sL1[64];
+  __shared__ __attribute__((aligned(256))) float sD0[64];    // Delta
+  __shared__ __attribute__((aligned(256))) float sD1[64];
 
   const RowTile t = DOC ? doc_tile(cu, blockIdx.x, gridDim.x, blockIdx.y, blockIdx.z, BN, false)
                         : causal_tile(blockIdx.x, gridDim.x, ntiles, BN, S, false);
@@ -103,6 +108,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const int c = lane % 32;
   const size_t base = (size_t)t.head * S * D;
   const size_t rbase = (size_t)t.head * S;
+  // Queries past the segment read as zeros (Q, dO, LSE, Delta all 0): their
+  // P is 1 but dO and Q are 0, so they add nothing to dV or dK.
   const GBuf gq(q + base, (uint32_t)(t.seg_end * D * sizeof(T)));
   const GBuf gdo(dO + base, (uint32_t)(t.seg_end * D * sizeof(T)));
   const GBuf gk(k + base, (uint32_t)(t.r_end * D * sizeof(T)));
@@ -110,189 +117,157 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const GBuf glse(lse + rbase, (uint32_t)(t.seg_end * sizeof(float)));
   const GBuf gdel(delta + rbase, (uint32_t)(t.seg_end * sizeof(float)));
 
-  const int w0 = t.r_start + wave * 32 * KBW;  // first key of this wave
+  const int w0 = t.r_start + wave * 32;  // first key of this wave
   const bool wave_active = w0 < t.r_end;
-  const int wave_last = min(w0 + 32 * KBW, t.r_end) - 1;
-
-  frag kf[KBW][KB], vf[KBW][KB];
-#pragma unroll
-  for (int kw = 0; kw < KBW; ++kw)
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      kf[kw][kb] = global_frag<T, D>(gk, w0 + 32 * kw + c, 16 * kb + 8 * hh);
-      vf[kw][kb] = global_frag<T, D>(gv, w0 + 32 * kw + c, 16 * kb + 8 * hh);
-    }
-
-  f32x16 dkacc[KBW][DB], dvacc[KBW][DB];
-#pragma unroll
-  for (int kw = 0; kw < KBW; ++kw)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      dkacc[kw][db] = f32x16{};
-      dvacc[kw][db] = f32x16{};
-    }
-
+  const int wave_last = min(w0 + 32, t.r_end) - 1;
+  const int key = w0 + c;
   const int q_lo = t.r_start;  // the first query that sees any of these keys
-  const int q_hi = t.seg_end;
-  const int ntile = (q_hi - q_lo + BMQ - 1) / BMQ;
+  const int ntile = (t.seg_end - q_lo + BMQ - 1) / BMQ;
 
-  // Per-row statistics of the next query tile: LSE (to base 2) and Delta.
-  float lval = 0.f, dval = 0.f;
-  // Every thread loads (rows past the end read 0); threads tid < BMQ publish.
-  auto load_stats = [&](int q0) {
-    const int row = q0 + tid % BMQ;
-    const float lv = glse.load4((uint32_t)row * 4);
-    dval = gdel.load4((uint32_t)row * 4);
-    lval = row < q_hi ? lv * kLog2e : INFINITY;
+  auto qslot = [&]<int P>() { return lds_cast(P == 0 ? sQ0 : sQ1); };
+  auto oslot = [&]<int P>() { return lds_cast(P == 0 ? sO0 : sO1); };
+  auto lslot = [&]<int P>() { return lds_cast(P == 0 ? sL0 : sL1); };
+  auto dslot = [&]<int P>() { return lds_cast(P == 0 ? sD0 : sD1); };
+  auto issue = [&]<int P>(int it) {
+    const int q0 = q_lo + it * BMQ;
+    QTile::issue(gq, qslot.template operator()<P>(), q0, wave, lane);
+    QTile::issue(gdo, oslot.template operator()<P>(), q0, wave, lane);
+    if (wave == 0) dma_vec64(glse, lslot.template operator()<P>(), q0, lane);
+    if (wave == 1) dma_vec64(gdel, dslot.template operator()<P>(), q0, lane);
   };
+  issue.template operator()<0>(0);
 
-  Loader lq, ldo;
-  lq.load(gq, q_lo, tid);
-  ldo.load(gdo, q_lo, tid);
-  load_stats(q_lo);
-
-  const TrRead<T, LD> trq(sQ, lane);
-  const TrRead<T, LD> trdo(sdO, lane);
-
-  auto tile = [&]<bool MASK>(int q0) {
-    // S and dP as [query][key] blocks: lane c owns key w0 + 32*kw + c.
-    f32x16 sacc[QB][KBW], pacc[QB][KBW];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kw = 0; kw < KBW; ++kw) {
-        sacc[qb][kw] = f32x16{};
-        pacc[qb][kw] = f32x16{};
-      }
+  // K and V fragments of this wave's keys stay in registers, except for fp32
+  // inputs at D = 128 (256 registers on their own), which re-read them from
+  // the cache at every query tile.
+  constexpr bool kKVRegs = !(sizeof(T) == 4 && D == 128);
+  constexpr int KBR = kKVRegs ? KB : 1;
+  frag kf[KBR], vf[KBR];
+  if constexpr (kKVRegs) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const frag aq = lds_frag<T>(sQ + (qb * 32 + c) * LD + 16 * kb + 8 * hh);
-        const frag ad = lds_frag<T>(sdO + (qb * 32 + c) * LD + 16 * kb + 8 * hh);
-#pragma unroll
-        for (int kw = 0; kw < KBW; ++kw) {
-          E::mma(sacc[qb][kw], aq, kf[kw][kb]);
-          E::mma(pacc[qb][kw], ad, vf[kw][kb]);
-        }
-      }
+      kf[kb] = global_frag<T, D>(gk, key, 16 * kb + 8 * hh);
+      vf[kb] = global_frag<T, D>(gv, key, 16 * kb + 8 * hh);
     }
+  }
+  auto kfrag = [&](int kb) { return kKVRegs ? kf[kKVRegs ? kb : 0] : global_frag<T, D>(gk, key, 16 * kb + 8 * hh); };
+  auto vfrag = [&](int kb) { return kKVRegs ? vf[kKVRegs ? kb : 0] : global_frag<T, D>(gv, key, 16 * kb + 8 * hh); };
+  f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dkacc[db] = f32x16{};
+    dvacc[db] = f32x16{};
+  }
 
-    // P = exp2(S * c2 - LSE2), dS = P (dP - Delta); packed as B operands whose
-    // slots run over queries.
-    frag pf[KBW][PB], sf[KBW][PB];
+  // One query tile: per 32-query block, S = Q K^T and dP = dO V^T as
+  // [query][key] blocks (lane c owns key w0 + c), P = exp2(S c2 - LSE log2 e),
+  // dS = P (dP - Delta), then dV^T += dO^T P and dK^T += Q^T dS.
+  auto tile = [&]<int P, bool MASK>(int q0) {
+    const lds_t<T> *sq = qslot.template operator()<P>();
+    const lds_t<T> *so = oslot.template operator()<P>();
+    const lds_t<float> *sl = lslot.template operator()<P>();
+    const lds_t<float> *sd = dslot.template operator()<P>();
+    const TrSwz<T, D> trq(sq, lane);
+    const TrSwz<T, D> trdo(so, lane);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      f32x4 lq4[4], dq4[4];
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int ch = (16 * kb + 8 * hh) / QTile::kVec;
+        E::mma(sacc, swz_frag<T, D, QTile::kSW>(sq, qb * 32 + c, ch), kfrag(kb));
+        E::mma(pacc, swz_frag<T, D, QTile::kSW>(so, qb * 32 + c, ch), vfrag(kb));
+      }
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        lq4[g] = *reinterpret_cast<const f32x4 *>(sL + qb * 32 + 8 * g + 4 * hh);
-        dq4[g] = *reinterpret_cast<const f32x4 *>(sD + qb * 32 + 8 * g + 4 * hh);
-      }
+        const f32x4 l4 = *(const lds_t<f32x4> *)(sl + qb * 32 + 8 * g + 4 * hh);
+        const f32x4 d4 = *(const lds_t<f32x4> *)(sd + qb * 32 + 8 * g + 4 * hh);
 #pragma unroll
-      for (int kw = 0; kw < KBW; ++kw) {
-        const int key = w0 + 32 * kw + c;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(__builtin_fmaf(sacc[qb][kw][r], c2, -lq4[r / 4][r % 4]));
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g + i;
+          float p = fast_exp2(__builtin_fmaf(sacc[r], c2, -l4[i] * kLog2e));
           if constexpr (MASK) {
-            const int qi = q0 + qb * 32 + 8 * (r / 4) + 4 * hh + (r % 4);
+            const int qi = q0 + qb * 32 + 8 * g + 4 * hh + i;
             p = qi < key ? 0.f : p;
           }
-          sacc[qb][kw][r] = p;
-          pacc[qb][kw][r] = p * (pacc[qb][kw][r] - dq4[r / 4][r % 4]);
+          sacc[r] = p;
+          pacc[r] = p * (pacc[r] - d4[i]);
         }
-        pf[kw][2 * qb] = E::pack(sacc[qb][kw], 0);
-        pf[kw][2 * qb + 1] = E::pack(sacc[qb][kw], 1);
-        sf[kw][2 * qb] = E::pack(pacc[qb][kw], 0);
-        sf[kw][2 * qb + 1] = E::pack(pacc[qb][kw], 1);
       }
-    }
-
-    // dV^T += dO^T P,  dK^T += Q^T dS : rows are head dims, lanes are keys.
+      const frag p0 = E::pack(sacc, 0), p1 = E::pack(sacc, 1);
+      const frag s0 = E::pack(pacc, 0), s1 = E::pack(pacc, 1);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int j = 0; j < PB; ++j) {
-        const frag ad = trdo(16 * j, 32 * db);
-        const frag aq = trq(16 * j, 32 * db);
-#pragma unroll
-        for (int kw = 0; kw < KBW; ++kw) {
-          E::mma(dvacc[kw][db], ad, pf[kw][j]);
-          E::mma(dkacc[kw][db], aq, sf[kw][j]);
-        }
+      for (int db = 0; db < DB; ++db) {
+        E::mma(dvacc[db], trdo(32 * qb, db), p0);
+        E::mma(dvacc[db], trdo(32 * qb + 16, db), p1);
+        E::mma(dkacc[db], trq(32 * qb, db), s0);
+        E::mma(dkacc[db], trq(32 * qb + 16, db), s1);
       }
     }
   };
 
-  for (int it = 0; it < ntile; ++it) {
+  // Query tile `it` in ring slot P: wait for its copies (this wave's, then
+  // everyone's), request the next tile into the other slot, compute.
+  auto step = [&]<int P>(int it) {
+    wait_vmcnt<0>();
+    wg_barrier();
+    if (it + 1 < ntile) issue.template operator()<1 - P>(it + 1);
     const int q0 = q_lo + it * BMQ;
-    __syncthreads();
-    lq.template store<LD>(sQ, tid);
-    ldo.template store<LD>(sdO, tid);
-    if (tid < BMQ) {
-      sL[tid] = lval;
-      sD[tid] = dval;
-    }
-    __syncthreads();
-    if (it + 1 < ntile) {
-      lq.load(gq, q0 + BMQ, tid);
-      ldo.load(gdo, q0 + BMQ, tid);
-      load_stats(q0 + BMQ);
-    }
-    if (!wave_active || q0 + BMQ - 1 < w0) continue;  // every query precedes every key here
+    if (!wave_active || q0 + BMQ - 1 < w0) return;  // every query precedes every key here
     if (q0 < wave_last)
-      tile.template operator()<true>(q0);
+      tile.template operator()<P, true>(q0);
     else
-      tile.template operator()<false>(q0);
+      tile.template operator()<P, false>(q0);
+  };
+  for (int it = 0; it < ntile; it += 2) {
+    step.template operator()<0>(it);
+    if (it + 1 < ntile) step.template operator()<1>(it + 1);
   }
 
   if (!wave_active) return;
   const GBuf gdk(dk + base, (uint32_t)(t.r_end * D * sizeof(float)));
   const GBuf gdv(dv + base, (uint32_t)(t.r_end * D * sizeof(float)));
 #pragma unroll
-  for (int kw = 0; kw < KBW; ++kw) {
-    const int key = w0 + 32 * kw + c;
+  for (int db = 0; db < DB; ++db) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int g = 0; g < 4; ++g) {
+      f32x4 a4, b4;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 a4, b4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a4[i] = dkacc[kw][db][4 * g + i] * scale;
-          b4[i] = dvacc[kw][db][4 * g + i];
-        }
-        const uint32_t off = (uint32_t)(key * D + db * 32 + 8 * g + 4 * hh) * sizeof(float);
-        gdk.store16(a4, off);
-        gdv.store16(b4, off);
+      for (int i = 0; i < 4; ++i) {
+        a4[i] = dkacc[db][4 * g + i] * scale;
+        b4[i] = dvacc[db][4 * g + i];
       }
+      const uint32_t off = (uint32_t)(key * D + db * 32 + 8 * g + 4 * hh) * sizeof(float);
+      gdk.store16(a4, off);
+      gdv.store16(b4, off);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// dQ.  A workgroup owns BM = 4 * 32 * QB queries of one head and loops over
-// key tiles of BN rows up to its causal diagonal.
-template <typename T, int D, int QB, int BN, bool DOC>
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
+// dQ.  A workgroup owns BM = 128 queries of one head (32 per wave) and loops
+// over key tiles of BN rows up to its causal diagonal.  K and V tiles arrive
+// by direct global->LDS copies into two ring slots one iteration ahead; K is
+// read both as row fragments and, through the transposing load, as K^T.
+template <typename T, int D, int BN, int MINB, bool DOC>
+__global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, float *__restrict__ dq, int S, float c2,
     float scale, const int32_t *__restrict__ cu, int ntiles) {
   constexpr int NW = 4;
   constexpr int NT = NW * kWaveSize;
-  constexpr int BM = NW * 32 * QB;
+  constexpr int BM = NW * 32;
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
   constexpr int NB = BN / 32;
-  constexpr int PB = BN / 16;
   using E = Elem<T>;
   using frag = typename E::frag;
-  constexpr int LD = RowStride<T, D>::kPadded;
-  using Loader = TileLoader<T, BN, D, NT>;
+  using KTile = DmaTile<T, BN, D, NT, true>;
 
-  __shared__ __attribute__((aligned(16))) T sK[BN * LD];
-  __shared__ __attribute__((aligned(16))) T sV[BN * LD];
+  __shared__ __attribute__((aligned(1024))) T sK0[BN * D];
+  __shared__ __attribute__((aligned(1024))) T sK1[BN * D];
+  __shared__ __attribute__((aligned(1024))) T sV0[BN * D];
+  __shared__ __attribute__((aligned(1024))) T sV1[BN * D];
 
   const RowTile t = DOC ? doc_tile(cu, blockIdx.x, gridDim.x, blockIdx.y, blockIdx.z, BM, true)
                         : causal_tile(blockIdx.x, gridDim.x, ntiles, BM, S, true);
@@ -312,128 +287,94 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const GBuf glse(lse + rbase, (uint32_t)(t.r_end * sizeof(float)));
   const GBuf gdel(delta + rbase, (uint32_t)(t.r_end * sizeof(float)));
 
-  const int w0 = t.r_start + wave * 32 * QB;
+  const int w0 = t.r_start + wave * 32;  // first query of this wave
   const bool wave_active = w0 < t.r_end;
-  const int wave_last = min(w0 + 32 * QB, t.r_end) - 1;
-
-  frag qf[QB][KB], df[QB][KB];
-  float l2[QB], dl[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = w0 + 32 * qb + c;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      qf[qb][kb] = global_frag<T, D>(gq, row, 16 * kb + 8 * hh);
-      df[qb][kb] = global_frag<T, D>(gdo, row, 16 * kb + 8 * hh);
-    }
-    const float lv = glse.load4((uint32_t)row * 4);
-    dl[qb] = gdel.load4((uint32_t)row * 4);
-    l2[qb] = row < t.r_end ? lv * kLog2e : INFINITY;
-  }
-
-  f32x16 dqacc[QB][DB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) dqacc[qb][db] = f32x16{};
-
+  const int wave_last = min(w0 + 32, t.r_end) - 1;
+  const int qi = w0 + c;
   const int kv_lo = t.seg_start;
   const int kv_hi = min(t.r_end, t.seg_end);
   const int ntile = (kv_hi - kv_lo + BN - 1) / BN;
+  const int jw = wave_active ? (wave_last - kv_lo) / BN + 1 : 0;  // tiles this wave needs
 
-  Loader lk, lv;
-  lk.load(gk, kv_lo, tid);
-  lv.load(gv, kv_lo, tid);
+  auto kslot = [&]<int P>() { return lds_cast(P == 0 ? sK0 : sK1); };
+  auto vslot = [&]<int P>() { return lds_cast(P == 0 ? sV0 : sV1); };
+  auto issue = [&]<int P>(int j) {
+    KTile::issue(gk, kslot.template operator()<P>(), kv_lo + j * BN, wave, lane);
+    KTile::issue(gv, vslot.template operator()<P>(), kv_lo + j * BN, wave, lane);
+  };
+  issue.template operator()<0>(0);
 
-  const TrRead<T, LD> trk(sK, lane);
-
-  auto tile = [&]<bool MASK>(int k0) {
-    // S^T = K Q^T and dP^T = V dO^T : rows are keys, lanes are queries.
-    f32x16 sacc[QB][NB], pacc[QB][NB];
+  frag qf[KB], df[KB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+  for (int kb = 0; kb < KB; ++kb) {
+    qf[kb] = global_frag<T, D>(gq, qi, 16 * kb + 8 * hh);
+    df[kb] = global_frag<T, D>(gdo, qi, 16 * kb + 8 * hh);
+  }
+  const float l2 = glse.load4((uint32_t)qi * 4) * kLog2e;
+  const float dl = gdel.load4((uint32_t)qi * 4);
+  f32x16 dqacc[DB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        sacc[qb][nb] = f32x16{};
-        pacc[qb][nb] = f32x16{};
+  for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
+
+  // One key tile: per 32-key block, S^T = K Q^T and dP^T = V dO^T (lane c owns
+  // query w0 + c), P, dS = P (dP - Delta), then dQ^T += K^T dS^T.
+  auto tile = [&]<int P, bool MASK>(int k0) {
+    const lds_t<T> *sk = kslot.template operator()<P>();
+    const lds_t<T> *sv = vslot.template operator()<P>();
+    const TrSwz<T, D> trk(sk, lane);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int ch = (16 * kb + 8 * hh) / KTile::kVec;
+        E::mma(sacc, swz_frag<T, D, KTile::kSW>(sk, nb * 32 + c, ch), qf[kb]);
+        E::mma(pacc, swz_frag<T, D, KTile::kSW>(sv, nb * 32 + c, ch), df[kb]);
       }
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const frag ak = lds_frag<T>(sK + (nb * 32 + c) * LD + 16 * kb + 8 * hh);
-        const frag av = lds_frag<T>(sV + (nb * 32 + c) * LD + 16 * kb + 8 * hh);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          E::mma(sacc[qb][nb], ak, qf[qb][kb]);
-          E::mma(pacc[qb][nb], av, df[qb][kb]);
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(__builtin_fmaf(sacc[r], c2, -l2));
+        if constexpr (MASK) {
+          const int kj = k0 + 32 * nb + 8 * (r / 4) + 4 * hh + (r % 4);
+          p = (kj > qi || kj >= t.seg_end) ? 0.f : p;
         }
+        pacc[r] = p * (pacc[r] - dl);
       }
-    }
-
-    frag sf[QB][PB];
+      const frag s0 = E::pack(pacc, 0), s1 = E::pack(pacc, 1);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int qi = w0 + 32 * qb + c;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(__builtin_fmaf(sacc[qb][nb][r], c2, -l2[qb]));
-          if constexpr (MASK) {
-            const int key = k0 + 32 * nb + 8 * (r / 4) + 4 * hh + (r % 4);
-            p = (key > qi || key >= t.seg_end) ? 0.f : p;
-          }
-          pacc[qb][nb][r] = p * (pacc[qb][nb][r] - dl[qb]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < PB; ++j) sf[qb][j] = E::pack(pacc[qb][j / 2], j % 2);
-    }
-
-    // dQ^T += K^T dS^T : rows are head dims, lanes are queries.
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int j = 0; j < PB; ++j) {
-        const frag a = trk(16 * j, 32 * db);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) E::mma(dqacc[qb][db], a, sf[qb][j]);
+      for (int db = 0; db < DB; ++db) {
+        E::mma(dqacc[db], trk(32 * nb, db), s0);
+        E::mma(dqacc[db], trk(32 * nb + 16, db), s1);
       }
     }
   };
 
-  for (int it = 0; it < ntile; ++it) {
-    const int k0 = kv_lo + it * BN;
-    __syncthreads();
-    lk.template store<LD>(sK, tid);
-    lv.template store<LD>(sV, tid);
-    __syncthreads();
-    if (it + 1 < ntile) {
-      lk.load(gk, k0 + BN, tid);
-      lv.load(gv, k0 + BN, tid);
-    }
-    if (!wave_active || k0 > wave_last) continue;
+  auto step = [&]<int P>(int j) {
+    wait_vmcnt<0>();
+    wg_barrier();
+    if (j + 1 < ntile) issue.template operator()<1 - P>(j + 1);
+    if (j >= jw) return;
+    const int k0 = kv_lo + j * BN;
     if ((k0 + BN - 1 > w0) || (k0 + BN > t.seg_end))
-      tile.template operator()<true>(k0);
+      tile.template operator()<P, true>(k0);
     else
-      tile.template operator()<false>(k0);
+      tile.template operator()<P, false>(k0);
+  };
+  for (int j = 0; j < ntile; j += 2) {
+    step.template operator()<0>(j);
+    if (j + 1 < ntile) step.template operator()<1>(j + 1);
   }
 
   if (!wave_active) return;
   const GBuf gdq(dq + base, (uint32_t)(t.r_end * D * sizeof(float)));
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = w0 + 32 * qb + c;
+  for (int db = 0; db < DB; ++db) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int g = 0; g < 4; ++g) {
+      f32x4 a4;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 a4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a4[i] = dqacc[qb][db][4 * g + i] * scale;
-        gdq.store16(a4, (uint32_t)(qi * D + db * 32 + 8 * g + 4 * hh) * sizeof(float));
-      }
+      for (int i = 0; i < 4; ++i) a4[i] = dqacc[db][4 * g + i] * scale;
+      gdq.store16(a4, (uint32_t)(qi * D + db * 32 + 8 * g + 4 * hh) * sizeof(float));
     }
   }
 }
@@ -441,23 +382,22 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 // Launchers.
 
-#ifndef ATTN_DKDV_KBW
-#define ATTN_DKDV_KBW 1
-#endif
-#ifndef ATTN_DKDV_BMQ
-#define ATTN_DKDV_BMQ 64
-#endif
-#ifndef ATTN_DQ_QB
-#define ATTN_DQ_QB 1
-#endif
-#ifndef ATTN_DQ_BN
-#define ATTN_DQ_BN 64
-#endif
+// Tile shapes: query tile of the dK/dV kernel (BMQ), key tile of the dQ
+// kernel (BN), and the minimum workgroups per CU each register allocation
+// must allow.  Two 64-row slots of Q and dO (or K and V) at D = 128, or in
+// fp32, would leave room for one workgroup per CU: those take 32 rows.
 template <typename T, int D> struct BwdCfg {
-  static constexpr int KBW = (D == 128 || sizeof(T) == 4) ? 1 : ATTN_DKDV_KBW;  // key blocks per wave (dK/dV)
-  static constexpr int BMQ = (D == 128 || sizeof(T) == 4) ? 32 : ATTN_DKDV_BMQ;  // query tile (dK/dV)
-  static constexpr int QB = ATTN_DQ_QB;                                         // query blocks per wave (dQ)
-  static constexpr int BN = ATTN_DQ_BN;                                         // key tile (dQ)
+#ifdef ATTN_BWD_BMQ
+  static constexpr int BMQ = (D == 128 || sizeof(T) == 4) ? 32 : ATTN_BWD_BMQ;
+  static constexpr int BN = (D == 128 && sizeof(T) == 4) ? 32 : ATTN_BWD_BN;
+  static constexpr int MINB_DKDV = ATTN_BWD_MINB_DKDV;
+  static constexpr int MINB_DQ = ATTN_BWD_MINB_DQ;
+#else
+  static constexpr int BMQ = (D == 128 || sizeof(T) == 4) ? 32 : 64;
+  static constexpr int BN = (D == 128 && sizeof(T) == 4) ? 32 : 64;
+  static constexpr int MINB_DKDV = 1;
+  static constexpr int MINB_DQ = 1;
+#endif
 };
 
 template <typename T, int D>
@@ -473,9 +413,9 @@ static hipError_t launch_pre_t(const Args &a) {
 
 template <typename T, int D, bool DOC>
 static hipError_t launch_dkdv_t(const Args &a) {
-  constexpr int KBW = BwdCfg<T, D>::KBW;
   constexpr int BMQ = BwdCfg<T, D>::BMQ;
-  constexpr int BN = 4 * 32 * KBW;
+  constexpr int MINB = BwdCfg<T, D>::MINB_DKDV;
+  constexpr int BN = 4 * 32;
   const float c2 = a.scale * kLog2e;
   dim3 grid;
   int ntiles;
@@ -486,7 +426,7 @@ static hipError_t launch_dkdv_t(const Args &a) {
     ntiles = (a.S + BN - 1) / BN;
     grid = dim3(ntiles * a.B * a.H);
   }
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, KBW, BMQ, DOC>), grid, dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, BMQ, MINB, DOC>), grid, dim3(256), 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
                      static_cast<const T *>(a.dO), a.lse_in, a.delta_in, a.dk, a.dv, a.S, c2, a.scale,
                      a.cu_seqlens, ntiles);
@@ -495,9 +435,9 @@ static hipError_t launch_dkdv_t(const Args &a) {
 
 template <typename T, int D, bool DOC>
 static hipError_t launch_dq_t(const Args &a) {
-  constexpr int QB = BwdCfg<T, D>::QB;
   constexpr int BN = BwdCfg<T, D>::BN;
-  constexpr int BM = 4 * 32 * QB;
+  constexpr int MINB = BwdCfg<T, D>::MINB_DQ;
+  constexpr int BM = 4 * 32;
   const float c2 = a.scale * kLog2e;
   dim3 grid;
   int ntiles;
@@ -508,7 +448,7 @@ static hipError_t launch_dq_t(const Args &a) {
     ntiles = (a.S + BM - 1) / BM;
     grid = dim3(ntiles * a.B * a.H);
   }
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, QB, BN, DOC>), grid, dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, MINB, DOC>), grid, dim3(256), 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
                      static_cast<const T *>(a.dO), a.lse_in, a.delta_in, a.dq, a.S, c2, a.scale, a.cu_seqlens,
                      ntiles);

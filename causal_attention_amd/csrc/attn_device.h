@@ -300,6 +300,79 @@ template <typename T, int R, int D, int NT, bool SWIZZLE> struct DmaTile {
   }
 };
 
+// One direct-to-LDS copy of 64 consecutive floats (elements e0 .. e0+63 of
+// the buffer; past its end they arrive as zeros), issued by one wave.
+__device__ __forceinline__ void dma_vec64(const GBuf &g, lds_t<float> *dst, int e0, int lane) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(g.r, (lds_void *)dst, 4, (uint32_t)(e0 + lane) * 4u, 0, 0, 0);
+}
+
+// Fragment of the TRANSPOSE of a swizzled tile written by DmaTile<T, R, D, NT,
+// true> (row-major, D columns, 16-byte chunk x of row r stored at chunk
+// x ^ (r & SW)), in the same slot order as TrRead: operator()(row0, db) gives
+// rows row0 .. row0+15 (row0 a multiple of 16) of columns 32*db .. 32*db+31.
+template <typename T, int D> struct TrSwz;
+
+template <int D> struct TrSwz<bf16, D> {
+  using frag = bf16x8;
+  static constexpr int kCPR = D / 8;
+  static constexpr int kSW = (kCPR < 8 ? kCPR : 8) - 1;
+  // Lane bases for even and odd 32-column blocks (chunk (4*db + x) ^ s equals
+  // 4*(db ^ (s >> 2)) + (x ^ (s & 3)) for x < 4), and the same 8 rows further
+  // down (kept opaque to constant folding, which would lose the LDS object
+  // the read belongs to).
+  const lds_t<bf16> *ev, *od, *ev8, *od8;
+  __device__ __forceinline__ TrSwz(const lds_t<bf16> *tile, int lane) {
+    const int g = lane / 16, i = lane % 16;
+    const int r = 4 * (g / 2) + i / 4;        // row within an 8-row group
+    const int x = 2 * (g % 2) + (i % 4) / 2;  // 16-byte chunk within the 32-column block
+    const int s = r & kSW;
+    const int lo = r * D + 8 * (x ^ (s & 3)) + 4 * (i % 2);
+    const int sb = 32 * ((s >> 2) & 1);
+    int e8 = lo + sb + 8 * D, o8 = lo - sb + 8 * D;
+    asm volatile("" : "+v"(e8));
+    asm volatile("" : "+v"(o8));
+    ev = tile + lo + sb;
+    od = tile + lo - sb;
+    ev8 = tile + e8;
+    od8 = tile + o8;
+  }
+  __device__ __forceinline__ frag operator()(int row0, int db) const {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const lds_t<bf16> *p = (db % 2 == 0 ? ev : od) + row0 * D + 32 * db;
+    const lds_t<bf16> *p8 = (db % 2 == 0 ? ev8 : od8) + row0 * D + 32 * db;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p8);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = a[j];
+      v[4 + j] = b[j];
+    }
+    return __builtin_bit_cast(frag, v);
+  }
+};
+
+template <int D> struct TrSwz<float, D> {
+  using frag = f32x8;
+  // 4-float chunks, SW = 7; rows 4h + u (u < 4) of an 8-row group, column c:
+  // chunk (8*db + c/4) ^ (4h + u) = 8*db + ((c/4) ^ (4h + u)).
+  int off[4];
+  const lds_t<float> *tile;
+  __device__ __forceinline__ TrSwz(const lds_t<float> *t, int lane) : tile(t) {
+    const int h = lane / 32, c = lane % 32;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) off[u] = (4 * h + u) * D + 4 * ((c / 4) ^ (4 * h + u)) + c % 4;
+  }
+  __device__ __forceinline__ frag operator()(int row0, int db) const {
+    frag f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) f[s] = tile[row0 * D + 32 * db + 8 * D * (s / 4) + off[s % 4]];
+    return f;
+  }
+};
+
 // Row fragment of a swizzled tile: 8 slots of row `row` starting at column
 // 8*(2*kb + hh) (natural slot order), for lanes whose row index is `row`.
 template <typename T, int D, int SW>
