@@ -159,49 +159,51 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     dvacc[db] = f32x16{};
   }
 
-  // One query tile: per 32-query block, S = Q K^T and dP = dO V^T as
-  // [query][key] blocks (lane c owns key w0 + c), P = exp2(S c2 - LSE log2 e),
-  // dS = P (dP - Delta), then dV^T += dO^T P and dK^T += Q^T dS.
+  const TrSwz<T, D> tr0(lane);    // transposed reads of the Q and dO tiles
+  const RowFrag<T, D> rf0(lane);  // row fragments of the same tiles
+
+  // One query tile: per 32-query block, S' = Q K^T - LSE/scale and
+  // dP' = dO V^T - Delta as [query][key] blocks (lane c owns key w0 + c; the
+  // per-query shifts enter as a rank-1 product, so no lane needs the shift of
+  // every row it holds), P = exp2(S' c2), dS = P dP', then dV^T += dO^T P and
+  // dK^T += Q^T dS.
+  const frag ones = E::rows_b(hh);
+  const float rscale = 1.0f / scale;
   auto tile = [&]<int P, bool MASK>(int q0) {
     const lds_t<T> *sq = qslot.template operator()<P>();
     const lds_t<T> *so = oslot.template operator()<P>();
     const lds_t<float> *sl = lslot.template operator()<P>();
     const lds_t<float> *sd = dslot.template operator()<P>();
-    const TrSwz<T, D> trq(sq, lane);
-    const TrSwz<T, D> trdo(so, lane);
+    const TrSwz<T, D> tr = tr0.pinned();
+    const RowFrag<T, D> rf = rf0.pinned();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       f32x16 sacc = f32x16{}, pacc = f32x16{};
+      E::mma(sacc, E::rows_a(-sl[qb * 32 + c] * rscale, hh), ones);
+      E::mma(pacc, E::rows_a(-sd[qb * 32 + c], hh), ones);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const int ch = (16 * kb + 8 * hh) / QTile::kVec;
-        E::mma(sacc, swz_frag<T, D, QTile::kSW>(sq, qb * 32 + c, ch), kfrag(kb));
-        E::mma(pacc, swz_frag<T, D, QTile::kSW>(so, qb * 32 + c, ch), vfrag(kb));
+        E::mma(sacc, rf(sq, qb, kb), kfrag(kb));
+        E::mma(pacc, rf(so, qb, kb), vfrag(kb));
       }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *(const lds_t<f32x4> *)(sl + qb * 32 + 8 * g + 4 * hh);
-        const f32x4 d4 = *(const lds_t<f32x4> *)(sd + qb * 32 + 8 * g + 4 * hh);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g + i;
-          float p = fast_exp2(__builtin_fmaf(sacc[r], c2, -l4[i] * kLog2e));
-          if constexpr (MASK) {
-            const int qi = q0 + qb * 32 + 8 * g + 4 * hh + i;
-            p = qi < key ? 0.f : p;
-          }
-          sacc[r] = p;
-          pacc[r] = p * (pacc[r] - d4[i]);
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(sacc[r] * c2);
+        if constexpr (MASK) {
+          const int qi = q0 + qb * 32 + 8 * (r / 4) + 4 * hh + (r % 4);
+          p = qi < key ? 0.f : p;
         }
+        sacc[r] = p;
+        pacc[r] = p * pacc[r];
       }
       const frag p0 = E::pack(sacc, 0), p1 = E::pack(sacc, 1);
       const frag s0 = E::pack(pacc, 0), s1 = E::pack(pacc, 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        E::mma(dvacc[db], trdo(32 * qb, db), p0);
-        E::mma(dvacc[db], trdo(32 * qb + 16, db), p1);
-        E::mma(dkacc[db], trq(32 * qb, db), s0);
-        E::mma(dkacc[db], trq(32 * qb + 16, db), s1);
+        E::mma(dvacc[db], tr(so, 32 * qb, db), p0);
+        E::mma(dvacc[db], tr(so, 32 * qb + 16, db), p1);
+        E::mma(dkacc[db], tr(sq, 32 * qb, db), s0);
+        E::mma(dkacc[db], tr(sq, 32 * qb + 16, db), s1);
       }
     }
   };
@@ -316,20 +318,24 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
 
+  const TrSwz<T, D> tr0(lane);    // transposed reads of the K tile
+  const RowFrag<T, D> rf0(lane);  // row fragments of the K and V tiles
+
   // One key tile: per 32-key block, S^T = K Q^T and dP^T = V dO^T (lane c owns
   // query w0 + c), P, dS = P (dP - Delta), then dQ^T += K^T dS^T.
   auto tile = [&]<int P, bool MASK>(int k0) {
     const lds_t<T> *sk = kslot.template operator()<P>();
     const lds_t<T> *sv = vslot.template operator()<P>();
-    const TrSwz<T, D> trk(sk, lane);
+    const TrSwz<T, D> tr = tr0.pinned();
+    const RowFrag<T, D> rf = rf0.pinned();
+
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const int ch = (16 * kb + 8 * hh) / KTile::kVec;
-        E::mma(sacc, swz_frag<T, D, KTile::kSW>(sk, nb * 32 + c, ch), qf[kb]);
-        E::mma(pacc, swz_frag<T, D, KTile::kSW>(sv, nb * 32 + c, ch), df[kb]);
+        E::mma(sacc, rf(sk, nb, kb), qf[kb]);
+        E::mma(pacc, rf(sv, nb, kb), df[kb]);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -343,8 +349,8 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
       const frag s0 = E::pack(pacc, 0), s1 = E::pack(pacc, 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        E::mma(dqacc[db], trk(32 * nb, db), s0);
-        E::mma(dqacc[db], trk(32 * nb + 16, db), s1);
+        E::mma(dqacc[db], tr(sk, 32 * nb, db), s0);
+        E::mma(dqacc[db], tr(sk, 32 * nb + 16, db), s1);
       }
     }
   };

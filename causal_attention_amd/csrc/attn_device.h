@@ -71,6 +71,30 @@ template <> struct Elem<bf16> {
     for (int s = 0; s < 8; ++s) sum += acc[8 * j + s];
     return pack(acc, j);
   }
+  // Operands of a rank-1 product mma(acc, rows_a(x, hh), rows_b(hh)) that adds
+  // x_c to every element of row c of a 32x32 result, x_c being the value lane
+  // c passes (lanes 32-63 pass anything).  x is split into three bf16 terms
+  // whose fp32 sum reproduces it to fp32 precision; the B side is ones.
+  __device__ __forceinline__ static frag rows_a(float x, int hh) {
+    const float y = hh == 0 ? x : 0.f;
+    const bf16 t0 = (bf16)y;
+    const float r0 = y - (float)t0;
+    const bf16 t1 = (bf16)r0;
+    const bf16 t2 = (bf16)(r0 - (float)t1);
+    frag f = {};
+    f[0] = t0;
+    f[1] = t1;
+    f[2] = t2;
+    return f;
+  }
+  __device__ __forceinline__ static frag rows_b(int hh) {
+    const bf16 one = (bf16)(hh == 0 ? 1.f : 0.f);
+    frag f = {};
+    f[0] = one;
+    f[1] = one;
+    f[2] = one;
+    return f;
+  }
 };
 
 template <> struct Elem<float> {
@@ -93,6 +117,16 @@ template <> struct Elem<float> {
       f[s] = acc[8 * j + s];
       sum += f[s];
     }
+    return f;
+  }
+  __device__ __forceinline__ static frag rows_a(float x, int hh) {
+    frag f = {};
+    f[0] = hh == 0 ? x : 0.f;
+    return f;
+  }
+  __device__ __forceinline__ static frag rows_b(int hh) {
+    frag f = {};
+    f[0] = hh == 0 ? 1.f : 0.f;
     return f;
   }
 };
@@ -277,10 +311,28 @@ template <typename T, int R, int D, int NT> struct TileLoader {
 // Tiles read as row fragments are XOR-swizzled: 16-byte chunk c of row r is
 // stored at chunk c ^ (r & SW), which puts the 16-byte reads of consecutive
 // rows on distinct LDS banks without padding.
+// XOR mask applied to the 16-byte chunk index of row `row` of a swizzled
+// tile (chunk x of the row is stored at x ^ mask).  Chosen by measurement so
+// that both ways the tiles are read run near the LDS peak: 16-byte row
+// fragments (16 consecutive rows at a time, one chunk each) and the
+// transposing 8-byte reads (rows 0-3 x chunks 0-3 of a 32-column block, then
+// rows 4-7).  For 128-byte rows a mask of row & 7 puts rows r and r + 8 on
+// the same banks and halves the row-fragment rate; these masks have period 16.
+template <typename T, int D> __device__ __forceinline__ uint32_t swz_mask(uint32_t row) {
+  if constexpr (sizeof(T) == 4) {
+    return row & 7;
+  } else if constexpr (D == 32) {
+    return row & 3;
+  } else if constexpr (D == 64) {
+    return (4 * ((row >> 1) & 1) + ((row >> 2) & 1)) ^ (2 * ((row >> 3) & 1));
+  } else {
+    return 4 * (row & 3) + ((row >> 2) & 3);
+  }
+}
+
 template <typename T, int R, int D, int NT, bool SWIZZLE> struct DmaTile {
   static constexpr int kVec = 16 / sizeof(T);                 // elements per chunk
   static constexpr int kCPR = D / kVec;                        // chunks per row
-  static constexpr int kSW = SWIZZLE ? (kCPR < 8 ? kCPR : 8) - 1 : 0;
   static constexpr int kBlocks = R * kCPR / kWaveSize;         // 1 KB blocks per tile
   static constexpr int kPerWave = kBlocks / (NT / kWaveSize);  // copy instructions per wave
   static_assert(R * kCPR % NT == 0, "tile must split evenly over the waves");
@@ -292,7 +344,8 @@ template <typename T, int R, int D, int NT, bool SWIZZLE> struct DmaTile {
       const int blk = wave * kPerWave + i;
       const int p = blk * kWaveSize + lane;
       const uint32_t row = (uint32_t)p / kCPR;
-      const uint32_t col = ((uint32_t)(p % kCPR) * kVec) ^ ((row & kSW) * kVec);  // swizzled chunk, in elements
+      const uint32_t chunk = (uint32_t)(p % kCPR) ^ (SWIZZLE ? swz_mask<T, D>(row) : 0u);
+      const uint32_t col = chunk * kVec;  // swizzled chunk, in elements
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           g.r, (lds_void *)(tile + blk * (1024 / sizeof(T))), 16,
           (((uint32_t)r0 + row) * D + col) * (uint32_t)sizeof(T), 0, 0, 0);
@@ -308,41 +361,46 @@ __device__ __forceinline__ void dma_vec64(const GBuf &g, lds_t<float> *dst, int 
 }
 
 // Fragment of the TRANSPOSE of a swizzled tile written by DmaTile<T, R, D, NT,
-// true> (row-major, D columns, 16-byte chunk x of row r stored at chunk
-// x ^ (r & SW)), in the same slot order as TrRead: operator()(row0, db) gives
-// rows row0 .. row0+15 (row0 a multiple of 16) of columns 32*db .. 32*db+31.
+// true> (row-major, D columns, chunks permuted by swz_mask), in the same slot
+// order as TrRead: operator()(tile, row0, db) gives rows row0 .. row0+15
+// (row0 a multiple of 16) of columns 32*db .. 32*db+31.  The object holds
+// only this lane's element offsets, so one serves every tile of that shape.
 template <typename T, int D> struct TrSwz;
 
 template <int D> struct TrSwz<bf16, D> {
   using frag = bf16x8;
-  static constexpr int kCPR = D / 8;
-  static constexpr int kSW = (kCPR < 8 ? kCPR : 8) - 1;
-  // Lane bases for even and odd 32-column blocks (chunk (4*db + x) ^ s equals
-  // 4*(db ^ (s >> 2)) + (x ^ (s & 3)) for x < 4), and the same 8 rows further
-  // down (kept opaque to constant folding, which would lose the LDS object
-  // the read belongs to).
-  const lds_t<bf16> *ev, *od, *ev8, *od8;
-  __device__ __forceinline__ TrSwz(const lds_t<bf16> *tile, int lane) {
+  static constexpr int DB = D / 32;
+  // [read][db]: the first read covers rows 0-7 of the 16, the second rows 8-15.
+  int off[2][DB];
+  __device__ __forceinline__ explicit TrSwz(int lane) {
     const int g = lane / 16, i = lane % 16;
-    const int r = 4 * (g / 2) + i / 4;        // row within an 8-row group
-    const int x = 2 * (g % 2) + (i % 4) / 2;  // 16-byte chunk within the 32-column block
-    const int s = r & kSW;
-    const int lo = r * D + 8 * (x ^ (s & 3)) + 4 * (i % 2);
-    const int sb = 32 * ((s >> 2) & 1);
-    int e8 = lo + sb + 8 * D, o8 = lo - sb + 8 * D;
-    asm volatile("" : "+v"(e8));
-    asm volatile("" : "+v"(o8));
-    ev = tile + lo + sb;
-    od = tile + lo - sb;
-    ev8 = tile + e8;
-    od8 = tile + o8;
+    const int rl = 4 * (g / 2) + i / 4;             // row within an 8-row group
+    const int x = 2 * (g % 2) + (i % 4) / 2;        // 16-byte chunk within the 32-column block
+    const int e = 4 * (i % 2);                      // element within the chunk
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int r = rl + 8 * k;
+        off[k][db] = r * D + 8 * (int)((uint32_t)(4 * db + x) ^ swz_mask<bf16, D>(r)) + e;
+      }
   }
-  __device__ __forceinline__ frag operator()(int row0, int db) const {
+  // A copy whose offsets the compiler cannot trace back to the loop-invariant
+  // originals: taken once per tile, it keeps the sum with each tile's LDS
+  // address inside the loop, where the constant part folds into the
+  // instruction's offset field instead of occupying a register per tile.
+  __device__ __forceinline__ TrSwz pinned() const {
+    TrSwz t = *this;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(t.off[k][db]));
+    return t;
+  }
+  __device__ __forceinline__ frag operator()(const lds_t<bf16> *tile, int row0, int db) const {
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const lds_t<bf16> *p = (db % 2 == 0 ? ev : od) + row0 * D + 32 * db;
-    const lds_t<bf16> *p8 = (db % 2 == 0 ? ev8 : od8) + row0 * D + 32 * db;
-    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
-    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p8);
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tile + row0 * D + off[0][db]));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tile + row0 * D + off[1][db]));
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     s16x8 v;
 #pragma unroll
@@ -356,16 +414,21 @@ template <int D> struct TrSwz<bf16, D> {
 
 template <int D> struct TrSwz<float, D> {
   using frag = f32x8;
-  // 4-float chunks, SW = 7; rows 4h + u (u < 4) of an 8-row group, column c:
-  // chunk (8*db + c/4) ^ (4h + u) = 8*db + ((c/4) ^ (4h + u)).
+  // 4-float chunks, mask row & 7; rows 4h + u (u < 4) of an 8-row group,
+  // column c: chunk (8*db + c/4) ^ (4h + u) = 8*db + ((c/4) ^ (4h + u)).
   int off[4];
-  const lds_t<float> *tile;
-  __device__ __forceinline__ TrSwz(const lds_t<float> *t, int lane) : tile(t) {
+  __device__ __forceinline__ explicit TrSwz(int lane) {
     const int h = lane / 32, c = lane % 32;
 #pragma unroll
     for (int u = 0; u < 4; ++u) off[u] = (4 * h + u) * D + 4 * ((c / 4) ^ (4 * h + u)) + c % 4;
   }
-  __device__ __forceinline__ frag operator()(int row0, int db) const {
+  __device__ __forceinline__ TrSwz pinned() const {
+    TrSwz t = *this;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) asm volatile("" : "+v"(t.off[u]));
+    return t;
+  }
+  __device__ __forceinline__ frag operator()(const lds_t<float> *tile, int row0, int db) const {
     frag f;
 #pragma unroll
     for (int s = 0; s < 8; ++s) f[s] = tile[row0 * D + 32 * db + 8 * D * (s / 4) + off[s % 4]];
@@ -373,29 +436,53 @@ template <int D> struct TrSwz<float, D> {
   }
 };
 
-// Row fragment of a swizzled tile: 8 slots of row `row` starting at column
-// 8*(2*kb + hh) (natural slot order), for lanes whose row index is `row`.
-template <typename T, int D, int SW>
-__device__ __forceinline__ typename Elem<T>::frag swz_frag(const lds_t<T> *tile, int row, int chunk0) {
+// Row fragments of a swizzled tile for lanes that own row 32*blk + c (c the
+// lane's column index): operator()(tile, blk, kb) gives the 8 slots of that
+// row at columns 16*kb + 8*hh .. +7 (natural slot order).  Holds this lane's
+// element offsets (the swizzle mask depends on the row modulo 16 only).
+template <typename T, int D> struct RowFrag {
   using frag = typename Elem<T>::frag;
-  constexpr int kVec = 16 / sizeof(T);
-  // (chunk ^ s) * kVec == (chunk * kVec) ^ (s * kVec): kVec is a power of two
-  const int sw = (row & SW) * kVec;
-  const int rbase = row * D;
-  if constexpr (sizeof(T) == 2) {
-    return *(const lds_t<frag> *)(tile + rbase + ((chunk0 * kVec) ^ sw));
-  } else {
-    const f32x4 a = *(const lds_t<f32x4> *)(tile + rbase + ((chunk0 * kVec) ^ sw));
-    const f32x4 b = *(const lds_t<f32x4> *)(tile + rbase + (((chunk0 + 1) * kVec) ^ sw));
-    frag f;
+  static constexpr int KB = D / 16;
+  static constexpr int kVec = 16 / sizeof(T);  // elements per 16-byte chunk
+  static constexpr int kReads = sizeof(T) == 2 ? 1 : 2;
+  int off[KB][kReads];
+  __device__ __forceinline__ explicit RowFrag(int lane) {
+    const int c = lane % 32, hh = lane / 32;
+    const uint32_t m = swz_mask<T, D>((uint32_t)c);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[i] = a[i];
-      f[4 + i] = b[i];
-    }
-    return f;
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < kReads; ++i) {
+        const uint32_t chunk = (uint32_t)((16 * kb + 8 * hh) / kVec + i);
+        off[kb][i] = c * D + (int)((chunk ^ m) * kVec);
+      }
   }
-}
+  // See TrSwz::pinned.
+  __device__ __forceinline__ RowFrag pinned() const {
+    RowFrag t = *this;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < kReads; ++i) asm volatile("" : "+v"(t.off[kb][i]));
+    return t;
+  }
+  __device__ __forceinline__ frag operator()(const lds_t<T> *tile, int blk, int kb) const {
+    const lds_t<T> *p = tile + blk * 32 * D;
+    if constexpr (sizeof(T) == 2) {
+      return *(const lds_t<frag> *)(p + off[kb][0]);
+    } else {
+      const f32x4 a = *(const lds_t<f32x4> *)(p + off[kb][0]);
+      const f32x4 b = *(const lds_t<f32x4> *)(p + off[kb][1]);
+      frag f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[i] = a[i];
+        f[4 + i] = b[i];
+      }
+      return f;
+    }
+  }
+};
 
 // Wait until at most N of this wave's vector-memory operations (including
 // direct-to-LDS copies) are outstanding.

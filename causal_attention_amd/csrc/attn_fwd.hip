@@ -98,15 +98,18 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
 
+  const RowFrag<T, D> rf0(lane);  // row fragments of the K tiles
+
   // S^T = K Q^T for the key tile in `ks`.
   auto scores = [&](const lds_t<T> *ks, f32x16 (&sacc)[NB]) {
+    const RowFrag<T, D> rf = rf0.pinned();
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) sacc[nb] = f32x16{};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const frag a = swz_frag<T, D, KTile::kSW>(ks, nb * 32 + c, (16 * kb + 8 * hh) / KTile::kVec);
+        const frag a = rf(ks, nb, kb);
         E::mma(sacc[nb], a, qf[kb]);
       }
   };
