@@ -521,22 +521,38 @@ struct RowTile {
   bool valid;
 };
 
-// Causal mode: tiles of BM rows, `ntiles` per head.  Block ids are remapped so
-// that each XCD (block id mod 8 on MI355X) receives a contiguous range of
-// heads, keeping one head's K and V in one XCD's L2, and within a head the
-// tiles are visited longest-first (most key tiles first), which shortens the
-// tail of the causal triangle.
+// Causal mode: a 1-D grid over (tile, head).  Workgroups are dealt to the 8
+// XCDs round-robin (block b runs on XCD b % 8) and, within an XCD, to its 32
+// CUs round-robin (local index l = b / 8 on CU l % 32); when every workgroup
+// is resident at once, a CU therefore runs local indices l, l+32, l+64, ...
+// together.  Each XCD gets a contiguous range of heads (so re-reads of a
+// head's K/V or Q/dO stay in that XCD's L2); its tiles are ranked by work
+// (the causal diagonal makes tile t of a head do t+1 or ntiles-t units) and
+// dealt in snake order over rounds of 32 (round r, position p -> rank 32r + p,
+// or 32r + 31 - p on odd rounds), so each CU gets a heavy and a light tile per
+// pair of rounds, and if the launch does not fit at once the heaviest tiles
+// still start first.  heavy_first: tile work grows with the tile index
+// (query tiles); otherwise it shrinks (key tiles of the dK/dV kernel).
 __device__ __forceinline__ RowTile causal_tile(int bid, int nblocks, int ntiles, int BM, int S,
                                                bool heavy_first) {
-  int id = bid;
-  if ((nblocks & 7) == 0) {
-    const int per_xcd = nblocks >> 3;
-    id = (bid & 7) * per_xcd + (bid >> 3);
+  int head, rank;
+  const int per_xcd = nblocks >> 3;
+  if ((nblocks & 7) == 0 && per_xcd % ntiles == 0) {
+    const int heads_x = per_xcd / ntiles;  // heads on this XCD
+    const int l = bid >> 3;
+    const int round0 = l & ~31;
+    const int m = min(32, per_xcd - round0);  // size of this (possibly partial) round
+    const int pos = l & 31;
+    const int s = round0 + (((l >> 5) & 1) ? m - 1 - pos : pos);
+    rank = s / heads_x;
+    head = (bid & 7) * heads_x + s % heads_x;
+  } else {
+    head = bid / ntiles;
+    rank = bid % ntiles;
   }
   RowTile t;
-  t.head = id / ntiles;
-  int ti = id % ntiles;
-  if (heavy_first) ti = ntiles - 1 - ti;
+  t.head = head;
+  const int ti = heavy_first ? ntiles - 1 - rank : rank;
   t.r_start = ti * BM;
   t.r_end = min(t.r_start + BM, S);
   t.seg_start = 0;
