@@ -28,8 +28,11 @@ int check_mask(int B, int H, int S, int mask_mode, const int32_t *cu_seqlens, in
   if (mask_mode == ATTN_MASK_CAUSAL) return ATTN_OK;
   if (mask_mode != ATTN_MASK_DOC_CAUSAL) return ATTN_ERR_MASK;
   if (cu_seqlens == nullptr) return ATTN_ERR_NULL;
-  if (B != 1 || n_seqs < 1 || n_seqs > S || n_seqs > 65535 || H > 65535) return ATTN_ERR_SEQLENS;
+  if (B != 1 || n_seqs < 1 || n_seqs > S) return ATTN_ERR_SEQLENS;
   if (max_seqlen < 1 || max_seqlen > S) return ATTN_ERR_SEQLENS;
+  // the launch has one workgroup per (128-row tile of the longest document,
+  // document, head)
+  if ((int64_t)((max_seqlen + 127) / 128) * n_seqs * H >= ((int64_t)1 << 31)) return ATTN_ERR_SEQLENS;
   return ATTN_OK;
 }
 

@@ -77,7 +77,7 @@ template <typename T, int D, int BMQ, int MINB, bool DOC>
 __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, float *__restrict__ dk,
-    float *__restrict__ dv, int S, float c2, float scale, const int32_t *__restrict__ cu, int ntiles) {
+    float *__restrict__ dv, int S, float c2, float scale, const int32_t *__restrict__ cu, int ntiles, int n_seqs) {
   constexpr int NW = 4;
   constexpr int NT = NW * kWaveSize;
   constexpr int BN = NW * 32;  // keys per workgroup
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(256))) float sD0[64];    // Delta
   __shared__ __attribute__((aligned(256))) float sD1[64];
 
-  const RowTile t = DOC ? doc_tile(cu, blockIdx.x, gridDim.x, blockIdx.y, blockIdx.z, BN, false)
+  const RowTile t = DOC ? doc_tile(cu, blockIdx.x, gridDim.x, ntiles, n_seqs, BN, false)
                         : causal_tile(blockIdx.x, gridDim.x, ntiles, BN, S, false);
   if (!t.valid) return;
 
@@ -255,7 +255,7 @@ template <typename T, int D, int BN, int MINB, bool DOC>
 __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, float *__restrict__ dq, int S, float c2,
-    float scale, const int32_t *__restrict__ cu, int ntiles) {
+    float scale, const int32_t *__restrict__ cu, int ntiles, int n_seqs) {
   constexpr int NW = 4;
   constexpr int NT = NW * kWaveSize;
   constexpr int BM = NW * 32;
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) T sV0[BN * D];
   __shared__ __attribute__((aligned(1024))) T sV1[BN * D];
 
-  const RowTile t = DOC ? doc_tile(cu, blockIdx.x, gridDim.x, blockIdx.y, blockIdx.z, BM, true)
+  const RowTile t = DOC ? doc_tile(cu, blockIdx.x, gridDim.x, ntiles, n_seqs, BM, true)
                         : causal_tile(blockIdx.x, gridDim.x, ntiles, BM, S, true);
   if (!t.valid) return;
 
@@ -427,7 +427,7 @@ static hipError_t launch_dkdv_t(const Args &a) {
   int ntiles;
   if (DOC) {
     ntiles = (a.max_seqlen + BN - 1) / BN;
-    grid = dim3(ntiles, a.n_seqs, a.H);
+    grid = dim3(ntiles * a.n_seqs * a.H);
   } else {
     ntiles = (a.S + BN - 1) / BN;
     grid = dim3(ntiles * a.B * a.H);
@@ -435,7 +435,7 @@ static hipError_t launch_dkdv_t(const Args &a) {
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, BMQ, MINB, DOC>), grid, dim3(256), 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
                      static_cast<const T *>(a.dO), a.lse_in, a.delta_in, a.dk, a.dv, a.S, c2, a.scale,
-                     a.cu_seqlens, ntiles);
+                     a.cu_seqlens, ntiles, a.n_seqs);
   return hipGetLastError();
 }
 
@@ -449,7 +449,7 @@ static hipError_t launch_dq_t(const Args &a) {
   int ntiles;
   if (DOC) {
     ntiles = (a.max_seqlen + BM - 1) / BM;
-    grid = dim3(ntiles, a.n_seqs, a.H);
+    grid = dim3(ntiles * a.n_seqs * a.H);
   } else {
     ntiles = (a.S + BM - 1) / BM;
     grid = dim3(ntiles * a.B * a.H);
@@ -457,7 +457,7 @@ static hipError_t launch_dq_t(const Args &a) {
   hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, MINB, DOC>), grid, dim3(256), 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
                      static_cast<const T *>(a.dO), a.lse_in, a.delta_in, a.dq, a.S, c2, a.scale, a.cu_seqlens,
-                     ntiles);
+                     ntiles, a.n_seqs);
   return hipGetLastError();
 }
 

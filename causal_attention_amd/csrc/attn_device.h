@@ -521,38 +521,45 @@ struct RowTile {
   bool valid;
 };
 
-// Causal mode: a 1-D grid over (tile, head).  Workgroups are dealt to the 8
-// XCDs round-robin (block b runs on XCD b % 8) and, within an XCD, to its 32
-// CUs round-robin (local index l = b / 8 on CU l % 32); when every workgroup
+// Tile schedule.  Workgroups are dealt to the 8 XCDs round-robin (block b
+// runs on XCD b % 8) and, within an XCD, to its 32 CUs round-robin (local
+// index l = b / 8 on CU l % 32), as measured on MI355X; when every workgroup
 // is resident at once, a CU therefore runs local indices l, l+32, l+64, ...
-// together.  Each XCD gets a contiguous range of heads (so re-reads of a
-// head's K/V or Q/dO stay in that XCD's L2); its tiles are ranked by work
-// (the causal diagonal makes tile t of a head do t+1 or ntiles-t units) and
-// dealt in snake order over rounds of 32 (round r, position p -> rank 32r + p,
-// or 32r + 31 - p on odd rounds), so each CU gets a heavy and a light tile per
-// pair of rounds, and if the launch does not fit at once the heaviest tiles
-// still start first.  heavy_first: tile work grows with the tile index
-// (query tiles); otherwise it shrinks (key tiles of the dK/dV kernel).
-__device__ __forceinline__ RowTile causal_tile(int bid, int nblocks, int ntiles, int BM, int S,
-                                               bool heavy_first) {
-  int head, rank;
+// together.  A launch covers `nunits` independent units (heads, or document x
+// head pairs) of `nranks` tiles each, and a tile's rank orders it by work
+// (rank 0 the most).  Each XCD gets a contiguous range of units (so re-reads
+// of a unit's K/V or Q/dO stay in that XCD's L2); its tiles are sorted by
+// rank and dealt in snake order over rounds of 32 (round r, position p ->
+// sorted slot 32r + p, or 32r + 31 - p on odd rounds), so each CU gets a heavy
+// and a light tile per pair of rounds, and if the launch does not fit at once
+// the heaviest tiles still start first.
+struct TileSlot {
+  int unit;
+  int rank;
+};
+__device__ __forceinline__ TileSlot snake_slot(int bid, int nblocks, int nranks) {
   const int per_xcd = nblocks >> 3;
-  if ((nblocks & 7) == 0 && per_xcd % ntiles == 0) {
-    const int heads_x = per_xcd / ntiles;  // heads on this XCD
+  if ((nblocks & 7) == 0 && per_xcd % nranks == 0) {
+    const int units_x = per_xcd / nranks;  // units on this XCD
     const int l = bid >> 3;
     const int round0 = l & ~31;
     const int m = min(32, per_xcd - round0);  // size of this (possibly partial) round
     const int pos = l & 31;
     const int s = round0 + (((l >> 5) & 1) ? m - 1 - pos : pos);
-    rank = s / heads_x;
-    head = (bid & 7) * heads_x + s % heads_x;
-  } else {
-    head = bid / ntiles;
-    rank = bid % ntiles;
+    return {(bid & 7) * units_x + s % units_x, s / units_x};
   }
+  return {bid / nranks, bid % nranks};
+}
+
+// Causal mode: 1-D grid of ntiles * B * H blocks; unit = head.  heavy_first:
+// tile work grows with the tile index (query tiles: t + 1 key tiles); else it
+// shrinks (key tiles of the dK/dV kernel: ntiles - t query tiles).
+__device__ __forceinline__ RowTile causal_tile(int bid, int nblocks, int ntiles, int BM, int S,
+                                               bool heavy_first) {
+  const TileSlot sl = snake_slot(bid, nblocks, ntiles);
+  const int ti = heavy_first ? ntiles - 1 - sl.rank : sl.rank;
   RowTile t;
-  t.head = head;
-  const int ti = heavy_first ? ntiles - 1 - rank : rank;
+  t.head = sl.unit;
   t.r_start = ti * BM;
   t.r_end = min(t.r_start + BM, S);
   t.seg_start = 0;
@@ -561,14 +568,18 @@ __device__ __forceinline__ RowTile causal_tile(int bid, int nblocks, int ntiles,
   return t;
 }
 
-// Packed-document mode: grid (tiles per longest document, documents, heads).
-__device__ __forceinline__ RowTile doc_tile(const int32_t *__restrict__ cu, int tile_x, int ntiles_x,
-                                            int doc, int head, int BM, bool heavy_first) {
-  RowTile t;
+// Packed-document mode: 1-D grid of ntiles * n_seqs * H blocks, ntiles the
+// tile count of the longest document; unit = head * n_seqs + document.  Tiles
+// past a document's end are invalid (the workgroup exits at once).
+__device__ __forceinline__ RowTile doc_tile(const int32_t *__restrict__ cu, int bid, int nblocks, int ntiles,
+                                            int n_seqs, int BM, bool heavy_first) {
+  const TileSlot sl = snake_slot(bid, nblocks, ntiles);
+  const int doc = sl.unit % n_seqs;
   const int ds = cu[doc];
   const int de = cu[doc + 1];
-  const int ti = heavy_first ? (ntiles_x - 1 - tile_x) : tile_x;
-  t.head = head;
+  const int ti = heavy_first ? ntiles - 1 - sl.rank : sl.rank;
+  RowTile t;
+  t.head = sl.unit / n_seqs;
   t.r_start = ds + ti * BM;
   t.r_end = min(t.r_start + BM, de);
   t.seg_start = ds;

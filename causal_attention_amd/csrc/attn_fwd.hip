@@ -38,7 +38,7 @@ template <typename T, int D, int NW, int BN, int MINB, bool DOC>
 __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                                  const T *__restrict__ v, float *__restrict__ o,
                                                                  float *__restrict__ lse, int S, float c2,
-                                                                 const int32_t *__restrict__ cu, int ntiles) {
+                                                                 const int32_t *__restrict__ cu, int ntiles, int n_seqs) {
   constexpr int NT = NW * kWaveSize;
   constexpr int BM = NW * 32;  // query rows per workgroup
   constexpr int KB = D / 16;   // k-blocks over the head dimension
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
   __shared__ __attribute__((aligned(1024))) T sV0[BN * D];
   __shared__ __attribute__((aligned(1024))) T sV1[BN * D];
 
-  const RowTile t = DOC ? doc_tile(cu, blockIdx.x, gridDim.x, blockIdx.y, blockIdx.z, BM, true)
+  const RowTile t = DOC ? doc_tile(cu, blockIdx.x, gridDim.x, ntiles, n_seqs, BM, true)
                         : causal_tile(blockIdx.x, gridDim.x, ntiles, BM, S, true);
   if (!t.valid) return;
 
@@ -250,14 +250,14 @@ static hipError_t launch_fwd_t(const Args &a) {
   int ntiles;
   if (DOC) {
     ntiles = (a.max_seqlen + BM - 1) / BM;
-    grid = dim3(ntiles, a.n_seqs, a.H);
+    grid = dim3(ntiles * a.n_seqs * a.H);
   } else {
     ntiles = (a.S + BM - 1) / BM;
     grid = dim3(ntiles * a.B * a.H);
   }
   hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW, BN, MINB, DOC>), grid, block, 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
-                     a.o, a.lse, a.S, c2, a.cu_seqlens, ntiles);
+                     a.o, a.lse, a.S, c2, a.cu_seqlens, ntiles, a.n_seqs);
   return hipGetLastError();
 }
 
