@@ -136,9 +136,12 @@ class Workload:
         return (time.perf_counter() - t0) / steps
 
     def kernel_times(self, reps):
-        """Mean duration of each kernel (ms) from HIP events recorded on the launch stream."""
+        """Mean duration (ms) from HIP events recorded on the launch stream: the
+        forward, the whole backward call, and the three backward stages run one
+        by one through their own entry points (with bf16 inputs attn_bwd runs
+        dQ with Delta fused, then dK/dV; the staged dQ reads Delta instead)."""
         import torch
-        stages = [("fwd", self.fwd), ("pre", self.pre), ("dkdv", self.dkdv), ("dq", self.dqk)]
+        stages = [("fwd", self.fwd), ("bwd", self.bwd), ("pre", self.pre), ("dkdv", self.dkdv), ("dq", self.dqk)]
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(reps)]
         for _ in range(3):
             self.step()
@@ -254,7 +257,7 @@ def write_traffic(fetch_dir, write_dir, workload, mib):
 def roofline(w, times):
     """The dominant kernel (most time per step) against its roofline."""
     peak = PEAK_BF16_TFLOPS if w.cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
-    dom = max(times, key=lambda k: times[k]["mean_ms"])
+    dom = max((k for k in times if k in KERNEL_FLOPS_PER_PAIR or k == "pre"), key=lambda k: times[k]["mean_ms"])
     t = times[dom]["mean_ms"] * 1e-3
     if dom == "pre":
         achieved = w.preprocess_bytes() / t / 1e9
@@ -305,7 +308,7 @@ def measure(name, steps, warmup, reps):
     times = w.kernel_times(reps)
     peak = PEAK_BF16_TFLOPS if w.cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
     ms_fwd = times["fwd"]["mean_ms"]
-    ms_bwd = sum(times[k]["mean_ms"] for k in ("pre", "dkdv", "dq"))
+    ms_bwd = times["bwd"]["mean_ms"]
     summary = {
         "tflops": tflops, "pct_peak": 100.0 * tflops / peak, "ms_per_step": sec * 1e3,
         "fwd_tflops": w.flops_fwd / (ms_fwd * 1e-3) / 1e12,

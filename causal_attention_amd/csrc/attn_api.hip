@@ -170,9 +170,17 @@ int attn_bwd(const void *q, const void *k, const void *v, const float *o, const 
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  hipError_t e = attn::launch_bwd_preprocess(a);
-  if (e == hipSuccess) e = attn::launch_bwd_dkdv(a);
-  if (e == hipSuccess) e = attn::launch_bwd_dq(a);
+  hipError_t e;
+  if (a.bf16) {
+    // dQ computes Delta on the way (bitwise equal to the preprocess kernel's)
+    // and writes it for dK/dV: one pass over O and dO fewer.
+    e = attn::launch_bwd_dq_delta(a);
+    if (e == hipSuccess) e = attn::launch_bwd_dkdv(a);
+  } else {
+    e = attn::launch_bwd_preprocess(a);
+    if (e == hipSuccess) e = attn::launch_bwd_dkdv(a);
+    if (e == hipSuccess) e = attn::launch_bwd_dq(a);
+  }
   return to_status(e);
 }
 

@@ -176,6 +176,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     const lds_t<float> *sd = dslot.template operator()<P>();
     const TrSwz<T, D> tr = tr0.pinned();
     const RowFrag<T, D> rf = rf0.pinned();
+    ATTN_SCHED_HINT();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       f32x16 sacc = f32x16{}, pacc = f32x16{};
@@ -251,11 +252,24 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
 // over key tiles of BN rows up to its causal diagonal.  K and V tiles arrive
 // by direct global->LDS copies into two ring slots one iteration ahead; K is
 // read both as row fragments and, through the transposing load, as K^T.
-template <typename T, int D, int BN, int MINB, bool DOC>
+template <int LPR, int M, int J, int KB>
+__device__ __forceinline__ float delta_tree(const float (&part)[KB]) {
+  if constexpr (M == LPR)
+    return part[J];
+  else
+    return delta_tree<LPR, 2 * M, J, KB>(part) + delta_tree<LPR, 2 * M, J + M / 2, KB>(part);
+}
+
+// FUSE_DELTA (bf16 inputs): the kernel also computes Delta_i = sum_d dO_id O_id
+// for its queries from O, in the same summation order as the preprocess
+// kernel (so the result is bitwise the same), uses it, and writes it to
+// `delta_out` for the dK/dV kernel that runs after it.
+template <typename T, int D, int BN, int MINB, bool DOC, bool FUSE_DELTA>
 __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dO,
-    const float *__restrict__ lse, const float *__restrict__ delta, float *__restrict__ dq, int S, float c2,
-    float scale, const int32_t *__restrict__ cu, int ntiles, int n_seqs) {
+    const float *__restrict__ lse, const float *__restrict__ delta, const float *__restrict__ o,
+    float *__restrict__ delta_out, float *__restrict__ dq, int S, float c2, float scale,
+    const int32_t *__restrict__ cu, int ntiles, int n_seqs) {
   constexpr int NW = 4;
   constexpr int NT = NW * kWaveSize;
   constexpr int BM = NW * 32;
@@ -313,7 +327,34 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
     df[kb] = global_frag<T, D>(gdo, qi, 16 * kb + 8 * hh);
   }
   const float l2 = glse.load4((uint32_t)qi * 4) * kLog2e;
-  const float dl = gdel.load4((uint32_t)qi * 4);
+  float dl;
+  if constexpr (FUSE_DELTA) {
+    static_assert(sizeof(T) == 2, "fused Delta follows the bf16 preprocess layout");
+    // The preprocess kernel gives lane `sub` of a row elements 8*sub .. 8*sub+7
+    // (an FMA chain from 0) and reduces the D/8 partial sums by butterfly.
+    // Fragment kb of this lane is sub-block 2*kb + hh, so the lane computes
+    // the butterfly's tree over its own sub-blocks and one swap across the
+    // halves adds the other half's.
+    const GBuf go(o + base, (uint32_t)(t.r_end * D * sizeof(float)));
+    float part[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const uint32_t off = (uint32_t)(qi * D + 16 * kb + 8 * hh) * sizeof(float);
+      const f32x4 o0 = __builtin_bit_cast(f32x4, go.load16(off));
+      const f32x4 o1 = __builtin_bit_cast(f32x4, go.load16(off + 16));
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc += (float)df[kb][i] * o0[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc += (float)df[kb][4 + i] * o1[i];
+      part[kb] = acc;
+    }
+    const float mine = delta_tree<2 * KB, 2, 0, KB>(part);
+    dl = mine + swap_halves(mine);
+    if (hh == 0 && qi < t.r_end) delta_out[rbase + qi] = dl;
+  } else {
+    dl = gdel.load4((uint32_t)qi * 4);
+  }
   f32x16 dqacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
@@ -328,7 +369,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
     const lds_t<T> *sv = vslot.template operator()<P>();
     const TrSwz<T, D> tr = tr0.pinned();
     const RowFrag<T, D> rf = rf0.pinned();
-
+    ATTN_SCHED_HINT();
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       f32x16 sacc = f32x16{}, pacc = f32x16{};
@@ -439,7 +480,7 @@ static hipError_t launch_dkdv_t(const Args &a) {
   return hipGetLastError();
 }
 
-template <typename T, int D, bool DOC>
+template <typename T, int D, bool DOC, bool FUSE_DELTA = false>
 static hipError_t launch_dq_t(const Args &a) {
   constexpr int BN = BwdCfg<T, D>::BN;
   constexpr int MINB = BwdCfg<T, D>::MINB_DQ;
@@ -454,10 +495,10 @@ static hipError_t launch_dq_t(const Args &a) {
     ntiles = (a.S + BM - 1) / BM;
     grid = dim3(ntiles * a.B * a.H);
   }
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, MINB, DOC>), grid, dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, MINB, DOC, FUSE_DELTA>), grid, dim3(256), 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
-                     static_cast<const T *>(a.dO), a.lse_in, a.delta_in, a.dq, a.S, c2, a.scale, a.cu_seqlens,
-                     ntiles, a.n_seqs);
+                     static_cast<const T *>(a.dO), a.lse_in, a.delta_in, a.o_in, a.delta, a.dq, a.S, c2, a.scale,
+                     a.cu_seqlens, ntiles, a.n_seqs);
   return hipGetLastError();
 }
 
@@ -487,6 +528,20 @@ hipError_t launch_bwd_dkdv(const Args &a) {
 hipError_t launch_bwd_dq(const Args &a) {
   if (a.bf16) return a.doc ? launch_dq_dt<bf16, true>(a) : launch_dq_dt<bf16, false>(a);
   return a.doc ? launch_dq_dt<float, true>(a) : launch_dq_dt<float, false>(a);
+}
+
+template <bool DOC>
+static hipError_t launch_dq_delta_d(const Args &a) {
+  switch (a.D) {
+    case 32: return launch_dq_t<bf16, 32, DOC, true>(a);
+    case 64: return launch_dq_t<bf16, 64, DOC, true>(a);
+    default: return launch_dq_t<bf16, 128, DOC, true>(a);
+  }
+}
+
+hipError_t launch_bwd_dq_delta(const Args &a) {
+  if (!a.bf16) return hipErrorInvalidValue;
+  return a.doc ? launch_dq_delta_d<true>(a) : launch_dq_delta_d<false>(a);
 }
 
 }  // namespace attn

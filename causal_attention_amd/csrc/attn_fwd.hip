@@ -179,6 +179,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
     wg_barrier();
     if (j + 1 < ntile) issue.template operator()<1 - P>(j + 1);
     if (j >= jw) return;
+    ATTN_SCHED_HINT();
     const int k0 = kv_lo + j * BN;
     const bool masked = (k0 + BN - 1 > w0) || (k0 + BN > t.seg_end);
     const lds_t<T> *ks = kslot.template operator()<P>();

@@ -25,5 +25,7 @@ hipError_t launch_fwd(const Args &a);
 hipError_t launch_bwd_preprocess(const Args &a);
 hipError_t launch_bwd_dkdv(const Args &a);
 hipError_t launch_bwd_dq(const Args &a);
+// bf16 only: dQ that also computes Delta from O and dO (written to a.delta)
+hipError_t launch_bwd_dq_delta(const Args &a);
 
 }  // namespace attn
