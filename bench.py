@@ -190,6 +190,15 @@ KERNEL_NAMES = {"attn_fwd_kernel": "fwd", "attn_bwd_preprocess_kernel": "pre",
                 "attn_bwd_dkdv_kernel": "dkdv", "attn_bwd_dq_kernel": "dq", "neg_kernel": "copy"}
 
 
+def kernel_key(name):
+    """Short name of a kernel from its (mangled or demangled) name; the dQ kernel
+    with Delta fused (last template flag set) is 'dq_delta'."""
+    key = next((v for k, v in KERNEL_NAMES.items() if k in name), None)
+    if key == "dq" and ("Lb1EEEv" in name or name.rstrip(")").endswith("true>")):
+        key = "dq_delta"
+    return key
+
+
 def copy_calibration(mib):
     """A plain elementwise kernel of known HBM traffic: reads and writes mib MiB."""
     import torch
@@ -218,7 +227,7 @@ def _per_dispatch_kib(directory, counter):
     for row in _counter_rows(directory):
         if row["Counter_Name"] != counter:
             continue
-        name = next((v for k, v in KERNEL_NAMES.items() if k in row["Kernel_Name"]), None)
+        name = kernel_key(row["Kernel_Name"])
         if name is None:
             continue
         d = acc.setdefault(name, {})
@@ -238,7 +247,7 @@ def write_traffic(fetch_dir, write_dir, workload, mib):
     f_fetch = fetch["copy"] / known_kib
     f_write = write["copy"] / known_kib
     kernels = {}
-    for k in ("fwd", "pre", "dkdv", "dq"):
+    for k in ("fwd", "pre", "dkdv", "dq", "dq_delta"):
         if k in fetch and k in write:
             fb = fetch[k] * 1024 / f_fetch
             wb = write[k] * 1024 / f_write
