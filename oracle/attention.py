@@ -33,6 +33,12 @@ Readings where the pages are silent (each is listed in the design notes):
     rowsum(dO o O), which the kernels use (``delta_ref``).
 
 All arrays are float64 in [B, H, S, D] (LSE and Delta [B, H, S]).
+
+Grouped-query attention (Forge, "Architecture": attention with GQA behind an
+interface): K and V may have H_kv heads, H_kv dividing H; query head h then
+reads K/V head h // (H / H_kv) (consecutive query heads share one K/V head).
+The definition is plain attention with each K/V head repeated for its query
+heads; dK and dV of a K/V head are the sums of the gradients of its copies.
 """
 from __future__ import annotations
 
@@ -90,6 +96,14 @@ def _heads(B, H, heads):
     return list(heads)
 
 
+def _group(q, k, v):
+    """Query heads per K/V head (1 for plain multi-head attention)."""
+    H, H_kv = q.shape[1], k.shape[1]
+    if H_kv < 1 or H % H_kv != 0 or v.shape[1] != H_kv:
+        raise ValueError("K/V heads must divide the query heads")
+    return H // H_kv
+
+
 def attention_fwd_ref(q, k, v, scale, mask_mode=MASK_CAUSAL, cu_seqlens=None, heads=None):
     """Forward attention.  Returns (O [B,H,S,D], LSE [B,H,S]) in float64.
 
@@ -97,11 +111,12 @@ def attention_fwd_ref(q, k, v, scale, mask_mode=MASK_CAUSAL, cu_seqlens=None, he
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
     B, H, S, D = q.shape
+    G = _group(q, k, v)
     allowed = allowed_mask(S, mask_mode, cu_seqlens)
     o = np.full((B, H, S, D), np.nan)
     lse = np.full((B, H, S), np.nan)
     for b, h in _heads(B, H, heads):
-        _, o[b, h], lse[b, h] = _head_forward(q[b, h], k[b, h], v[b, h], scale, allowed)
+        _, o[b, h], lse[b, h] = _head_forward(q[b, h], k[b, h // G], v[b, h // G], scale, allowed)
     return o, lse
 
 
@@ -109,16 +124,23 @@ def attention_bwd_ref(q, k, v, do, scale, mask_mode=MASK_CAUSAL, cu_seqlens=None
     """Forward and analytic backward.  Returns a dict of float64 arrays:
     ``o, lse, dq, dk, dv, delta`` (``delta`` = rowsum(P o dP)).
 
-    ``heads``: optional list of (b, h) to compute; other heads are left NaN.
+    ``heads``: optional list of (b, h) to compute; other heads are left NaN
+    (plain multi-head attention only: with grouped heads dK and dV need every
+    query head of a group).  dk and dv have K's shape.
     """
     q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
     B, H, S, D = q.shape
+    G = _group(q, k, v)
+    if G > 1 and heads is not None:
+        raise ValueError("head selection needs plain multi-head attention")
     allowed = allowed_mask(S, mask_mode, cu_seqlens)
-    out = {name: np.full((B, H, S, D), np.nan) for name in ("o", "dq", "dk", "dv")}
+    out = {name: np.full((B, H, S, D), np.nan) for name in ("o", "dq")}
+    for name in ("dk", "dv"):
+        out[name] = np.full(k.shape, np.nan) if G == 1 else np.zeros(k.shape)
     out["lse"] = np.full((B, H, S), np.nan)
     out["delta"] = np.full((B, H, S), np.nan)
     for b, h in _heads(B, H, heads):
-        qh, kh, vh, doh = q[b, h], k[b, h], v[b, h], do[b, h]
+        qh, kh, vh, doh = q[b, h], k[b, h // G], v[b, h // G], do[b, h]
         p, o, lse = _head_forward(qh, kh, vh, scale, allowed)
         dv = p.T @ doh
         dp = doh @ vh.T
@@ -126,9 +148,13 @@ def attention_bwd_ref(q, k, v, do, scale, mask_mode=MASK_CAUSAL, cu_seqlens=None
         ds = p * (dp - delta[:, None])
         out["o"][b, h] = o
         out["lse"][b, h] = lse
-        out["dv"][b, h] = dv
         out["dq"][b, h] = scale * (ds @ kh)
-        out["dk"][b, h] = scale * (ds.T @ qh)
+        if G == 1:
+            out["dv"][b, h] = dv
+            out["dk"][b, h] = scale * (ds.T @ qh)
+        else:  # this head's share of its K/V head's gradient
+            out["dv"][b, h // G] += dv
+            out["dk"][b, h // G] += scale * (ds.T @ qh)
         out["delta"][b, h] = delta
     return out
 

@@ -342,3 +342,87 @@ def test_heads_selection_computes_only_those_heads():
     for name in full:
         assert np.array_equal(full[name][1, 0], part[name][1, 0])
         assert np.all(np.isnan(part[name][0, 0]))
+
+
+# ---------------------------------------------------------------- grouped-query attention
+
+def _gqa_inputs(B, H, H_kv, S, D, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, S, D))
+    k = rng.standard_normal((B, H_kv, S, D))
+    v = rng.standard_normal((B, H_kv, S, D))
+    do = rng.standard_normal((B, H, S, D))
+    return q, k, v, do
+
+
+@pytest.mark.parametrize("mode", [MASK_CAUSAL, MASK_DOC_CAUSAL])
+@pytest.mark.parametrize("H,H_kv", [(4, 2), (6, 2), (4, 1)])
+def test_gqa_equals_mha_on_repeated_kv(mode, H, H_kv):
+    """Grouped heads = plain attention with each K/V head repeated for its G query
+    heads (consecutive heads share one K/V head); dK, dV = sums over the copies."""
+    B, S, D = 2, 20, 8
+    q, k, v, do = _gqa_inputs(B, H, H_kv, S, D, 20 + H + H_kv)
+    G = H // H_kv
+    cu = CU_SMALL if mode == MASK_DOC_CAUSAL else None
+    r = attention_bwd_ref(q, k, v, do, 0.35, mode, cu)
+    kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    m = attention_bwd_ref(q, kr, vr, do, 0.35, mode, cu)
+    for name in ("o", "lse", "dq", "delta"):
+        np.testing.assert_allclose(r[name], m[name], rtol=1e-13, atol=1e-14)
+    for name in ("dk", "dv"):
+        summed = m[name].reshape(B, H_kv, G, S, D).sum(axis=2)
+        np.testing.assert_allclose(r[name], summed, rtol=1e-12, atol=1e-13)
+    o, lse = attention_fwd_ref(q, k, v, 0.35, mode, cu)
+    np.testing.assert_allclose(o, m["o"], rtol=1e-13, atol=1e-14)
+
+
+def test_gqa_matches_torch_enable_gqa_and_autograd():
+    """PyTorch's CPU SDPA with enable_gqa=True in float64, differentiated by autograd."""
+    torch = pytest.importorskip("torch")
+    B, H, H_kv, S, D = 2, 6, 2, 18, 16
+    q, k, v, do = _gqa_inputs(B, H, H_kv, S, D, 31)
+    scale = 1 / math.sqrt(D)
+    r = attention_bwd_ref(q, k, v, do, scale)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale,
+                                                          enable_gqa=True)
+    to.backward(torch.tensor(do))
+    np.testing.assert_allclose(r["o"], to.detach().numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(r["dq"], tq.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(r["dk"], tk.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(r["dv"], tv.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_gqa_gradients_match_central_differences():
+    """dK and dV of a shared K/V head against central differences of L = sum(O * dO)."""
+    B, H, H_kv, S, D = 1, 4, 2, 10, 4
+    q, k, v, do = _gqa_inputs(B, H, H_kv, S, D, 32)
+    scale = 0.5
+
+    def loss():
+        o, _ = attention_fwd_ref(q, k, v, scale)
+        return float(np.sum(o * do))
+
+    r = attention_bwd_ref(q, k, v, do, scale)
+    h = 1e-6
+    for name, x in (("dk", k), ("dv", v), ("dq", q)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            orig = x[idx]
+            x[idx] = orig + h
+            lp = loss()
+            x[idx] = orig - h
+            lm = loss()
+            x[idx] = orig
+            fd[idx] = (lp - lm) / (2 * h)
+        err = np.max(np.abs(fd - r[name])) / np.max(np.abs(r[name]))
+        assert err < 1e-7, (name, err)
+
+
+def test_gqa_rejects_heads_that_do_not_divide():
+    q, k, v, do = _gqa_inputs(1, 4, 3, 8, 4, 33)
+    with pytest.raises(ValueError):
+        attention_fwd_ref(q, k, v, 0.5)
+    q, k, v, do = _gqa_inputs(1, 4, 2, 8, 4, 33)
+    with pytest.raises(ValueError):
+        attention_bwd_ref(q, k, v, do, 0.5, heads=[(0, 1)])
