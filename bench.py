@@ -38,7 +38,8 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 flop/CU/clk (dense)
 PEAK_FP32_TFLOPS = 157.3    # fp32 matrix/vector peak used for fp32 inputs
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "lm237m_ctx1024"
-SEEDS = {"tiny_f32": 1, "lm12m_ctx512": 2, "lm237m_ctx1024": 3, "long_ctx8192": 4, "packed_docs8192": 5}
+SEEDS = {"tiny_f32": 1, "lm12m_ctx512": 2, "lm237m_ctx1024": 3, "long_ctx8192": 4, "packed_docs8192": 5,
+         "lm237m_ctx1024_gqa4": 6}
 # algorithmic flops per allowed pair, per kernel (times D)
 KERNEL_FLOPS_PER_PAIR = {"fwd": 4, "dkdv": 8, "dq": 2}
 KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip"]
@@ -82,11 +83,12 @@ class Workload:
         d = {n: torch.from_numpy(x[n]).to("cuda").to(dt).contiguous() for n in ("q", "k", "v", "do")}
         self.q, self.k, self.v, self.do = d["q"], d["k"], d["v"], d["do"]
         B, H, S, D = x["B"], x["H"], x["S"], x["D"]
+        self.grouped = self.k.shape[1] != H
         f32 = dict(dtype=torch.float32, device="cuda")
         self.o = torch.empty((B, H, S, D), **f32)
         self.dq = torch.empty_like(self.o)
-        self.dk = torch.empty_like(self.o)
-        self.dv = torch.empty_like(self.o)
+        self.dk = torch.empty(tuple(self.k.shape), **f32)
+        self.dv = torch.empty_like(self.dk)
         self.lse = torch.empty((B, H, S), **f32)
         self.delta = torch.empty((B, H, S), **f32)
         cu = x["cu_seqlens"]
@@ -141,7 +143,9 @@ class Workload:
         by one through their own entry points (with bf16 inputs attn_bwd runs
         dQ with Delta fused, then dK/dV; the staged dQ reads Delta instead)."""
         import torch
-        stages = [("fwd", self.fwd), ("bwd", self.bwd), ("pre", self.pre), ("dkdv", self.dkdv), ("dq", self.dqk)]
+        stages = [("fwd", self.fwd), ("bwd", self.bwd)]
+        if not self.grouped:  # the staged entry points take plain multi-head inputs
+            stages += [("pre", self.pre), ("dkdv", self.dkdv), ("dq", self.dqk)]
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(reps)]
         for _ in range(3):
             self.step()
@@ -352,7 +356,7 @@ def main():
         f"{sec * 1e3:.4f} ms/step, kernels {summary['kernels_ms']}")
     by_workload = {a.workload: summary}
     if not a.no_others:
-        for name in ("lm12m_ctx512", "long_ctx8192", "packed_docs8192", "lm237m_ctx1024"):
+        for name in ("lm12m_ctx512", "long_ctx8192", "packed_docs8192", "lm237m_ctx1024_gqa4", "lm237m_ctx1024"):
             if name == a.workload:
                 continue
             _, _, _, s = measure(name, max(10, a.steps // 4), max(3, a.warmup // 2), max(10, a.kernel_reps // 2))

@@ -25,7 +25,7 @@ ATTN_DTYPE_BF16 = 1
 STATUS_NAMES = {
     0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEAD_DIM",
     -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_MASK", -6: "ATTN_ERR_SEQLENS", -7: "ATTN_ERR_HIP",
-    -8: "ATTN_ERR_UNIMPLEMENTED", -9: "ATTN_ERR_SCALE",
+    -8: "ATTN_ERR_UNIMPLEMENTED", -9: "ATTN_ERR_SCALE", -10: "ATTN_ERR_HEADS",
 }
 
 
@@ -46,6 +46,8 @@ SIGNATURES = {
     "attn_bwd_preprocess": [_P, _P, _P, _I, _I, _I, _I, _I, _P],
     "attn_bwd_dkdv": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
     "attn_bwd_dq": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
+    "attn_fwd_gqa": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
+    "attn_bwd_gqa": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
     "attn_status_string": [_I],
     "attn_abi_version": [],
 }
@@ -144,46 +146,59 @@ def _mask_args(mask_mode, cu_seqlens, n_seqs, max_seqlen, device):
     return None, 0, 0
 
 
-def _qkv_info(q, k, v):
+def _qkv_info(q, k, v, grouped=True):
+    """(B, H, H_kv, S, D, dtype code) of q [B,H,S,D] and k, v [B,H_kv,S,D]."""
     if q.dim() != 4:
         raise ValueError("q must be [B, H, S, D]")
     B, H, S, D = q.shape
+    if k.dim() != 4:
+        raise ValueError("k must be [B, H_kv, S, D]")
+    H_kv = k.shape[1] if grouped else H
     for name, t in (("k", k), ("v", v)):
-        if tuple(t.shape) != (B, H, S, D) or t.dtype != q.dtype:
-            raise ValueError(f"{name} must match q in shape and dtype")
-    return B, H, S, D, _dtype_code(q)
+        if tuple(t.shape) != (B, H_kv, S, D) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be [B, {H_kv}, S, D] with q's dtype"
+                             + ("" if grouped else " (this entry point has no grouped heads)"))
+    return B, H, H_kv, S, D, _dtype_code(q)
 
 
 def attn_fwd(q, k, v, o, lse, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None, n_seqs=None,
              max_seqlen=None, stream=None):
-    """Enqueue the forward: o [B,H,S,D] fp32 and lse [B,H,S] fp32 (or None)."""
+    """Enqueue the forward: o [B,H,S,D] fp32 and lse [B,H,S] fp32 (or None).
+    k and v may have fewer heads than q (grouped-query attention: attn_fwd_gqa)."""
     torch = _torch()
     lib = load_library()
-    B, H, S, D, dt = _qkv_info(q, k, v)
+    B, H, H_kv, S, D, dt = _qkv_info(q, k, v)
     dev = q.device
     cu, ns, ms = _mask_args(mask_mode, cu_seqlens, n_seqs, max_seqlen, dev)
-    _check(lib.attn_fwd(
-        _ptr(q, "q", device=dev), _ptr(k, "k", device=dev), _ptr(v, "v", device=dev),
-        _ptr(o, "o", (B, H, S, D), torch.float32, dev), _ptr(lse, "lse", (B, H, S), torch.float32, dev),
-        B, H, S, D, float(scale), int(mask_mode), cu, ns, ms, dt, _stream(stream)))
+    ptrs = (_ptr(q, "q", device=dev), _ptr(k, "k", device=dev), _ptr(v, "v", device=dev),
+            _ptr(o, "o", (B, H, S, D), torch.float32, dev), _ptr(lse, "lse", (B, H, S), torch.float32, dev))
+    tail = (S, D, float(scale), int(mask_mode), cu, ns, ms, dt, _stream(stream))
+    if H_kv == H:
+        _check(lib.attn_fwd(*ptrs, B, H, *tail))
+    else:
+        _check(lib.attn_fwd_gqa(*ptrs, B, H, H_kv, *tail))
 
 
 def attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None,
              n_seqs=None, max_seqlen=None, stream=None):
-    """Enqueue the backward: dq, dk, dv [B,H,S,D] fp32; delta [B,H,S] fp32 workspace."""
+    """Enqueue the backward: dq [B,H,S,D], dk, dv [B,H_kv,S,D] fp32; delta [B,H,S] fp32
+    workspace.  k and v may have fewer heads than q (attn_bwd_gqa)."""
     torch = _torch()
     lib = load_library()
-    B, H, S, D, dt = _qkv_info(q, k, v)
+    B, H, H_kv, S, D, dt = _qkv_info(q, k, v)
     dev = q.device
     cu, ns, ms = _mask_args(mask_mode, cu_seqlens, n_seqs, max_seqlen, dev)
     f32 = torch.float32
-    _check(lib.attn_bwd(
-        _ptr(q, "q", device=dev), _ptr(k, "k", device=dev), _ptr(v, "v", device=dev),
-        _ptr(o, "o", (B, H, S, D), f32, dev), _ptr(dO, "dO", (B, H, S, D), q.dtype, dev),
-        _ptr(lse, "lse", (B, H, S), f32, dev), _ptr(dq, "dq", (B, H, S, D), f32, dev),
-        _ptr(dk, "dk", (B, H, S, D), f32, dev), _ptr(dv, "dv", (B, H, S, D), f32, dev),
-        _ptr(delta, "delta", (B, H, S), f32, dev),
-        B, H, S, D, float(scale), int(mask_mode), cu, ns, ms, dt, _stream(stream)))
+    ptrs = (_ptr(q, "q", device=dev), _ptr(k, "k", device=dev), _ptr(v, "v", device=dev),
+            _ptr(o, "o", (B, H, S, D), f32, dev), _ptr(dO, "dO", (B, H, S, D), q.dtype, dev),
+            _ptr(lse, "lse", (B, H, S), f32, dev), _ptr(dq, "dq", (B, H, S, D), f32, dev),
+            _ptr(dk, "dk", (B, H_kv, S, D), f32, dev), _ptr(dv, "dv", (B, H_kv, S, D), f32, dev),
+            _ptr(delta, "delta", (B, H, S), f32, dev))
+    tail = (S, D, float(scale), int(mask_mode), cu, ns, ms, dt, _stream(stream))
+    if H_kv == H:
+        _check(lib.attn_bwd(*ptrs, B, H, *tail))
+    else:
+        _check(lib.attn_bwd_gqa(*ptrs, B, H, H_kv, *tail))
 
 
 def attn_bwd_preprocess(o, dO, delta, stream=None):
@@ -200,7 +215,7 @@ def attn_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, scale, mask_mode=ATTN_MASK_CA
                   n_seqs=None, max_seqlen=None, stream=None):
     torch = _torch()
     lib = load_library()
-    B, H, S, D, dt = _qkv_info(q, k, v)
+    B, H, _, S, D, dt = _qkv_info(q, k, v, grouped=False)
     dev = q.device
     cu, ns, ms = _mask_args(mask_mode, cu_seqlens, n_seqs, max_seqlen, dev)
     f32 = torch.float32
@@ -216,7 +231,7 @@ def attn_bwd_dq(q, k, v, dO, lse, delta, dq, scale, mask_mode=ATTN_MASK_CAUSAL, 
                 n_seqs=None, max_seqlen=None, stream=None):
     torch = _torch()
     lib = load_library()
-    B, H, S, D, dt = _qkv_info(q, k, v)
+    B, H, _, S, D, dt = _qkv_info(q, k, v, grouped=False)
     dev = q.device
     cu, ns, ms = _mask_args(mask_mode, cu_seqlens, n_seqs, max_seqlen, dev)
     f32 = torch.float32
@@ -246,8 +261,8 @@ def backward(q, k, v, o, dO, lse, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=
     torch = _torch()
     B, H, S, D = q.shape
     dq = torch.empty((B, H, S, D), dtype=torch.float32, device=q.device)
-    dk = torch.empty_like(dq)
-    dv = torch.empty_like(dq)
+    dk = torch.empty(tuple(k.shape), dtype=torch.float32, device=q.device)
+    dv = torch.empty_like(dk)
     delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode, cu_seqlens, None, max_seqlen, stream)
     return dq, dk, dv, delta

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 100;  // 1.00
+constexpr int kAbiVersion = 110;  // 1.10: grouped-query entry points
 
 int check_common(int B, int H, int S, int D, int dtype) {
   if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
@@ -36,6 +36,11 @@ int check_mask(int B, int H, int S, int mask_mode, const int32_t *cu_seqlens, in
   return ATTN_OK;
 }
 
+int check_heads(int H, int H_kv) {
+  if (H_kv < 1 || H_kv > H || H % H_kv != 0) return ATTN_ERR_HEADS;
+  return ATTN_OK;
+}
+
 int check_scale(float scale) {
   if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_SCALE;
   return ATTN_OK;
@@ -46,6 +51,7 @@ attn::Args make_args(int B, int H, int S, int D, float scale, int mask_mode, con
   attn::Args a{};
   a.B = B;
   a.H = H;
+  a.H_kv = H;
   a.S = S;
   a.D = D;
   a.scale = scale;
@@ -78,25 +84,35 @@ const char *attn_status_string(int status) {
     case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case ATTN_ERR_UNIMPLEMENTED: return "not implemented in this build";
     case ATTN_ERR_SCALE: return "scale must be finite and > 0";
+    case ATTN_ERR_HEADS: return "H_kv must divide H (1 <= H_kv <= H)";
     default: return "unknown status";
   }
 }
 
-int attn_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int S, int D,
-             float scale, int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype,
-             void *stream) {
+int attn_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int H_kv, int S,
+                 int D, float scale, int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype,
+                 void *stream) {
   int st = check_common(B, H, S, D, dtype);
   if (st != ATTN_OK) return st;
+  if ((st = check_heads(H, H_kv)) != ATTN_OK) return st;
   if (!q || !k || !v || !o) return ATTN_ERR_NULL;
   if ((st = check_mask(B, H, S, mask_mode, cu_seqlens, n_seqs, max_seqlen)) != ATTN_OK) return st;
   if ((st = check_scale(scale)) != ATTN_OK) return st;
   attn::Args a = make_args(B, H, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
+  a.H_kv = H_kv;
   a.q = q;
   a.k = k;
   a.v = v;
   a.o = o;
   a.lse = lse;
   return to_status(attn::launch_fwd(a));
+}
+
+int attn_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int S, int D,
+             float scale, int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype,
+             void *stream) {
+  return attn_fwd_gqa(q, k, v, o, lse, B, H, H, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype,
+                      stream);
 }
 
 int attn_bwd_preprocess(const float *o, const void *dO, float *delta, int B, int H, int S, int D, int dtype,
@@ -150,15 +166,17 @@ int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dO, con
   return to_status(attn::launch_bwd_dq(a));
 }
 
-int attn_bwd(const void *q, const void *k, const void *v, const float *o, const void *dO, const float *lse,
-             float *dq, float *dk, float *dv, float *delta, int B, int H, int S, int D, float scale, int mask_mode,
-             const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype, void *stream) {
+int attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o, const void *dO, const float *lse,
+                 float *dq, float *dk, float *dv, float *delta, int B, int H, int H_kv, int S, int D, float scale,
+                 int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype, void *stream) {
   int st = check_common(B, H, S, D, dtype);
   if (st != ATTN_OK) return st;
+  if ((st = check_heads(H, H_kv)) != ATTN_OK) return st;
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL;
   if ((st = check_mask(B, H, S, mask_mode, cu_seqlens, n_seqs, max_seqlen)) != ATTN_OK) return st;
   if ((st = check_scale(scale)) != ATTN_OK) return st;
   attn::Args a = make_args(B, H, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
+  a.H_kv = H_kv;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -182,6 +200,13 @@ int attn_bwd(const void *q, const void *k, const void *v, const float *o, const 
     if (e == hipSuccess) e = attn::launch_bwd_dq(a);
   }
   return to_status(e);
+}
+
+int attn_bwd(const void *q, const void *k, const void *v, const float *o, const void *dO, const float *lse,
+             float *dq, float *dk, float *dv, float *delta, int B, int H, int S, int D, float scale, int mask_mode,
+             const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype, void *stream) {
+  return attn_bwd_gqa(q, k, v, o, dO, lse, dq, dk, dv, delta, B, H, H, S, D, scale, mask_mode, cu_seqlens, n_seqs,
+                      max_seqlen, dtype, stream);
 }
 
 }  // extern "C"

@@ -77,7 +77,8 @@ template <typename T, int D, int BMQ, int MINB, bool DOC>
 __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, float *__restrict__ dk,
-    float *__restrict__ dv, int S, float c2, float scale, const int32_t *__restrict__ cu, int ntiles, int n_seqs) {
+    float *__restrict__ dv, int S, float c2, float scale, const int32_t *__restrict__ cu, int ntiles, int n_seqs,
+    int H, int G) {
   constexpr int NW = 4;
   constexpr int NT = NW * kWaveSize;
   constexpr int BN = NW * 32;  // keys per workgroup
@@ -106,30 +107,36 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   const int lane = tid % kWaveSize;
   const int hh = lane / 32;
   const int c = lane % 32;
+  // t.head is a key/value head; its G query heads are qh0 .. qh0 + G - 1, and
+  // dK, dV sum over all of them (the query-tile loop runs over the group).
+  const int Hkv = H / G;
+  const int qh0 = (t.head / Hkv) * H + (t.head % Hkv) * G;
   const size_t base = (size_t)t.head * S * D;
-  const size_t rbase = (size_t)t.head * S;
-  // Queries past the segment read as zeros (Q, dO, LSE, Delta all 0): their
-  // P is 1 but dO and Q are 0, so they add nothing to dV or dK.
-  const GBuf gq(q + base, (uint32_t)(t.seg_end * D * sizeof(T)));
-  const GBuf gdo(dO + base, (uint32_t)(t.seg_end * D * sizeof(T)));
   const GBuf gk(k + base, (uint32_t)(t.r_end * D * sizeof(T)));
   const GBuf gv(v + base, (uint32_t)(t.r_end * D * sizeof(T)));
-  const GBuf glse(lse + rbase, (uint32_t)(t.seg_end * sizeof(float)));
-  const GBuf gdel(delta + rbase, (uint32_t)(t.seg_end * sizeof(float)));
 
   const int w0 = t.r_start + wave * 32;  // first key of this wave
   const bool wave_active = w0 < t.r_end;
   const int wave_last = min(w0 + 32, t.r_end) - 1;
   const int key = w0 + c;
   const int q_lo = t.r_start;  // the first query that sees any of these keys
-  const int ntile = (t.seg_end - q_lo + BMQ - 1) / BMQ;
+  const int ntq = (t.seg_end - q_lo + BMQ - 1) / BMQ;  // query tiles per query head
+  const int ntile = G * ntq;                            // over the whole group
 
   auto qslot = [&]<int P>() { return lds_cast(P == 0 ? sQ0 : sQ1); };
   auto oslot = [&]<int P>() { return lds_cast(P == 0 ? sO0 : sO1); };
   auto lslot = [&]<int P>() { return lds_cast(P == 0 ? sL0 : sL1); };
   auto dslot = [&]<int P>() { return lds_cast(P == 0 ? sD0 : sD1); };
   auto issue = [&]<int P>(int it) {
-    const int q0 = q_lo + it * BMQ;
+    const int g = it / ntq;
+    const int q0 = q_lo + (it - g * ntq) * BMQ;
+    const size_t rbase = (size_t)(qh0 + g) * S;
+    // Queries past the segment read as zeros (Q, dO, LSE, Delta all 0): their
+    // P is 1 but dO and Q are 0, so they add nothing to dV or dK.
+    const GBuf gq(q + rbase * D, (uint32_t)(t.seg_end * D * sizeof(T)));
+    const GBuf gdo(dO + rbase * D, (uint32_t)(t.seg_end * D * sizeof(T)));
+    const GBuf glse(lse + rbase, (uint32_t)(t.seg_end * sizeof(float)));
+    const GBuf gdel(delta + rbase, (uint32_t)(t.seg_end * sizeof(float)));
     QTile::issue(gq, qslot.template operator()<P>(), q0, wave, lane);
     QTile::issue(gdo, oslot.template operator()<P>(), q0, wave, lane);
     if (wave == 0) dma_vec64(glse, lslot.template operator()<P>(), q0, lane);
@@ -215,7 +222,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     wait_vmcnt<0>();
     wg_barrier();
     if (it + 1 < ntile) issue.template operator()<1 - P>(it + 1);
-    const int q0 = q_lo + it * BMQ;
+    const int q0 = q_lo + (it % ntq) * BMQ;
     if (!wave_active || q0 + BMQ - 1 < w0) return;  // every query precedes every key here
     if (q0 < wave_last)
       tile.template operator()<P, true>(q0);
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, const float *__restrict__ o,
     float *__restrict__ delta_out, float *__restrict__ dq, int S, float c2, float scale,
-    const int32_t *__restrict__ cu, int ntiles, int n_seqs) {
+    const int32_t *__restrict__ cu, int ntiles, int n_seqs, int H, int G) {
   constexpr int NW = 4;
   constexpr int NT = NW * kWaveSize;
   constexpr int BM = NW * 32;
@@ -294,12 +301,13 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
   const int lane = tid % kWaveSize;
   const int hh = lane / 32;
   const int c = lane % 32;
-  const size_t base = (size_t)t.head * S * D;
+  const size_t base = (size_t)t.head * S * D;                      // this query head
+  const size_t kvbase = (size_t)kv_head_of(t.head, H, G) * S * D;  // its key/value head
   const size_t rbase = (size_t)t.head * S;
   const GBuf gq(q + base, (uint32_t)(t.r_end * D * sizeof(T)));
   const GBuf gdo(dO + base, (uint32_t)(t.r_end * D * sizeof(T)));
-  const GBuf gk(k + base, (uint32_t)(t.seg_end * D * sizeof(T)));
-  const GBuf gv(v + base, (uint32_t)(t.seg_end * D * sizeof(T)));
+  const GBuf gk(k + kvbase, (uint32_t)(t.seg_end * D * sizeof(T)));
+  const GBuf gv(v + kvbase, (uint32_t)(t.seg_end * D * sizeof(T)));
   const GBuf glse(lse + rbase, (uint32_t)(t.r_end * sizeof(float)));
   const GBuf gdel(delta + rbase, (uint32_t)(t.r_end * sizeof(float)));
 
@@ -468,15 +476,15 @@ static hipError_t launch_dkdv_t(const Args &a) {
   int ntiles;
   if (DOC) {
     ntiles = (a.max_seqlen + BN - 1) / BN;
-    grid = dim3(ntiles * a.n_seqs * a.H);
+    grid = dim3(ntiles * a.n_seqs * a.H_kv);
   } else {
     ntiles = (a.S + BN - 1) / BN;
-    grid = dim3(ntiles * a.B * a.H);
+    grid = dim3(ntiles * a.B * a.H_kv);
   }
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, BMQ, MINB, DOC>), grid, dim3(256), 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
                      static_cast<const T *>(a.dO), a.lse_in, a.delta_in, a.dk, a.dv, a.S, c2, a.scale,
-                     a.cu_seqlens, ntiles, a.n_seqs);
+                     a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv);
   return hipGetLastError();
 }
 
@@ -498,7 +506,7 @@ static hipError_t launch_dq_t(const Args &a) {
   hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, MINB, DOC, FUSE_DELTA>), grid, dim3(256), 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
                      static_cast<const T *>(a.dO), a.lse_in, a.delta_in, a.o_in, a.delta, a.dq, a.S, c2, a.scale,
-                     a.cu_seqlens, ntiles, a.n_seqs);
+                     a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv);
   return hipGetLastError();
 }
 

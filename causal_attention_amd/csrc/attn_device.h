@@ -534,6 +534,11 @@ struct RowTile {
   bool valid;
 };
 
+// Grouped-query attention: H query heads share H / G key/value heads, query
+// head h reading K/V head h / G of its batch entry.  Global head indices run
+// b * H + h (queries) and b * (H / G) + h / G (keys and values).
+__device__ __forceinline__ int kv_head_of(int qhead, int H, int G) { return (qhead / H) * (H / G) + (qhead % H) / G; }
+
 // Tile schedule.  Workgroups are dealt to the 8 XCDs round-robin (block b
 // runs on XCD b % 8) and, within an XCD, to its 32 CUs round-robin (local
 // index l = b / 8 on CU l % 32), as measured on MI355X; when every workgroup

@@ -38,7 +38,7 @@ template <typename T, int D, int NW, int BN, int MINB, bool DOC>
 __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                                  const T *__restrict__ v, float *__restrict__ o,
                                                                  float *__restrict__ lse, int S, float c2,
-                                                                 const int32_t *__restrict__ cu, int ntiles, int n_seqs) {
+                                                                 const int32_t *__restrict__ cu, int ntiles, int n_seqs, int H, int G) {
   constexpr int NT = NW * kWaveSize;
   constexpr int BM = NW * 32;  // query rows per workgroup
   constexpr int KB = D / 16;   // k-blocks over the head dimension
@@ -67,10 +67,11 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
   const int lane = tid % kWaveSize;
   const int hh = lane / 32;
   const int c = lane % 32;
-  const size_t base = (size_t)t.head * S * D;
+  const size_t base = (size_t)t.head * S * D;                      // this query head
+  const size_t kvbase = (size_t)kv_head_of(t.head, H, G) * S * D;  // its key/value head
   const GBuf gq(q + base, (uint32_t)(t.r_end * D * sizeof(T)));
-  const GBuf gk(k + base, (uint32_t)(t.seg_end * D * sizeof(T)));
-  const GBuf gv(v + base, (uint32_t)(t.seg_end * D * sizeof(T)));
+  const GBuf gk(k + kvbase, (uint32_t)(t.seg_end * D * sizeof(T)));
+  const GBuf gv(v + kvbase, (uint32_t)(t.seg_end * D * sizeof(T)));
 
   const int w0 = t.r_start + wave * 32;  // first query of this wave
   const bool wave_active = w0 < t.r_end;
@@ -258,7 +259,7 @@ static hipError_t launch_fwd_t(const Args &a) {
   }
   hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW, BN, MINB, DOC>), grid, block, 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
-                     a.o, a.lse, a.S, c2, a.cu_seqlens, ntiles, a.n_seqs);
+                     a.o, a.lse, a.S, c2, a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv);
   return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@ struct Args {
   const float *o_in, *lse_in, *delta_in;
   float *o, *lse, *dq, *dk, *dv, *delta;
   int B, H, S, D;
+  int H_kv;                 // key/value heads (H for plain multi-head attention)
   float scale;
   bool doc;                 // packed-document mask
   const int32_t *cu_seqlens;

@@ -70,7 +70,8 @@ typedef enum attn_status {
                                   outside 1..S, or ceil(max_seqlen/128)*n_seqs*H >= 2^31 */
   ATTN_ERR_HIP = -7,           /* a HIP runtime call or kernel launch failed       */
   ATTN_ERR_UNIMPLEMENTED = -8, /* valid request this build does not implement      */
-  ATTN_ERR_SCALE = -9          /* scale not finite or not > 0                      */
+  ATTN_ERR_SCALE = -9,         /* scale not finite or not > 0                      */
+  ATTN_ERR_HEADS = -10         /* H_kv not a divisor of H (grouped-query calls)    */
 } attn_status;
 
 enum { ATTN_MASK_CAUSAL = 0, ATTN_MASK_DOC_CAUSAL = 1 };
@@ -93,8 +94,9 @@ int attn_fwd(const void *q, const void *k, const void *v, float *o, float *lse,
  * Backward.  Reads q, k, v, dO (dtype), o and lse (float32, from attn_fwd
  * with the same arguments) and writes dq, dk, dv [B,H,S,D] float32.
  * delta: caller-owned float32 workspace of B*H*S elements; on return it holds
- * Delta_i = sum_d dO_id O_id.  Runs the three stages below in order on
- * `stream`.
+ * Delta_i = sum_d dO_id O_id.  The results are bit for bit those of the three
+ * stages below run in order; with bf16 inputs the dQ stage computes Delta
+ * itself and runs first, then dK/dV (one pass over O and dO fewer).
  */
 int attn_bwd(const void *q, const void *k, const void *v, const float *o,
              const void *dO, const float *lse, float *dq, float *dk, float *dv,
@@ -128,6 +130,28 @@ int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dO,
                 int B, int H, int S, int D, float scale, int mask_mode,
                 const int32_t *cu_seqlens, int n_seqs, int max_seqlen,
                 int dtype, void *stream);
+
+/*
+ * Grouped-query attention (Forge, "Architecture": attention with GQA behind
+ * an interface).  H query heads share H_kv key/value heads (H_kv divides H;
+ * H_kv = H is plain multi-head attention, H_kv = 1 multi-query): query head h
+ * of batch entry b attends with key/value head h / (H / H_kv) of that entry.
+ * k, v, dk, dv are [B, H_kv, S, D]; q, o, dO, dq are [B, H, S, D]; lse and
+ * delta [B, H, S].  dK and dV of a key/value head sum the contributions of
+ * all its query heads, in a fixed order (no atomics: results are bitwise
+ * reproducible).  Other arguments and rules as attn_fwd / attn_bwd, which are
+ * these calls with H_kv = H.  Returns ATTN_ERR_HEADS if H_kv does not divide H.
+ */
+int attn_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse,
+                 int B, int H, int H_kv, int S, int D, float scale, int mask_mode,
+                 const int32_t *cu_seqlens, int n_seqs, int max_seqlen,
+                 int dtype, void *stream);
+
+int attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o,
+                 const void *dO, const float *lse, float *dq, float *dk, float *dv,
+                 float *delta, int B, int H, int H_kv, int S, int D, float scale,
+                 int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen,
+                 int dtype, void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *attn_status_string(int status);

@@ -46,7 +46,9 @@ def run_hip(x, dev=None, poison=True, stream=None):
     B, H, S, D = x["B"], x["H"], x["S"], x["D"]
     fill = float("nan") if poison else 0.0
     f32 = dict(dtype=torch.float32, device="cuda")
-    out = {n: torch.full((B, H, S, D), fill, **f32) for n in ("o", "dq", "dk", "dv")}
+    out = {n: torch.full((B, H, S, D), fill, **f32) for n in ("o", "dq")}
+    for n in ("dk", "dv"):  # K/V may have fewer heads (grouped-query attention)
+        out[n] = torch.full(tuple(x["k"].shape), fill, **f32)
     out["lse"] = torch.full((B, H, S), fill, **f32)
     out["delta"] = torch.full((B, H, S), fill, **f32)
     mode = x["mask_mode"]

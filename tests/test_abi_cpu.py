@@ -31,7 +31,7 @@ def test_header_status_codes_match_binding():
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 100
+    assert lib.attn_abi_version() == 110
 
 
 def test_status_strings(lib):
@@ -101,12 +101,45 @@ def test_stage_entry_points_reject_invalid_arguments(lib):
                            None, 0, 0, 1, None) == -9
 
 
+def _fwd_gqa(lib, H_kv, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=4, S=64, D=64, scale=0.125, mask=0,
+             cu=None, n=0, mx=0, dtype=1, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], H_kv, a["S"], a["D"],
+                            a["scale"], a["mask"], a["cu"], a["n"], a["mx"], a["dtype"], a["stream"])
+
+
+def _bwd_gqa(lib, H_kv, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, delta=FAKE,
+             B=1, H=4, S=64, D=64, scale=0.125, mask=0, cu=None, n=0, mx=0, dtype=1, stream=None)
+    a.update(kw)
+    return lib.attn_bwd_gqa(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                            a["delta"], a["B"], a["H"], H_kv, a["S"], a["D"], a["scale"], a["mask"], a["cu"],
+                            a["n"], a["mx"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("H,H_kv", [(4, 0), (4, 3), (4, 5), (4, -1), (6, 4)])
+def test_gqa_rejects_head_counts_that_do_not_divide(lib, H, H_kv):
+    assert _fwd_gqa(lib, H_kv, H=H) == -10
+    assert _bwd_gqa(lib, H_kv, H=H) == -10
+
+
+def test_gqa_checks_the_rest_as_the_plain_calls(lib):
+    assert _fwd_gqa(lib, 2, q=None) == -1
+    assert _fwd_gqa(lib, 2, D=40) == -3
+    assert _bwd_gqa(lib, 2, dk=None) == -1
+    assert _bwd_gqa(lib, 1, mask=1, cu=FAKE, n=1, mx=64, B=2) == -6
+    assert _bwd_gqa(lib, 2, scale=0.0) == -9
+
+
 def test_no_device_reports_hip_error(lib):
     """A valid call with no GPU present fails with ATTN_ERR_HIP instead of aborting."""
     torch = pytest.importorskip("torch")
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert _fwd(lib) == -7
+    assert _fwd_gqa(lib, 2) == -7
+    assert _bwd_gqa(lib, 1) == -7
 
 
 def test_binding_refuses_host_tensors():

@@ -71,3 +71,14 @@ def test_packed_config_draw():
     cu = x["cu_seqlens"]
     assert x["q"].shape == (1, 16, 8192, 64)
     assert cu[-1] == 8192 and len(cu) >= 9
+
+
+def test_grouped_query_config_draws_fewer_kv_heads():
+    cfg = CONFIGS["lm237m_ctx1024_gqa4"]
+    small = make_inputs(cfg, 6, shape=(1, 4, 8, 64))  # an explicit shape keeps K/V at H heads
+    assert small["k"].shape == (1, 4, 8, 64)
+    from dataclasses import replace
+    tiny = replace(cfg, B=1, S=8)
+    x = make_inputs(tiny, 6)
+    assert x["q"].shape == (1, 16, 8, 64) and x["do"].shape == (1, 16, 8, 64)
+    assert x["k"].shape == (1, 4, 8, 64) and x["v"].shape == (1, 4, 8, 64)

@@ -12,7 +12,8 @@ Recipe (stated once so that every consumer draws the same numbers):
 
 * generator ``numpy.random.default_rng(seed)`` (PCG64);
 * draw ``standard_normal`` float64 arrays in the order Q, K, V, dO, each a full
-  C-order [B, H, S, D] array;
+  C-order [B, H, S, D] array (K and V [B, H_kv, S, D] for grouped-query
+  workloads);
 * multiply Q, K, V (not dO) by ``qkv_scale``;
 * round to the input dtype (bf16: round-to-nearest-even from float32; fp32:
   round-to-nearest from float64);
@@ -44,6 +45,7 @@ class AttnConfig:
     mask_mode: int = MASK_CAUSAL
     doc_len_range: tuple | None = None  # (lo, hi) inclusive, packed mode only
     doc_seed: int = 500
+    H_kv: int | None = None  # key/value heads (grouped-query attention); None = H
     note: str = field(default="", compare=False)
 
     @property
@@ -70,6 +72,10 @@ CONFIGS = {
     "packed_docs8192": AttnConfig("packed_docs8192", B=1, H=16, S=8192, D=64, dtype="bf16",
                                   mask_mode=MASK_DOC_CAUSAL, doc_len_range=(32, 1024),
                                   note="packed short documents, block-diagonal causal"),
+    # Grouped-query attention (Forge, "Architecture": attention with GQA): the
+    # context-1024 shape with 4 key/value heads for the 16 query heads.
+    "lm237m_ctx1024_gqa4": AttnConfig("lm237m_ctx1024_gqa4", B=8, H=16, S=1024, D=64, dtype="bf16", H_kv=4,
+                                      note="237M-class layer with grouped-query attention"),
 }
 
 
@@ -125,10 +131,11 @@ def make_inputs(cfg: AttnConfig, seed: int, shape=None):
     values in the input dtype.
     """
     B, H, S, D = shape if shape is not None else (cfg.B, cfg.H, cfg.S, cfg.D)
+    H_kv = cfg.H_kv if (cfg.H_kv is not None and shape is None) else H
     rng = np.random.default_rng(seed)
     out = {}
     for name in ("q", "k", "v", "do"):
-        x = rng.standard_normal((B, H, S, D))
+        x = rng.standard_normal((B, H_kv if name in ("k", "v") else H, S, D))
         if name != "do":
             x = x * cfg.qkv_scale
         if cfg.dtype == "bf16":
