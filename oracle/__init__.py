@@ -16,6 +16,7 @@ from .attention import (  # noqa: F401
     allowed_mask,
     attention_fwd_ref,
     attention_bwd_ref,
+    attention_decode_ref,
     attention_fwd_rows_ref,
     attention_dq_rows_ref,
     attention_dkdv_rows_ref,

@@ -247,3 +247,37 @@ def attention_dkdv_rows_ref(q, k, v, do, scale, b, h, cols, mask_mode=MASK_CAUSA
                 dv[c] += p[j] * doh[i]
                 dk[c] += scale * p[j] * (dp[j] - delta) * qh[i]
     return dk, dv
+
+
+def attention_decode_ref(q, k_cache, v_cache, cache_lens, scale):
+    """Decode step with a key/value cache: one new query per (batch entry b, head h)
+    attending keys 0 .. cache_lens[b] - 1 of its K/V head (the query is the newest
+    token, its own key already in the cache, so causality admits every cached key).
+
+    q: [B, H, D]; k_cache, v_cache: [B, H_kv, S_max, D] (H_kv divides H; query head
+    h reads K/V head h // (H / H_kv)); cache_lens: B integers in 1 .. S_max.
+    Returns (O [B, H, D], LSE [B, H]) in float64: the plain softmax over the
+    cached keys' scaled scores, its weighted sum of values, and its natural-log
+    normaliser.
+    """
+    q, k_cache, v_cache = _as64(q), _as64(k_cache), _as64(v_cache)
+    B, H, D = q.shape
+    H_kv = k_cache.shape[1]
+    if H % H_kv != 0:
+        raise ValueError("K/V heads must divide the query heads")
+    G = H // H_kv
+    o = np.zeros((B, H, D))
+    lse = np.zeros((B, H))
+    for b in range(B):
+        n = int(cache_lens[b])
+        if not 1 <= n <= k_cache.shape[2]:
+            raise ValueError("cache length out of range")
+        for h in range(H):
+            kh, vh = k_cache[b, h // G, :n], v_cache[b, h // G, :n]
+            s = scale * (kh @ q[b, h])
+            m = s.max()
+            e = np.exp(s - m)
+            l = e.sum()
+            o[b, h] = (e / l) @ vh
+            lse[b, h] = m + np.log(l)
+    return o, lse

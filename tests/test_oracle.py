@@ -426,3 +426,57 @@ def test_gqa_rejects_heads_that_do_not_divide():
     q, k, v, do = _gqa_inputs(1, 4, 2, 8, 4, 33)
     with pytest.raises(ValueError):
         attention_bwd_ref(q, k, v, do, 0.5, heads=[(0, 1)])
+
+
+# ---------------------------------------------------------------- decode with a K/V cache
+
+def test_decode_equals_last_row_of_causal_attention():
+    """The decode step for a query at position n-1 is row n-1 of causal attention over
+    the first n tokens (per head, with grouped K/V heads repeated)."""
+    from oracle import attention_decode_ref
+    rng = np.random.default_rng(40)
+    B, H, H_kv, S_max, D = 3, 4, 2, 24, 8
+    G = H // H_kv
+    k = rng.standard_normal((B, H_kv, S_max, D))
+    v = rng.standard_normal((B, H_kv, S_max, D))
+    q_seq = rng.standard_normal((B, H, S_max, D))
+    lens = [24, 1, 13]
+    q = np.stack([q_seq[b, :, lens[b] - 1] for b in range(B)])
+    o, lse = attention_decode_ref(q, k, v, lens, 0.4)
+    for b, n in enumerate(lens):
+        kr = np.repeat(k[b:b + 1, :, :n], G, axis=1)
+        vr = np.repeat(v[b:b + 1, :, :n], G, axis=1)
+        fo, flse = attention_fwd_ref(q_seq[b:b + 1, :, :n], kr, vr, 0.4)
+        np.testing.assert_allclose(o[b], fo[0, :, n - 1], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse[b], flse[0, :, n - 1], rtol=1e-13, atol=1e-14)
+
+
+def test_decode_matches_torch_sdpa():
+    """One query attending every cached key: PyTorch's CPU SDPA (no mask) in float64."""
+    torch = pytest.importorskip("torch")
+    from oracle import attention_decode_ref
+    rng = np.random.default_rng(41)
+    B, H, H_kv, S_max, D = 2, 8, 2, 40, 16
+    q = rng.standard_normal((B, H, D))
+    k = rng.standard_normal((B, H_kv, S_max, D))
+    v = rng.standard_normal((B, H_kv, S_max, D))
+    lens = [40, 17]
+    o, _ = attention_decode_ref(q, k, v, lens, 0.25)
+    for b, n in enumerate(lens):
+        to = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(q[b][None, :, None]), torch.tensor(k[b][None, :, :n]), torch.tensor(v[b][None, :, :n]),
+            scale=0.25, enable_gqa=True)
+        np.testing.assert_allclose(o[b], to.numpy()[0, :, 0], rtol=1e-12, atol=1e-13)
+
+
+def test_decode_single_key_and_constant_values():
+    from oracle import attention_decode_ref
+    rng = np.random.default_rng(42)
+    q = rng.standard_normal((1, 2, 8))
+    k = rng.standard_normal((1, 2, 5, 8))
+    v = rng.standard_normal((1, 2, 5, 8))
+    o, lse = attention_decode_ref(q, k, v, [1], 0.5)       # one key: O = V_0, LSE = scale q.k_0
+    np.testing.assert_allclose(o[0], v[0, :, 0], rtol=1e-15)
+    np.testing.assert_allclose(lse[0], 0.5 * np.einsum("hd,hd->h", q[0], k[0, :, 0]), rtol=1e-14)
+    o, _ = attention_decode_ref(q, k, np.ones_like(v), [5], 0.5)  # V = 1 -> O = 1
+    np.testing.assert_allclose(o, 1.0, rtol=1e-14)
