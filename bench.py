@@ -11,7 +11,9 @@ accounting), divided by the measured time.  One JSON line is printed.
 
 Besides the headline workload the line carries:
   by_workload   the same measurement at the other full-size workloads
-                (context 512, 8192 and packed documents), fewer steps;
+                (context 512, 8192, packed documents, grouped-query heads),
+                fewer steps, and one decode step against a full 8192-token
+                K/V cache (time, GB/s against HBM peak);
   kernels       per-kernel mean duration from HIP events on the launch stream;
   roofline      the dominant kernel against its roofline;
   cpu_baseline  the fp64 oracle timed on this host's cores on a bounded sample.
@@ -313,6 +315,47 @@ def cpu_baseline(w, seconds):
             "sample": f"fwd+bwd of {done} heads (of {len(heads)}, cycled) of B{B} H{H} S{S} D{D}, {dt:.1f} s"}
 
 
+def measure_decode(name, reps):
+    """One decode step (attn_decode) on the cache workload: mean time from HIP events
+    over `reps` back-to-back calls, and the cache-read rate against HBM peak.
+    Algorithmic bytes: K and V rows read (sum of lengths x H_kv x D x 2 tensors),
+    q, and the fp32 outputs O and LSE; the chunk partials are not counted."""
+    import torch
+    import causal_attention_amd as ca
+    from workload import DECODE_CONFIGS, make_decode_inputs
+    cfg = DECODE_CONFIGS[name]
+    x = make_decode_inputs(cfg, 7)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x[n]).cuda().to(dt) for n in ("q", "k", "v"))
+    lens = torch.from_numpy(x["lens"]).cuda()
+    o = torch.empty((cfg.B, cfg.H, cfg.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((cfg.B, cfg.H), dtype=torch.float32, device="cuda")
+    nbytes = ca.decode_workspace_bytes(cfg.B, cfg.H, cfg.H_kv, cfg.D, int(x["lens"].max()))
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        ca.attn_decode(q, k, v, lens, o, lse, ws, x["scale"], int(x["lens"].max()), stream)
+
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    esz = 2 if cfg.dtype == "bf16" else 4
+    kv_bytes = int(x["lens"].sum()) * cfg.H_kv * cfg.D * 2 * esz
+    alg = kv_bytes + cfg.B * cfg.H * cfg.D * esz + cfg.B * cfg.H * (cfg.D + 1) * 4
+    gbs = alg / t / 1e9
+    return {"us_per_step": t * 1e6, "achieved_GBs": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS,
+            "bytes_per_step": alg, "config": {"B": cfg.B, "H": cfg.H, "H_kv": cfg.H_kv, "cache": cfg.length,
+                                               "D": cfg.D, "dtype": cfg.dtype}}
+
+
 def measure(name, steps, warmup, reps):
     w = Workload(name)
     sec = w.timed_steps(steps, warmup)
@@ -363,6 +406,10 @@ def main():
             by_workload[name] = s
             log(f"[bench] {name}: {s['tflops']:.1f} TFLOPS ({s['pct_peak']:.1f}% of peak), "
                 f"kernels {s['kernels_ms']}")
+        d = measure_decode("decode_ctx8192", max(20, a.kernel_reps))
+        by_workload["decode_ctx8192"] = d
+        log(f"[bench] decode_ctx8192: {d['us_per_step']:.1f} us/step, {d['achieved_GBs']:.0f} GB/s "
+            f"({100 * d['frac_hbm_peak']:.1f}% of HBM peak)")
     rl = roofline(w, times)
     log(f"[bench] roofline: {rl}")
     cpu = None

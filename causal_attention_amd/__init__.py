@@ -16,8 +16,11 @@ from ._binding import (  # noqa: F401
     attn_bwd_dkdv,
     attn_bwd_dq,
     attn_bwd_preprocess,
+    attn_decode,
     attn_fwd,
     backward,
+    decode,
+    decode_workspace_bytes,
     forward,
     header_functions,
     load_library,

@@ -25,7 +25,7 @@ ATTN_DTYPE_BF16 = 1
 STATUS_NAMES = {
     0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEAD_DIM",
     -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_MASK", -6: "ATTN_ERR_SEQLENS", -7: "ATTN_ERR_HIP",
-    -8: "ATTN_ERR_UNIMPLEMENTED", -9: "ATTN_ERR_SCALE", -10: "ATTN_ERR_HEADS",
+    -8: "ATTN_ERR_UNIMPLEMENTED", -9: "ATTN_ERR_SCALE", -10: "ATTN_ERR_HEADS", -11: "ATTN_ERR_WORKSPACE",
 }
 
 
@@ -48,6 +48,8 @@ SIGNATURES = {
     "attn_bwd_dq": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
     "attn_fwd_gqa": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
     "attn_bwd_gqa": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
+    "attn_decode_workspace_bytes": [_I, _I, _I, _I, _I],
+    "attn_decode": [_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _I, _F, _I, _I, _P],
     "attn_status_string": [_I],
     "attn_abi_version": [],
 }
@@ -60,7 +62,7 @@ def header_functions(path: str = HEADER_PATH):
     with open(path) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?(?:int|char|void)\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)
+    return re.findall(r"^\s*(?:const\s+)?(?:int|char|void|size_t)\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -76,7 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name, args in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.argtypes = args
-        fn.restype = ctypes.c_char_p if name == "attn_status_string" else ctypes.c_int
+        fn.restype = {"attn_status_string": ctypes.c_char_p,
+                      "attn_decode_workspace_bytes": ctypes.c_size_t}.get(name, ctypes.c_int)
     _lib = lib
     return lib
 
@@ -242,8 +245,50 @@ def attn_bwd_dq(q, k, v, dO, lse, delta, dq, scale, mask_mode=ATTN_MASK_CAUSAL, 
         B, H, S, D, float(scale), int(mask_mode), cu, ns, ms, dt, _stream(stream)))
 
 
+def decode_workspace_bytes(B, H, H_kv, D, max_len):
+    return int(load_library().attn_decode_workspace_bytes(int(B), int(H), int(H_kv), int(D), int(max_len)))
+
+
+def attn_decode(q, k_cache, v_cache, cache_lens, o, lse, workspace, scale, max_len, stream=None):
+    """Enqueue one decode step: q [B,H,D] against the first cache_lens[b] rows of
+    k_cache, v_cache [B,H_kv,S_max,D]; o [B,H,D] and lse [B,H] (or None) fp32;
+    workspace: a device tensor of at least decode_workspace_bytes(...) bytes (or
+    None when that is 0)."""
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, H, D] and the caches [B, H_kv, S_max, D]")
+    B, H, D = q.shape
+    _, H_kv, S_max, _ = k_cache.shape
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if tuple(t.shape) != (B, H_kv, S_max, D) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be [B, H_kv, S_max, D] with q's dtype")
+    dev = q.device
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _ptr(workspace, "workspace", device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.attn_decode(
+        _ptr(q, "q", device=dev), _ptr(k_cache, "k_cache", device=dev), _ptr(v_cache, "v_cache", device=dev),
+        _ptr(cache_lens, "cache_lens", (B,), torch.int32, dev), _ptr(o, "o", (B, H, D), torch.float32, dev),
+        _ptr(lse, "lse", (B, H), torch.float32, dev), ws_ptr, ws_bytes,
+        B, H, H_kv, S_max, D, float(scale), int(max_len), _dtype_code(q), _stream(stream)))
+
+
 # ---------------------------------------------------------------------------
 # Allocating conveniences (torch supplies the device memory).
+
+def decode(q, k_cache, v_cache, cache_lens, scale, max_len, stream=None):
+    """Returns (o, lse) of one decode step as new fp32 device tensors."""
+    torch = _torch()
+    B, H, D = q.shape
+    H_kv = k_cache.shape[1]
+    o = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    n = decode_workspace_bytes(B, H, H_kv, D, max_len)
+    ws = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+    attn_decode(q, k_cache, v_cache, cache_lens, o, lse, ws, scale, max_len, stream)
+    return o, lse
 
 def forward(q, k, v, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None, max_seqlen=None, stream=None):
     """Returns (o, lse) as new fp32 device tensors."""

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 110;  // 1.10: grouped-query entry points
+constexpr int kAbiVersion = 120;  // 1.20: grouped-query and decode entry points
 
 int check_common(int B, int H, int S, int D, int dtype) {
   if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
@@ -85,6 +85,7 @@ const char *attn_status_string(int status) {
     case ATTN_ERR_UNIMPLEMENTED: return "not implemented in this build";
     case ATTN_ERR_SCALE: return "scale must be finite and > 0";
     case ATTN_ERR_HEADS: return "H_kv must divide H (1 <= H_kv <= H)";
+    case ATTN_ERR_WORKSPACE: return "workspace NULL or smaller than attn_decode_workspace_bytes()";
     default: return "unknown status";
   }
 }
@@ -207,6 +208,45 @@ int attn_bwd(const void *q, const void *k, const void *v, const float *o, const 
              const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype, void *stream) {
   return attn_bwd_gqa(q, k, v, o, dO, lse, dq, dk, dv, delta, B, H, H, S, D, scale, mask_mode, cu_seqlens, n_seqs,
                       max_seqlen, dtype, stream);
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int D, int max_len) {
+  if (B < 1 || H < 1 || H_kv < 1 || max_len < 1) return 0;
+  return attn::decode_workspace_bytes(B, H, H_kv, D, max_len);
+}
+
+int attn_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *cache_lens, float *o,
+                float *lse, void *workspace, size_t workspace_bytes, int B, int H, int H_kv, int S_max, int D,
+                float scale, int max_len, int dtype, void *stream) {
+  int st = check_common(B, H, S_max, D, dtype);
+  if (st != ATTN_OK) return st;
+  if ((st = check_heads(H, H_kv)) != ATTN_OK) return st;
+  if (H / H_kv > 32) return ATTN_ERR_UNIMPLEMENTED;  // one wave holds a group's queries
+  if ((int64_t)B * H_kv * S_max * D >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+  if (max_len < 1 || max_len > S_max) return ATTN_ERR_SHAPE;
+  if (!q || !k_cache || !v_cache || !cache_lens || !o) return ATTN_ERR_NULL;
+  if ((st = check_scale(scale)) != ATTN_OK) return st;
+  const size_t need = attn::decode_workspace_bytes(B, H, H_kv, D, max_len);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  attn::DecodeArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cache_lens = cache_lens;
+  a.o = o;
+  a.lse = lse;
+  a.o_part = static_cast<float *>(workspace);
+  a.lse_part = need > 0 ? static_cast<float *>(workspace) + (need / sizeof(float)) / (D + 1) * D : nullptr;
+  a.B = B;
+  a.H = H;
+  a.H_kv = H_kv;
+  a.S_max = S_max;
+  a.D = D;
+  a.max_len = max_len;
+  a.scale = scale;
+  a.bf16 = dtype == ATTN_DTYPE_BF16;
+  a.stream = static_cast<hipStream_t>(stream);
+  return to_status(attn::launch_decode(a));
 }
 
 }  // extern "C"

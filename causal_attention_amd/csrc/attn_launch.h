@@ -21,6 +21,20 @@ struct Args {
   hipStream_t stream;
 };
 
+// Decode step against a key/value cache (attn_decode).
+struct DecodeArgs {
+  const void *q, *k_cache, *v_cache;
+  const int32_t *cache_lens;
+  float *o, *lse;
+  float *o_part, *lse_part;  // chunk partials (workspace), unused with one chunk
+  int B, H, H_kv, S_max, D, max_len;
+  float scale;
+  bool bf16;
+  hipStream_t stream;
+};
+hipError_t launch_decode(const DecodeArgs &a);
+size_t decode_workspace_bytes(int B, int H, int H_kv, int D, int max_len);
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const Args &a);
 hipError_t launch_bwd_preprocess(const Args &a);

@@ -53,6 +53,7 @@
 #ifndef CAUSAL_ATTN_API_H
 #define CAUSAL_ATTN_API_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -71,7 +72,8 @@ typedef enum attn_status {
   ATTN_ERR_HIP = -7,           /* a HIP runtime call or kernel launch failed       */
   ATTN_ERR_UNIMPLEMENTED = -8, /* valid request this build does not implement      */
   ATTN_ERR_SCALE = -9,         /* scale not finite or not > 0                      */
-  ATTN_ERR_HEADS = -10         /* H_kv not a divisor of H (grouped-query calls)    */
+  ATTN_ERR_HEADS = -10,        /* H_kv not a divisor of H (grouped-query calls)    */
+  ATTN_ERR_WORKSPACE = -11     /* decode workspace missing or too small            */
 } attn_status;
 
 enum { ATTN_MASK_CAUSAL = 0, ATTN_MASK_DOC_CAUSAL = 1 };
@@ -152,6 +154,35 @@ int attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o,
                  float *delta, int B, int H, int H_kv, int S, int D, float scale,
                  int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen,
                  int dtype, void *stream);
+
+/*
+ * Decode step against a key/value cache (Forge, "Roadmap": KV cache for
+ * generation).  For each batch entry b and query head h, one new query -- the
+ * newest token, whose own key and value are already appended to the cache --
+ * attends keys 0 .. cache_lens[b] - 1 of its key/value head h / (H / H_kv):
+ *
+ *   O[b,h] = softmax_j(scale * q[b,h] . k_cache[b,kv,j]) v_cache[b,kv,:],
+ *   LSE[b,h] = ln sum_j exp(scale * q[b,h] . k_cache[b,kv,j]).
+ *
+ * q: [B, H, D] (dtype); k_cache, v_cache: [B, H_kv, S_max, D] (dtype; only the
+ * first cache_lens[b] rows of batch entry b are read); cache_lens: DEVICE
+ * int32 [B], each in 1 .. max_len; max_len: host int, the largest length
+ * (sizes the launch), 1 <= max_len <= S_max.  o: [B, H, D] float32; lse:
+ * [B, H] float32 or NULL.  H / H_kv <= 32.
+ * workspace: caller-owned device memory of attn_decode_workspace_bytes(B, H,
+ * H_kv, D, max_len) bytes (the keys are split into chunks whose partial results
+ * are merged exactly; 0 bytes, and workspace may be NULL, when one chunk
+ * suffices).  Contents on return are unspecified.  Errors as for attn_fwd;
+ * ATTN_ERR_WORKSPACE if the workspace is missing or too small,
+ * ATTN_ERR_UNIMPLEMENTED if H / H_kv > 32.  cache_lens is not validated.
+ */
+size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int D, int max_len);
+
+int attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                const int32_t *cache_lens, float *o, float *lse,
+                void *workspace, size_t workspace_bytes,
+                int B, int H, int H_kv, int S_max, int D, float scale, int max_len,
+                int dtype, void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *attn_status_string(int status);

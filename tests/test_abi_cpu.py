@@ -31,7 +31,7 @@ def test_header_status_codes_match_binding():
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 110
+    assert lib.attn_abi_version() == 120
 
 
 def test_status_strings(lib):
@@ -132,12 +132,43 @@ def test_gqa_checks_the_rest_as_the_plain_calls(lib):
     assert _bwd_gqa(lib, 2, scale=0.0) == -9
 
 
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, o=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 40, B=2, H=8, H_kv=2,
+             S_max=4096, D=64, scale=0.125, max_len=4096, dtype=1, stream=None)
+    a.update(kw)
+    return lib.attn_decode(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["ws"], a["wsb"], a["B"], a["H"],
+                           a["H_kv"], a["S_max"], a["D"], a["scale"], a["max_len"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(lens=None), -1), (dict(o=None), -1),
+    (dict(D=48), -3), (dict(dtype=3), -4), (dict(H_kv=3), -10), (dict(H_kv=0), -10),
+    (dict(H=64, H_kv=1), -8),                       # a group wider than one wave's 32 columns
+    (dict(max_len=0), -2), (dict(max_len=4097), -2), (dict(S_max=0), -2), (dict(B=0), -2),
+    (dict(scale=float("inf")), -9), (dict(ws=None), -11), (dict(wsb=16), -11),
+])
+def test_decode_rejects_invalid_arguments(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def test_decode_workspace_size(lib):
+    # many (batch, K/V head) pairs and a short cache: one chunk each, no workspace
+    assert lib.attn_decode_workspace_bytes(64, 64, 64, 64, 32) == 0
+    # long cache: split into chunks, partial O (D floats) and LSE per chunk and query head
+    n = lib.attn_decode_workspace_bytes(2, 8, 2, 64, 4096)
+    assert n > 0 and n % (2 * 8 * 65 * 4) == 0
+    assert lib.attn_decode_workspace_bytes(0, 8, 2, 64, 4096) == 0
+    # a valid call without workspace is accepted when none is needed (fails later only for lack of a GPU)
+    assert _decode(lib, B=64, H=64, H_kv=64, S_max=32, max_len=32, ws=None, wsb=0) in (0, -7)
+
+
 def test_no_device_reports_hip_error(lib):
     """A valid call with no GPU present fails with ATTN_ERR_HIP instead of aborting."""
     torch = pytest.importorskip("torch")
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert _fwd(lib) == -7
+    assert _decode(lib) == -7
     assert _fwd_gqa(lib, 2) == -7
     assert _bwd_gqa(lib, 1) == -7
 

@@ -6,9 +6,12 @@ the HIP path receive the arrays it returns.
 """
 from .synth import (  # noqa: F401
     CONFIGS,
+    DECODE_CONFIGS,
     AttnConfig,
+    DecodeConfig,
     round_to_bf16,
     make_cu_seqlens,
     make_inputs,
+    make_decode_inputs,
     allowed_pair_count,
 )

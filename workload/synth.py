@@ -153,3 +153,41 @@ def make_inputs(cfg: AttnConfig, seed: int, shape=None):
     out.update(cu_seqlens=cu, B=B, H=H, S=S, D=D, scale=1.0 / math.sqrt(D),
                mask_mode=cfg.mask_mode, dtype=cfg.dtype)
     return out
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    """One decode step against a key/value cache: q [B, H, D], caches [B, H_kv, S_max, D],
+    every batch entry's cache filled to `length` (<= S_max)."""
+    name: str
+    B: int
+    H: int
+    H_kv: int
+    S_max: int
+    D: int
+    dtype: str
+    length: int
+
+
+# Generation with the long-context model shape (16 heads of 128) over a full
+# 8192-token cache (Forge, "Roadmap": KV cache for generation; Cort33x: 2K-8K
+# training contexts), eight sequences at once.
+DECODE_CONFIGS = {
+    "decode_ctx8192": DecodeConfig("decode_ctx8192", B=8, H=16, H_kv=16, S_max=8192, D=128, dtype="bf16",
+                                   length=8192),
+}
+
+
+def make_decode_inputs(cfg: DecodeConfig, seed: int, lens=None):
+    """Seeded decode inputs: ``standard_normal`` draws in the order q, k_cache,
+    v_cache from ``default_rng(seed)``, rounded like make_inputs; ``lens`` (int32
+    [B]) defaults to ``cfg.length`` for every entry."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, shape in (("q", (cfg.B, cfg.H, cfg.D)), ("k", (cfg.B, cfg.H_kv, cfg.S_max, cfg.D)),
+                        ("v", (cfg.B, cfg.H_kv, cfg.S_max, cfg.D))):
+        x = rng.standard_normal(shape)
+        out[name] = round_to_bf16(x) if cfg.dtype == "bf16" else x.astype(np.float32)
+    lens = np.full(cfg.B, cfg.length, dtype=np.int32) if lens is None else np.asarray(lens, dtype=np.int32)
+    out.update(lens=lens, scale=1.0 / math.sqrt(cfg.D), dtype=cfg.dtype)
+    return out
