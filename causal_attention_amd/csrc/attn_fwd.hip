@@ -231,7 +231,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
 template <typename T, int D> struct FwdCfg {
 #ifdef ATTN_FWD_BN
   static constexpr int NW = ATTN_FWD_NW;
-  static constexpr int BN = (sizeof(T) == 4 && D == 128) ? 32 : ATTN_FWD_BN;
+  static constexpr int BN = (sizeof(T) == 4 && D == 128) ? 32 : D == 32 ? 64 : ATTN_FWD_BN;
   static constexpr int MINB = ATTN_FWD_MINB;
 #else
   static constexpr int NW = 4;
