@@ -7,6 +7,7 @@ binding: the same entry points, taking torch device tensors.
 """
 from ._binding import (  # noqa: F401
     ATTN_DTYPE_BF16,
+    ATTN_DTYPE_F16,
     ATTN_DTYPE_F32,
     ATTN_MASK_CAUSAL,
     ATTN_MASK_DOC_CAUSAL,

@@ -21,6 +21,7 @@ ATTN_MASK_CAUSAL = 0
 ATTN_MASK_DOC_CAUSAL = 1
 ATTN_DTYPE_F32 = 0
 ATTN_DTYPE_BF16 = 1
+ATTN_DTYPE_F16 = 2
 
 STATUS_NAMES = {
     0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEAD_DIM",
@@ -105,9 +106,11 @@ def _dtype_code(t):
     torch = _torch()
     if t.dtype == torch.bfloat16:
         return ATTN_DTYPE_BF16
+    if t.dtype == torch.float16:
+        return ATTN_DTYPE_F16
     if t.dtype == torch.float32:
         return ATTN_DTYPE_F32
-    raise TypeError(f"unsupported input dtype {t.dtype} (bfloat16 or float32)")
+    raise TypeError(f"unsupported input dtype {t.dtype} (bfloat16, float16 or float32)")
 
 
 def _ptr(t, name, shape=None, dtype=None, device=None):

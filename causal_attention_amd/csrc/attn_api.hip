@@ -11,10 +11,10 @@
 
 namespace {
 
-constexpr int kAbiVersion = 120;  // 1.20: grouped-query and decode entry points
+constexpr int kAbiVersion = 130;  // 1.30: grouped-query and decode entry points, fp16 inputs
 
 int check_common(int B, int H, int S, int D, int dtype) {
-  if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_DTYPE;
   if (D != 32 && D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
   if (B < 1 || H < 1 || S < 1) return ATTN_ERR_SHAPE;
   const int64_t elems = (int64_t)B * H * S * D;
@@ -59,7 +59,7 @@ attn::Args make_args(int B, int H, int S, int D, float scale, int mask_mode, con
   a.cu_seqlens = cu_seqlens;
   a.n_seqs = n_seqs;
   a.max_seqlen = max_seqlen;
-  a.bf16 = dtype == ATTN_DTYPE_BF16;
+  a.dtype = dtype;
   a.stream = static_cast<hipStream_t>(stream);
   return a;
 }
@@ -78,7 +78,7 @@ const char *attn_status_string(int status) {
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "B, H or S out of range (each >= 1, B*H*S*D < 2^31)";
     case ATTN_ERR_HEAD_DIM: return "head dimension D must be 32, 64 or 128";
-    case ATTN_ERR_DTYPE: return "unknown input dtype (ATTN_DTYPE_F32 or ATTN_DTYPE_BF16)";
+    case ATTN_ERR_DTYPE: return "unknown input dtype (ATTN_DTYPE_F32, ATTN_DTYPE_BF16 or ATTN_DTYPE_F16)";
     case ATTN_ERR_MASK: return "unknown mask mode (ATTN_MASK_CAUSAL or ATTN_MASK_DOC_CAUSAL)";
     case ATTN_ERR_SEQLENS: return "packed-document mode needs B == 1, 1 <= n_seqs <= S and 1 <= max_seqlen <= S";
     case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
@@ -190,8 +190,9 @@ int attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o, co
   a.dk = dk;
   a.dv = dv;
   hipError_t e;
-  if (a.bf16) {
-    // dQ computes Delta on the way (bitwise equal to the preprocess kernel's)
+  if (a.half()) {
+    // 16-bit inputs: dQ computes Delta on the way (bitwise equal to the
+    // preprocess kernel's)
     // and writes it for dK/dV: one pass over O and dO fewer.
     e = attn::launch_bwd_dq_delta(a);
     if (e == hipSuccess) e = attn::launch_bwd_dkdv(a);
@@ -244,7 +245,7 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, const i
   a.D = D;
   a.max_len = max_len;
   a.scale = scale;
-  a.bf16 = dtype == ATTN_DTYPE_BF16;
+  a.dtype = dtype;
   a.stream = static_cast<hipStream_t>(stream);
   return to_status(attn::launch_decode(a));
 }

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const float *_
       const T *dp = dO + (size_t)row * D + sub * VEC;
       const float *op = o + (size_t)row * D + sub * VEC;
       if constexpr (sizeof(T) == 2) {
-        const bf16x8 g = *reinterpret_cast<const bf16x8 *>(dp);
+        const typename Elem<T>::frag g = *reinterpret_cast<const typename Elem<T>::frag *>(dp);
         const f32x4 o0 = *reinterpret_cast<const f32x4 *>(op);
         const f32x4 o1 = *reinterpret_cast<const f32x4 *>(op + 4);
 #pragma unroll
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   // per-query shifts enter as a rank-1 product, so no lane needs the shift of
   // every row it holds), P = exp2(S' c2), dS = P dP', then dV^T += dO^T P and
   // dK^T += Q^T dS.
-  const frag ones = E::rows_b(hh);
+  const typename E::rows_frag ones = E::rows_b(hh);
   const float rscale = 1.0f / scale;
   auto tile = [&]<int P, bool MASK>(int q0) {
     const lds_t<T> *sq = qslot.template operator()<P>();
@@ -187,8 +187,8 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       f32x16 sacc = f32x16{}, pacc = f32x16{};
-      E::mma(sacc, E::rows_a(-sl[qb * 32 + c] * rscale, hh), ones);
-      E::mma(pacc, E::rows_a(-sd[qb * 32 + c], hh), ones);
+      E::mma_rows(sacc, E::rows_a(-sl[qb * 32 + c] * rscale, hh), ones);
+      E::mma_rows(pacc, E::rows_a(-sd[qb * 32 + c], hh), ones);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         E::mma(sacc, rf(sq, qb, kb), kfrag(kb));
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
   const float l2 = glse.load4((uint32_t)qi * 4) * kLog2e;
   float dl;
   if constexpr (FUSE_DELTA) {
-    static_assert(sizeof(T) == 2, "fused Delta follows the bf16 preprocess layout");
+    static_assert(sizeof(T) == 2, "fused Delta follows the 16-bit preprocess layout");
     // The preprocess kernel gives lane `sub` of a row elements 8*sub .. 8*sub+7
     // (an FMA chain from 0) and reduces the D/8 partial sums by butterfly.
     // Fragment kb of this lane is sub-block 2*kb + hh, so the lane computes
@@ -537,31 +537,44 @@ template <typename T, bool DOC>
 static hipError_t launch_dq_dt(const Args &a) { ATTN_DISPATCH_D(launch_dq_t, T, DOC) }
 
 hipError_t launch_bwd_preprocess(const Args &a) {
-  return a.bf16 ? launch_pre_dt<bf16>(a) : launch_pre_dt<float>(a);
+  switch (a.dtype) {
+    case 1: return launch_pre_dt<bf16>(a);
+    case 2: return launch_pre_dt<f16>(a);
+    default: return launch_pre_dt<float>(a);
+  }
 }
 
 hipError_t launch_bwd_dkdv(const Args &a) {
-  if (a.bf16) return a.doc ? launch_dkdv_dt<bf16, true>(a) : launch_dkdv_dt<bf16, false>(a);
-  return a.doc ? launch_dkdv_dt<float, true>(a) : launch_dkdv_dt<float, false>(a);
+  switch (a.dtype) {
+    case 1: return a.doc ? launch_dkdv_dt<bf16, true>(a) : launch_dkdv_dt<bf16, false>(a);
+    case 2: return a.doc ? launch_dkdv_dt<f16, true>(a) : launch_dkdv_dt<f16, false>(a);
+    default: return a.doc ? launch_dkdv_dt<float, true>(a) : launch_dkdv_dt<float, false>(a);
+  }
 }
 
 hipError_t launch_bwd_dq(const Args &a) {
-  if (a.bf16) return a.doc ? launch_dq_dt<bf16, true>(a) : launch_dq_dt<bf16, false>(a);
-  return a.doc ? launch_dq_dt<float, true>(a) : launch_dq_dt<float, false>(a);
+  switch (a.dtype) {
+    case 1: return a.doc ? launch_dq_dt<bf16, true>(a) : launch_dq_dt<bf16, false>(a);
+    case 2: return a.doc ? launch_dq_dt<f16, true>(a) : launch_dq_dt<f16, false>(a);
+    default: return a.doc ? launch_dq_dt<float, true>(a) : launch_dq_dt<float, false>(a);
+  }
 }
 
-template <bool DOC>
+template <typename T, bool DOC>
 static hipError_t launch_dq_delta_d(const Args &a) {
   switch (a.D) {
-    case 32: return launch_dq_t<bf16, 32, DOC, true>(a);
-    case 64: return launch_dq_t<bf16, 64, DOC, true>(a);
-    default: return launch_dq_t<bf16, 128, DOC, true>(a);
+    case 32: return launch_dq_t<T, 32, DOC, true>(a);
+    case 64: return launch_dq_t<T, 64, DOC, true>(a);
+    default: return launch_dq_t<T, 128, DOC, true>(a);
   }
 }
 
 hipError_t launch_bwd_dq_delta(const Args &a) {
-  if (!a.bf16) return hipErrorInvalidValue;
-  return a.doc ? launch_dq_delta_d<true>(a) : launch_dq_delta_d<false>(a);
+  switch (a.dtype) {
+    case 1: return a.doc ? launch_dq_delta_d<bf16, true>(a) : launch_dq_delta_d<bf16, false>(a);
+    case 2: return a.doc ? launch_dq_delta_d<f16, true>(a) : launch_dq_delta_d<f16, false>(a);
+    default: return hipErrorInvalidValue;  // Delta fusion follows the 16-bit preprocess layout
+  }
 }
 
 }  // namespace attn

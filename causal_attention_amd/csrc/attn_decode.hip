@@ -215,7 +215,11 @@ static hipError_t launch_decode_dt(const DecodeArgs &a) {
 }
 
 hipError_t launch_decode(const DecodeArgs &a) {
-  return a.bf16 ? launch_decode_dt<bf16>(a) : launch_decode_dt<float>(a);
+  switch (a.dtype) {
+    case 1: return launch_decode_dt<bf16>(a);
+    case 2: return launch_decode_dt<f16>(a);
+    default: return launch_decode_dt<float>(a);
+  }
 }
 
 size_t decode_workspace_bytes(int B, int H, int H_kv, int D, int max_len) {

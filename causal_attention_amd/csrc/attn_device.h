@@ -2,7 +2,7 @@
 //
 // Matrix-core tiling.  Every contraction is built from one 32x32 output block
 // per wave and 16-deep reduction steps ("k-blocks"):
-//   * bf16 inputs: one v_mfma_f32_32x32x16_bf16 per k-block;
+//   * bf16 / fp16 inputs: one v_mfma_f32_32x32x16_{bf16,f16} per k-block;
 //   * fp32 inputs: eight v_mfma_f32_32x32x2_f32 per k-block (true fp32).
 // Lane l = 32*h + c (h = l/32 the wave half, c = l%32) feeds eight k-slots of
 // one k-block: A[row c][slot s of half h] and B[slot s of half h][col c], and
@@ -27,6 +27,8 @@ namespace attn {
 
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16;
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -63,17 +65,21 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Element traits: the 8-slot fragment type and the 32x32x16 step.
 template <typename T> struct Elem;
 
-template <> struct Elem<bf16> {
-  using frag = bf16x8;                  // 8 x bf16 = 16 bytes
+// 16-bit inputs (bf16 or fp16): one 32x32x16 step per k-block.
+template <typename T, typename V> struct Elem16 {
+  using frag = V;                       // 8 x 16-bit = 16 bytes
   static constexpr int kFragWords = 4;  // 32-bit words per fragment
   __device__ __forceinline__ static void mma(f32x16 &acc, const frag &a, const frag &b) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    if constexpr (__is_same(T, bf16))
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    else
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
   }
   // Round slots 8*j .. 8*j+7 of a 32x32 result to a fragment (RNE).
   __device__ __forceinline__ static frag pack(const f32x16 &acc, int j) {
     frag f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) f[s] = (bf16)acc[8 * j + s];
+    for (int s = 0; s < 8; ++s) f[s] = (T)acc[8 * j + s];
     return f;
   }
   // pack() and add the eight fp32 values to `sum` (round-to-nearest-even is
@@ -84,31 +90,39 @@ template <> struct Elem<bf16> {
     for (int s = 0; s < 8; ++s) sum += acc[8 * j + s];
     return pack(acc, j);
   }
-  // Operands of a rank-1 product mma(acc, rows_a(x, hh), rows_b(hh)) that adds
-  // x_c to every element of row c of a 32x32 result, x_c being the value lane
-  // c passes (lanes 32-63 pass anything).  x is split into three bf16 terms
-  // whose fp32 sum reproduces it to fp32 precision; the B side is ones.
-  __device__ __forceinline__ static frag rows_a(float x, int hh) {
+  // Operands of a rank-1 product mma_rows(acc, rows_a(x, hh), rows_b(hh)) that
+  // adds x_c to every element of row c of a 32x32 result, x_c being the value
+  // lane c passes (lanes 32-63 pass anything).  x is split into three bf16
+  // terms whose fp32 sum reproduces it to fp32 precision, times ones.  bf16
+  // has fp32's exponent range, so this step uses bf16 for fp16 inputs too
+  // (the two instructions accumulate into the same fp32 result).
+  using rows_frag = bf16x8;
+  __device__ __forceinline__ static void mma_rows(f32x16 &acc, const rows_frag &a, const rows_frag &b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+  }
+  __device__ __forceinline__ static rows_frag rows_a(float x, int hh) {
     const float y = hh == 0 ? x : 0.f;
     const bf16 t0 = (bf16)y;
     const float r0 = y - (float)t0;
     const bf16 t1 = (bf16)r0;
     const bf16 t2 = (bf16)(r0 - (float)t1);
-    frag f = {};
+    rows_frag f = {};
     f[0] = t0;
     f[1] = t1;
     f[2] = t2;
     return f;
   }
-  __device__ __forceinline__ static frag rows_b(int hh) {
+  __device__ __forceinline__ static rows_frag rows_b(int hh) {
     const bf16 one = (bf16)(hh == 0 ? 1.f : 0.f);
-    frag f = {};
+    rows_frag f = {};
     f[0] = one;
     f[1] = one;
     f[2] = one;
     return f;
   }
 };
+template <> struct Elem<bf16> : Elem16<bf16, bf16x8> {};
+template <> struct Elem<f16> : Elem16<f16, f16x8> {};
 
 template <> struct Elem<float> {
   using frag = f32x8;                   // 8 x fp32 = 32 bytes
@@ -132,6 +146,8 @@ template <> struct Elem<float> {
     }
     return f;
   }
+  using rows_frag = frag;
+  __device__ __forceinline__ static void mma_rows(f32x16 &acc, const frag &a, const frag &b) { mma(acc, a, b); }
   __device__ __forceinline__ static frag rows_a(float x, int hh) {
     frag f = {};
     f[0] = hh == 0 ? x : 0.f;
@@ -166,11 +182,11 @@ __device__ __forceinline__ typename Elem<T>::frag lds_frag(const lds_t<T> *p) {
 // fp32: eight ds_read_b32 (no transposing read exists for 32-bit data).
 template <typename T, int LD> struct TrRead;
 
-template <int LD> struct TrRead<bf16, LD> {
-  using frag = bf16x8;
-  const lds_t<bf16> *base;   // this lane's source address for row0 = col0 = 0
-  const lds_t<bf16> *base8;  // ... and for the rows 8 further down
-  __device__ __forceinline__ TrRead(const lds_t<bf16> *tile, int lane) {
+template <typename T, int LD> struct TrRead16 {
+  using frag = typename Elem<T>::frag;
+  const lds_t<T> *base;   // this lane's source address for row0 = col0 = 0
+  const lds_t<T> *base8;  // ... and for the rows 8 further down
+  __device__ __forceinline__ TrRead16(const lds_t<T> *tile, int lane) {
     const int g = lane / 16, i = lane % 16, h = g / 2;
     const int off = (4 * h + i / 4) * LD + 16 * (g % 2) + 4 * (i % 4);
     // The second read's offset is kept opaque to constant folding: folded
@@ -181,7 +197,7 @@ template <int LD> struct TrRead<bf16, LD> {
     base = tile + off;
     base8 = tile + off8;
   }
-  __device__ __forceinline__ TrRead(const bf16 *tile, int lane) : TrRead(lds_cast(const_cast<bf16 *>(tile)), lane) {}
+  __device__ __forceinline__ TrRead16(const T *tile, int lane) : TrRead16(lds_cast(const_cast<T *>(tile)), lane) {}
   __device__ __forceinline__ frag operator()(int row0, int col0) const {
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + row0 * LD + col0));
@@ -195,6 +211,13 @@ template <int LD> struct TrRead<bf16, LD> {
     }
     return __builtin_bit_cast(frag, v);
   }
+};
+
+template <int LD> struct TrRead<bf16, LD> : TrRead16<bf16, LD> {
+  using TrRead16<bf16, LD>::TrRead16;
+};
+template <int LD> struct TrRead<f16, LD> : TrRead16<f16, LD> {
+  using TrRead16<f16, LD>::TrRead16;
 };
 
 template <int LD> struct TrRead<float, LD> {
@@ -380,12 +403,12 @@ __device__ __forceinline__ void dma_vec64(const GBuf &g, lds_t<float> *dst, int 
 // only this lane's element offsets, so one serves every tile of that shape.
 template <typename T, int D> struct TrSwz;
 
-template <int D> struct TrSwz<bf16, D> {
-  using frag = bf16x8;
+template <typename T, int D> struct TrSwz16 {
+  using frag = typename Elem<T>::frag;
   static constexpr int DB = D / 32;
   // [read][db]: the first read covers rows 0-7 of the 16, the second rows 8-15.
   int off[2][DB];
-  __device__ __forceinline__ explicit TrSwz(int lane) {
+  __device__ __forceinline__ explicit TrSwz16(int lane) {
     const int g = lane / 16, i = lane % 16;
     const int rl = 4 * (g / 2) + i / 4;             // row within an 8-row group
     const int x = 2 * (g % 2) + (i % 4) / 2;        // 16-byte chunk within the 32-column block
@@ -395,22 +418,22 @@ template <int D> struct TrSwz<bf16, D> {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int r = rl + 8 * k;
-        off[k][db] = r * D + 8 * (int)((uint32_t)(4 * db + x) ^ swz_mask<bf16, D>(r)) + e;
+        off[k][db] = r * D + 8 * (int)((uint32_t)(4 * db + x) ^ swz_mask<T, D>(r)) + e;
       }
   }
   // A copy whose offsets the compiler cannot trace back to the loop-invariant
   // originals: taken once per tile, it keeps the sum with each tile's LDS
   // address inside the loop, where the constant part folds into the
   // instruction's offset field instead of occupying a register per tile.
-  __device__ __forceinline__ TrSwz pinned() const {
-    TrSwz t = *this;
+  __device__ __forceinline__ TrSwz16 pinned() const {
+    TrSwz16 t = *this;
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
       for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(t.off[k][db]));
     return t;
   }
-  __device__ __forceinline__ frag operator()(const lds_t<bf16> *tile, int row0, int db) const {
+  __device__ __forceinline__ frag operator()(const lds_t<T> *tile, int row0, int db) const {
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tile + row0 * D + off[0][db]));
     const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tile + row0 * D + off[1][db]));
@@ -423,6 +446,17 @@ template <int D> struct TrSwz<bf16, D> {
     }
     return __builtin_bit_cast(frag, v);
   }
+};
+
+template <int D> struct TrSwz<bf16, D> : TrSwz16<bf16, D> {
+  using TrSwz16<bf16, D>::TrSwz16;
+  __device__ __forceinline__ TrSwz(const TrSwz16<bf16, D> &t) : TrSwz16<bf16, D>(t) {}
+  __device__ __forceinline__ TrSwz pinned() const { return TrSwz(TrSwz16<bf16, D>::pinned()); }
+};
+template <int D> struct TrSwz<f16, D> : TrSwz16<f16, D> {
+  using TrSwz16<f16, D>::TrSwz16;
+  __device__ __forceinline__ TrSwz(const TrSwz16<f16, D> &t) : TrSwz16<f16, D>(t) {}
+  __device__ __forceinline__ TrSwz pinned() const { return TrSwz(TrSwz16<f16, D>::pinned()); }
 };
 
 template <int D> struct TrSwz<float, D> {

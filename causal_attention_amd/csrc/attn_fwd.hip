@@ -277,6 +277,12 @@ static hipError_t launch_fwd_dt(const Args &a) {
   }
 }
 
-hipError_t launch_fwd(const Args &a) { return a.bf16 ? launch_fwd_dt<bf16>(a) : launch_fwd_dt<float>(a); }
+hipError_t launch_fwd(const Args &a) {
+  switch (a.dtype) {
+    case 1: return launch_fwd_dt<bf16>(a);
+    case 2: return launch_fwd_dt<f16>(a);
+    default: return launch_fwd_dt<float>(a);
+  }
+}
 
 }  // namespace attn

@@ -17,7 +17,8 @@ struct Args {
   bool doc;                 // packed-document mask
   const int32_t *cu_seqlens;
   int n_seqs, max_seqlen;
-  bool bf16;                // input dtype: bf16 (true) or fp32 (false)
+  int dtype;                // input dtype: ATTN_DTYPE_F32, _BF16 or _F16 (attn_api.h)
+  bool half() const { return dtype != 0; }  // 16-bit inputs
   hipStream_t stream;
 };
 
@@ -29,7 +30,7 @@ struct DecodeArgs {
   float *o_part, *lse_part;  // chunk partials (workspace), unused with one chunk
   int B, H, H_kv, S_max, D, max_len;
   float scale;
-  bool bf16;
+  int dtype;
   hipStream_t stream;
 };
 hipError_t launch_decode(const DecodeArgs &a);
@@ -40,7 +41,7 @@ hipError_t launch_fwd(const Args &a);
 hipError_t launch_bwd_preprocess(const Args &a);
 hipError_t launch_bwd_dkdv(const Args &a);
 hipError_t launch_bwd_dq(const Args &a);
-// bf16 only: dQ that also computes Delta from O and dO (written to a.delta)
+// 16-bit inputs only: dQ that also computes Delta from O and dO (written to a.delta)
 hipError_t launch_bwd_dq_delta(const Args &a);
 
 }  // namespace attn

@@ -29,8 +29,10 @@
  *
  * Layout.  Q, K, V, dO, O, dQ, dK, dV are contiguous [B, H, S, D] row-major
  * (D fastest); LSE and Delta are contiguous [B, H, S].  In DOC_CAUSAL mode
- * B must be 1.  Q, K, V and dO share one input dtype (ATTN_DTYPE_*); O, LSE,
- * Delta, dQ, dK and dV are always float32.
+ * B must be 1.  Q, K, V and dO share one input dtype (ATTN_DTYPE_F32, _BF16
+ * or _F16; the 16-bit types run on the bf16 / fp16 matrix cores with fp32
+ * accumulation, P and dS rounded to the input type); O, LSE, Delta, dQ, dK
+ * and dV are always float32.
  *
  * Ownership.  Every pointer except where noted is a DEVICE pointer on the
  * current HIP device, allocated and owned by the caller.  The library never
@@ -77,7 +79,7 @@ typedef enum attn_status {
 } attn_status;
 
 enum { ATTN_MASK_CAUSAL = 0, ATTN_MASK_DOC_CAUSAL = 1 };
-enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 };
+enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1, ATTN_DTYPE_F16 = 2 };
 
 /*
  * Forward.  Reads q, k, v [B,H,S,D] (dtype), writes o [B,H,S,D] float32 and,

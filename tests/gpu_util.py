@@ -14,6 +14,7 @@ from oracle import attention_bwd_ref
 TOL = {
     "f32": dict(max_abs=1e-4, rel_fro=None, lse=1e-4),
     "bf16": dict(max_abs=2e-2, rel_fro=1e-2, lse=1e-3),
+    "f16": dict(max_abs=2e-2, rel_fro=1e-2, lse=1e-3),  # 16-bit inputs: the bf16 bounds
 }
 
 
@@ -24,7 +25,7 @@ def log(msg):
 
 def to_device(x):
     import torch
-    dt = torch.bfloat16 if x["dtype"] == "bf16" else torch.float32
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[x["dtype"]]
     dev = {n: torch.from_numpy(np.ascontiguousarray(x[n])).to("cuda").to(dt).contiguous()
            for n in ("q", "k", "v", "do")}
     cu = x.get("cu_seqlens")

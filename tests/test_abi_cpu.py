@@ -31,7 +31,7 @@ def test_header_status_codes_match_binding():
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 120
+    assert lib.attn_abi_version() == 130
 
 
 def test_status_strings(lib):
@@ -61,7 +61,7 @@ def _bwd(lib, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
     (dict(D=48), -3), (dict(D=256), -3), (dict(D=0), -3),
-    (dict(dtype=2), -4), (dict(dtype=-1), -4),
+    (dict(dtype=3), -4), (dict(dtype=-1), -4),
     (dict(mask=2), -5), (dict(mask=-1), -5),
     (dict(mask=1, cu=None, n=1, mx=64), -1),
     (dict(mask=1, cu=FAKE, n=1, mx=64, B=2), -6),
@@ -182,7 +182,7 @@ def test_binding_refuses_host_tensors():
 
 def test_binding_rejects_unsupported_dtype():
     torch = pytest.importorskip("torch")
-    q = torch.zeros(1, 1, 16, 32, dtype=torch.float16)
+    q = torch.zeros(1, 1, 16, 32, dtype=torch.float64)
     with pytest.raises(TypeError):
         ca.attn_fwd(q, q, q, None, None, 0.1)
 

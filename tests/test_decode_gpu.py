@@ -9,7 +9,7 @@ import pytest
 
 from oracle import attention_decode_ref
 from tests.gpu_util import TOL, errors, log
-from workload import round_to_bf16
+from workload import round_to
 
 pytestmark = pytest.mark.gpu
 
@@ -28,15 +28,14 @@ def decode_inputs(dtype, B, H, H_kv, S_max, D, lens, seed):
     q = rng.standard_normal((B, H, D))
     k = rng.standard_normal((B, H_kv, S_max, D))
     v = rng.standard_normal((B, H_kv, S_max, D))
-    cast = round_to_bf16 if dtype == "bf16" else (lambda x: x.astype(np.float32))
-    return dict(q=cast(q), k=cast(k), v=cast(v), lens=np.asarray(lens, dtype=np.int32), dtype=dtype,
+    return dict(q=round_to(q, dtype), k=round_to(k, dtype), v=round_to(v, dtype), lens=np.asarray(lens, dtype=np.int32), dtype=dtype,
                 scale=1.0 / np.sqrt(D))
 
 
 def run_decode(x):
     import torch
     import causal_attention_amd as ca
-    dt = torch.bfloat16 if x["dtype"] == "bf16" else torch.float32
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[x["dtype"]]
     q, k, v = (torch.from_numpy(np.ascontiguousarray(x[n])).cuda().to(dt) for n in ("q", "k", "v"))
     lens = torch.from_numpy(x["lens"]).cuda()
     B, H, D = q.shape
@@ -72,6 +71,8 @@ CASES = [
     ("bf16", 2, 4, 4, 777, 32, [777, 400]),
     ("f32", 2, 4, 1, 257, 64, [257, 256]),
     ("f32", 1, 8, 2, 100, 128, [65]),
+    ("f16", 2, 8, 2, 1500, 128, [1500, 700]),
+    ("f16", 1, 4, 4, 300, 64, [300]),
 ]
 
 

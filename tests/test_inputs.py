@@ -82,3 +82,20 @@ def test_grouped_query_config_draws_fewer_kv_heads():
     x = make_inputs(tiny, 6)
     assert x["q"].shape == (1, 16, 8, 64) and x["do"].shape == (1, 16, 8, 64)
     assert x["k"].shape == (1, 4, 8, 64) and x["v"].shape == (1, 4, 8, 64)
+
+
+def test_fp16_rounding_is_nearest_even():
+    """Round-to-nearest-even to IEEE half: every result is representable, lies within
+    half a unit in the last place of the input, and equals PyTorch's float32 -> float16
+    cast on inputs that are exact in float32 (PyTorch's float64 -> float16 cast rounds
+    twice, through float32, so it is not the reference for float64 inputs)."""
+    torch = pytest.importorskip("torch")
+    from workload import round_to_f16
+    x = np.random.default_rng(3).standard_normal(10000) * np.logspace(-4, 4, 10000)
+    r = round_to_f16(x).astype(np.float64)
+    assert np.array_equal(r, r.astype(np.float16).astype(np.float64))
+    ulp = np.spacing(np.abs(r).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(x - r) <= ulp / 2)
+    x32 = x.astype(np.float32)
+    ref = torch.tensor(x32).to(torch.float16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(round_to_f16(x32), ref)

@@ -9,7 +9,9 @@ from .synth import (  # noqa: F401
     DECODE_CONFIGS,
     AttnConfig,
     DecodeConfig,
+    round_to,
     round_to_bf16,
+    round_to_f16,
     make_cu_seqlens,
     make_inputs,
     make_decode_inputs,

@@ -15,7 +15,8 @@ Recipe (stated once so that every consumer draws the same numbers):
   C-order [B, H, S, D] array (K and V [B, H_kv, S, D] for grouped-query
   workloads);
 * multiply Q, K, V (not dO) by ``qkv_scale``;
-* round to the input dtype (bf16: round-to-nearest-even from float32; fp32:
+* round to the input dtype (bf16: round-to-nearest-even from float32; fp16:
+  round-to-nearest-even from float64; fp32:
   round-to-nearest from float64);
 * document lengths for the packed workload come from a separate generator
   ``default_rng(doc_seed)``: integers uniform in [lo, hi] (both inclusive) are
@@ -40,7 +41,7 @@ class AttnConfig:
     H: int
     S: int
     D: int
-    dtype: str  # "f32" or "bf16": the dtype of Q, K, V and dO
+    dtype: str  # "f32", "bf16" or "f16": the dtype of Q, K, V and dO
     qkv_scale: float = 1.0
     mask_mode: int = MASK_CAUSAL
     doc_len_range: tuple | None = None  # (lo, hi) inclusive, packed mode only
@@ -92,6 +93,22 @@ def round_to_bf16(x) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32).reshape(f.shape)
 
 
+def round_to_f16(x) -> np.ndarray:
+    """Round to the nearest IEEE half (ties to even); returns float32 holding it."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float32)
+
+
+def round_to(x, dtype: str) -> np.ndarray:
+    """Round to input dtype `dtype` ("bf16", "f16" or "f32"); returns float32."""
+    if dtype == "bf16":
+        return round_to_bf16(x)
+    if dtype == "f16":
+        return round_to_f16(x)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32)
+    raise ValueError(f"unknown dtype {dtype}")
+
+
 def make_cu_seqlens(total: int, lo: int, hi: int, seed: int) -> np.ndarray:
     """Cumulative document boundaries [0, L0, L0+L1, ..., total] as int32."""
     if total < 1 or lo < 1 or hi < lo:
@@ -138,12 +155,7 @@ def make_inputs(cfg: AttnConfig, seed: int, shape=None):
         x = rng.standard_normal((B, H_kv if name in ("k", "v") else H, S, D))
         if name != "do":
             x = x * cfg.qkv_scale
-        if cfg.dtype == "bf16":
-            out[name] = round_to_bf16(x)
-        elif cfg.dtype == "f32":
-            out[name] = x.astype(np.float32)
-        else:
-            raise ValueError(f"unknown dtype {cfg.dtype}")
+        out[name] = round_to(x, cfg.dtype)
     cu = None
     if cfg.mask_mode == MASK_DOC_CAUSAL:
         if B != 1:
@@ -187,7 +199,7 @@ def make_decode_inputs(cfg: DecodeConfig, seed: int, lens=None):
     for name, shape in (("q", (cfg.B, cfg.H, cfg.D)), ("k", (cfg.B, cfg.H_kv, cfg.S_max, cfg.D)),
                         ("v", (cfg.B, cfg.H_kv, cfg.S_max, cfg.D))):
         x = rng.standard_normal(shape)
-        out[name] = round_to_bf16(x) if cfg.dtype == "bf16" else x.astype(np.float32)
+        out[name] = round_to(x, cfg.dtype)
     lens = np.full(cfg.B, cfg.length, dtype=np.int32) if lens is None else np.asarray(lens, dtype=np.int32)
     out.update(lens=lens, scale=1.0 / math.sqrt(cfg.D), dtype=cfg.dtype)
     return out
