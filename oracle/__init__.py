@@ -22,3 +22,11 @@ from .attention import (  # noqa: F401
     attention_dkdv_rows_ref,
     delta_ref,
 )
+from .rope import (  # noqa: F401
+    ROPE_BASE,
+    attention_rope_ref,
+    rope_angles,
+    rope_positions,
+    rope_rotate,
+    round_to_dtype,
+)
