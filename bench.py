@@ -11,7 +11,8 @@ accounting), divided by the measured time.  One JSON line is printed.
 
 Besides the headline workload the line carries:
   by_workload   the same measurement at the other full-size workloads
-                (context 512, 8192, packed documents, grouped-query heads),
+                (context 512, 8192, packed documents, grouped-query heads,
+                RoPE on q and k),
                 fewer steps, and one decode step against a full 8192-token
                 K/V cache (time, GB/s against HBM peak);
   kernels       per-kernel mean duration from HIP events on the launch stream;
@@ -41,7 +42,7 @@ PEAK_FP32_TFLOPS = 157.3    # fp32 matrix/vector peak used for fp32 inputs
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "lm237m_ctx1024"
 SEEDS = {"tiny_f32": 1, "lm12m_ctx512": 2, "lm237m_ctx1024": 3, "long_ctx8192": 4, "packed_docs8192": 5,
-         "lm237m_ctx1024_gqa4": 6}
+         "lm237m_ctx1024_gqa4": 6, "lm237m_ctx1024_rope": 7}
 # algorithmic flops per allowed pair, per kernel (times D)
 KERNEL_FLOPS_PER_PAIR = {"fwd": 4, "dkdv": 8, "dq": 2}
 KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip"]
@@ -105,13 +106,25 @@ class Workload:
         self.stream = torch.cuda.current_stream()
         self.sargs = dict(mask_mode=cfg.mask_mode, cu_seqlens=self.cu, max_seqlen=self.max_seqlen,
                           stream=self.stream)
+        if cfg.rope:  # RoPE: the table is built once, as a model does; q_rot, k_rot are kept for the backward
+            self.tab = ca.rope_table(self.max_seqlen or S, D, 10000.0)
+            self.q_rot = torch.empty_like(self.q)
+            self.k_rot = torch.empty_like(self.k)
 
     def fwd(self):
-        self.ca.attn_fwd(self.q, self.k, self.v, self.o, self.lse, self.x["scale"], **self.sargs)
+        if self.cfg.rope:
+            self.ca.attn_fwd_rope(self.q, self.k, self.v, self.q_rot, self.k_rot, self.o, self.lse, self.tab,
+                                  self.x["scale"], **self.sargs)
+        else:
+            self.ca.attn_fwd(self.q, self.k, self.v, self.o, self.lse, self.x["scale"], **self.sargs)
 
     def bwd(self):
-        self.ca.attn_bwd(self.q, self.k, self.v, self.o, self.do, self.lse, self.dq, self.dk, self.dv,
-                         self.delta, self.x["scale"], **self.sargs)
+        if self.cfg.rope:
+            self.ca.attn_bwd_rope(self.q_rot, self.k_rot, self.v, self.o, self.do, self.lse, self.dq, self.dk,
+                                  self.dv, self.delta, self.tab, self.x["scale"], **self.sargs)
+        else:
+            self.ca.attn_bwd(self.q, self.k, self.v, self.o, self.do, self.lse, self.dq, self.dk, self.dv,
+                             self.delta, self.x["scale"], **self.sargs)
 
     def pre(self):
         self.ca.attn_bwd_preprocess(self.o, self.do, self.delta, stream=self.stream)
@@ -146,7 +159,10 @@ class Workload:
         dQ with Delta fused, then dK/dV; the staged dQ reads Delta instead)."""
         import torch
         stages = [("fwd", self.fwd), ("bwd", self.bwd)]
-        if not self.grouped:  # the staged entry points take plain multi-head inputs
+        if self.cfg.rope:  # the rotation pass alone (it is part of the forward above)
+            stages.append(("rope", lambda: self.ca.attn_rope(self.q, self.k, self.q_rot, self.k_rot, self.tab,
+                                                             stream=self.stream)))
+        elif not self.grouped:  # the staged entry points take plain multi-head inputs
             stages += [("pre", self.pre), ("dkdv", self.dkdv), ("dq", self.dqk)]
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(reps)]
         for _ in range(3):
@@ -372,6 +388,9 @@ def measure(name, steps, warmup, reps):
         "kernels_ms": {k: round(v["mean_ms"], 5) for k, v in times.items()},
         "pairs": w.pairs,
     }
+    if "rope" in times:  # the rotation pass reads q, k and writes q_rot, k_rot once (the table stays in L2)
+        nbytes = 2 * (w.q.numel() + w.k.numel()) * w.q.element_size()
+        summary["rope_GBs"] = nbytes / (times["rope"]["mean_ms"] * 1e-3) / 1e9
     return w, sec, times, summary
 
 
@@ -399,7 +418,8 @@ def main():
         f"{sec * 1e3:.4f} ms/step, kernels {summary['kernels_ms']}")
     by_workload = {a.workload: summary}
     if not a.no_others:
-        for name in ("lm12m_ctx512", "long_ctx8192", "packed_docs8192", "lm237m_ctx1024_gqa4", "lm237m_ctx1024"):
+        for name in ("lm12m_ctx512", "long_ctx8192", "packed_docs8192", "lm237m_ctx1024_gqa4",
+                     "lm237m_ctx1024_rope", "lm237m_ctx1024"):
             if name == a.workload:
                 continue
             _, _, _, s = measure(name, max(10, a.steps // 4), max(3, a.warmup // 2), max(10, a.kernel_reps // 2))

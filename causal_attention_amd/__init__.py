@@ -17,13 +17,18 @@ from ._binding import (  # noqa: F401
     attn_bwd_dkdv,
     attn_bwd_dq,
     attn_bwd_preprocess,
+    attn_bwd_rope,
     attn_decode,
     attn_fwd,
+    attn_fwd_rope,
+    attn_rope,
+    attn_rope_table,
     backward,
     decode,
     decode_workspace_bytes,
     forward,
     header_functions,
     load_library,
+    rope_table,
     status_string,
 )

@@ -27,6 +27,7 @@ STATUS_NAMES = {
     0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEAD_DIM",
     -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_MASK", -6: "ATTN_ERR_SEQLENS", -7: "ATTN_ERR_HIP",
     -8: "ATTN_ERR_UNIMPLEMENTED", -9: "ATTN_ERR_SCALE", -10: "ATTN_ERR_HEADS", -11: "ATTN_ERR_WORKSPACE",
+    -12: "ATTN_ERR_ROPE",
 }
 
 
@@ -51,6 +52,11 @@ SIGNATURES = {
     "attn_bwd_gqa": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
     "attn_decode_workspace_bytes": [_I, _I, _I, _I, _I],
     "attn_decode": [_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _I, _F, _I, _I, _P],
+    "attn_rope_table": [_P, _I, _I, _F, _P],
+    "attn_rope": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _I, _I, _P],
+    "attn_fwd_rope": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
+    "attn_bwd_rope": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _I, _I,
+                      _I, _P],
     "attn_status_string": [_I],
     "attn_abi_version": [],
 }
@@ -248,6 +254,73 @@ def attn_bwd_dq(q, k, v, dO, lse, delta, dq, scale, mask_mode=ATTN_MASK_CAUSAL, 
         B, H, S, D, float(scale), int(mask_mode), cu, ns, ms, dt, _stream(stream)))
 
 
+def _rope_table_ptr(tab, D, dev):
+    torch = _torch()
+    if tab is None or tab.dim() != 3 or tuple(tab.shape[1:]) != (D // 2, 2):
+        raise ValueError(f"the RoPE table must be [n_pos, {D // 2}, 2] float32")
+    return _ptr(tab, "rope table", dtype=torch.float32, device=dev), int(tab.shape[0])
+
+
+def attn_rope_table(tab, base=10000.0, stream=None):
+    """Fill tab [n_pos, D/2, 2] fp32 with (cos, sin) of p * base^(-2i/D)."""
+    lib = load_library()
+    if tab.dim() != 3 or tab.shape[2] != 2:
+        raise ValueError("the RoPE table must be [n_pos, D/2, 2] float32")
+    n_pos, half = int(tab.shape[0]), int(tab.shape[1])
+    _check(lib.attn_rope_table(_ptr(tab, "tab", dtype=_torch().float32), n_pos, 2 * half, float(base),
+                               _stream(stream)))
+
+
+def attn_rope(q, k, q_rot, k_rot, tab, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None, n_seqs=None,
+              max_seqlen=None, stream=None):
+    """Enqueue the rotation: q_rot, k_rot (q's and k's shapes and dtype; may be q, k)."""
+    lib = load_library()
+    B, H, H_kv, S, D, dt = _qkv_info(q, k, k)
+    dev = q.device
+    cu, ns, ms = _mask_args(mask_mode, cu_seqlens, n_seqs, max_seqlen, dev)
+    tp, n_pos = _rope_table_ptr(tab, D, dev)
+    _check(lib.attn_rope(
+        _ptr(q, "q", device=dev), _ptr(k, "k", device=dev), _ptr(q_rot, "q_rot", tuple(q.shape), q.dtype, dev),
+        _ptr(k_rot, "k_rot", tuple(k.shape), k.dtype, dev), tp, n_pos, B, H, H_kv, S, D, int(mask_mode), cu, ns, ms,
+        dt, _stream(stream)))
+
+
+def attn_fwd_rope(q, k, v, q_rot, k_rot, o, lse, tab, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None,
+                  n_seqs=None, max_seqlen=None, stream=None):
+    """Enqueue RoPE on q, k (into q_rot, k_rot, kept for the backward), then the forward."""
+    torch = _torch()
+    lib = load_library()
+    B, H, H_kv, S, D, dt = _qkv_info(q, k, v)
+    dev = q.device
+    cu, ns, ms = _mask_args(mask_mode, cu_seqlens, n_seqs, max_seqlen, dev)
+    tp, n_pos = _rope_table_ptr(tab, D, dev)
+    _check(lib.attn_fwd_rope(
+        _ptr(q, "q", device=dev), _ptr(k, "k", device=dev), _ptr(v, "v", device=dev),
+        _ptr(q_rot, "q_rot", tuple(q.shape), q.dtype, dev), _ptr(k_rot, "k_rot", tuple(k.shape), k.dtype, dev),
+        _ptr(o, "o", (B, H, S, D), torch.float32, dev), _ptr(lse, "lse", (B, H, S), torch.float32, dev),
+        tp, n_pos, B, H, H_kv, S, D, float(scale), int(mask_mode), cu, ns, ms, dt, _stream(stream)))
+
+
+def attn_bwd_rope(q_rot, k_rot, v, o, dO, lse, dq, dk, dv, delta, tab, scale, mask_mode=ATTN_MASK_CAUSAL,
+                  cu_seqlens=None, n_seqs=None, max_seqlen=None, stream=None):
+    """Enqueue the backward on the rotated q_rot, k_rot; dq and dk come out with
+    respect to the unrotated q and k."""
+    torch = _torch()
+    lib = load_library()
+    B, H, H_kv, S, D, dt = _qkv_info(q_rot, k_rot, v)
+    dev = q_rot.device
+    cu, ns, ms = _mask_args(mask_mode, cu_seqlens, n_seqs, max_seqlen, dev)
+    tp, n_pos = _rope_table_ptr(tab, D, dev)
+    f32 = torch.float32
+    _check(lib.attn_bwd_rope(
+        _ptr(q_rot, "q_rot", device=dev), _ptr(k_rot, "k_rot", device=dev), _ptr(v, "v", device=dev),
+        _ptr(o, "o", (B, H, S, D), f32, dev), _ptr(dO, "dO", (B, H, S, D), q_rot.dtype, dev),
+        _ptr(lse, "lse", (B, H, S), f32, dev), _ptr(dq, "dq", (B, H, S, D), f32, dev),
+        _ptr(dk, "dk", (B, H_kv, S, D), f32, dev), _ptr(dv, "dv", (B, H_kv, S, D), f32, dev),
+        _ptr(delta, "delta", (B, H, S), f32, dev), tp, n_pos,
+        B, H, H_kv, S, D, float(scale), int(mask_mode), cu, ns, ms, dt, _stream(stream)))
+
+
 def decode_workspace_bytes(B, H, H_kv, D, max_len):
     return int(load_library().attn_decode_workspace_bytes(int(B), int(H), int(H_kv), int(D), int(max_len)))
 
@@ -314,3 +387,11 @@ def backward(q, k, v, o, dO, lse, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=
     delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode, cu_seqlens, None, max_seqlen, stream)
     return dq, dk, dv, delta
+
+
+def rope_table(n_pos, D, base=10000.0, device="cuda", stream=None):
+    """Returns a new [n_pos, D/2, 2] fp32 device table of (cos, sin) for RoPE."""
+    torch = _torch()
+    tab = torch.empty((n_pos, D // 2, 2), dtype=torch.float32, device=device)
+    attn_rope_table(tab, base, stream)
+    return tab

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libcausal_attn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip"]
+SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_rope.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

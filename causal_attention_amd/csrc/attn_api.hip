@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 130;  // 1.30: grouped-query and decode entry points, fp16 inputs
+constexpr int kAbiVersion = 140;  // 1.40: grouped-query, decode and RoPE entry points, fp16 inputs
 
 int check_common(int B, int H, int S, int D, int dtype) {
   if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_DTYPE;
@@ -43,6 +43,15 @@ int check_heads(int H, int H_kv) {
 
 int check_scale(float scale) {
   if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_SCALE;
+  return ATTN_OK;
+}
+
+// The RoPE table must cover every position: sequence indices (causal) or
+// offsets inside the longest document.
+int check_rope(const float *tab, int n_pos, int S, int mask_mode, int max_seqlen) {
+  if (tab == nullptr) return ATTN_ERR_ROPE;
+  const int need = mask_mode == ATTN_MASK_DOC_CAUSAL ? max_seqlen : S;
+  if (n_pos < need) return ATTN_ERR_ROPE;
   return ATTN_OK;
 }
 
@@ -86,6 +95,7 @@ const char *attn_status_string(int status) {
     case ATTN_ERR_SCALE: return "scale must be finite and > 0";
     case ATTN_ERR_HEADS: return "H_kv must divide H (1 <= H_kv <= H)";
     case ATTN_ERR_WORKSPACE: return "workspace NULL or smaller than attn_decode_workspace_bytes()";
+    case ATTN_ERR_ROPE: return "RoPE table NULL or shorter than the positions (S, or max_seqlen for documents), or base not finite and > 0";
     default: return "unknown status";
   }
 }
@@ -167,17 +177,23 @@ int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dO, con
   return to_status(attn::launch_bwd_dq(a));
 }
 
-int attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o, const void *dO, const float *lse,
-                 float *dq, float *dk, float *dv, float *delta, int B, int H, int H_kv, int S, int D, float scale,
-                 int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype, void *stream) {
+// Whole backward (optionally with RoPE gradients turned back in the dQ and dK
+// epilogues): argument checks, then the kernels on one stream.
+static int bwd_all(const void *q, const void *k, const void *v, const float *o, const void *dO, const float *lse,
+                   float *dq, float *dk, float *dv, float *delta, bool with_rope, const float *rope, int rope_npos,
+                   int B, int H, int H_kv, int S, int D, float scale, int mask_mode, const int32_t *cu_seqlens,
+                   int n_seqs, int max_seqlen, int dtype, void *stream) {
   int st = check_common(B, H, S, D, dtype);
   if (st != ATTN_OK) return st;
   if ((st = check_heads(H, H_kv)) != ATTN_OK) return st;
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL;
   if ((st = check_mask(B, H, S, mask_mode, cu_seqlens, n_seqs, max_seqlen)) != ATTN_OK) return st;
   if ((st = check_scale(scale)) != ATTN_OK) return st;
+  if (with_rope && (st = check_rope(rope, rope_npos, S, mask_mode, max_seqlen)) != ATTN_OK) return st;
   attn::Args a = make_args(B, H, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
   a.H_kv = H_kv;
+  a.rope = rope;
+  a.rope_npos = rope_npos;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -192,8 +208,7 @@ int attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o, co
   hipError_t e;
   if (a.half()) {
     // 16-bit inputs: dQ computes Delta on the way (bitwise equal to the
-    // preprocess kernel's)
-    // and writes it for dK/dV: one pass over O and dO fewer.
+    // preprocess kernel's) and writes it for dK/dV: one pass over O and dO fewer.
     e = attn::launch_bwd_dq_delta(a);
     if (e == hipSuccess) e = attn::launch_bwd_dkdv(a);
   } else {
@@ -204,11 +219,78 @@ int attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o, co
   return to_status(e);
 }
 
+int attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o, const void *dO, const float *lse,
+                 float *dq, float *dk, float *dv, float *delta, int B, int H, int H_kv, int S, int D, float scale,
+                 int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype, void *stream) {
+  return bwd_all(q, k, v, o, dO, lse, dq, dk, dv, delta, false, nullptr, 0, B, H, H_kv, S, D, scale, mask_mode,
+                 cu_seqlens, n_seqs, max_seqlen, dtype, stream);
+}
+
 int attn_bwd(const void *q, const void *k, const void *v, const float *o, const void *dO, const float *lse,
              float *dq, float *dk, float *dv, float *delta, int B, int H, int S, int D, float scale, int mask_mode,
              const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype, void *stream) {
   return attn_bwd_gqa(q, k, v, o, dO, lse, dq, dk, dv, delta, B, H, H, S, D, scale, mask_mode, cu_seqlens, n_seqs,
                       max_seqlen, dtype, stream);
+}
+
+int attn_rope_table(float *tab, int n_pos, int D, float base, void *stream) {
+  if (D != 32 && D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (n_pos < 1 || (int64_t)n_pos * D >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+  if (tab == nullptr) return ATTN_ERR_NULL;
+  if (!std::isfinite(base) || !(base > 0.f)) return ATTN_ERR_ROPE;
+  return to_status(attn::launch_rope_table(tab, n_pos, D, (double)base, static_cast<hipStream_t>(stream)));
+}
+
+int attn_rope(const void *q, const void *k, void *q_rot, void *k_rot, const float *tab, int n_pos, int B, int H,
+              int H_kv, int S, int D, int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype,
+              void *stream) {
+  int st = check_common(B, H, S, D, dtype);
+  if (st != ATTN_OK) return st;
+  if ((st = check_heads(H, H_kv)) != ATTN_OK) return st;
+  if (!q || !k || !q_rot || !k_rot) return ATTN_ERR_NULL;
+  if ((st = check_mask(B, H, S, mask_mode, cu_seqlens, n_seqs, max_seqlen)) != ATTN_OK) return st;
+  if ((st = check_rope(tab, n_pos, S, mask_mode, max_seqlen)) != ATTN_OK) return st;
+  attn::Args a = make_args(B, H, S, D, 1.f, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
+  a.H_kv = H_kv;
+  a.q = q;
+  a.k = k;
+  a.rope = tab;
+  a.rope_npos = n_pos;
+  return to_status(attn::launch_rope(a, q_rot, k_rot));
+}
+
+int attn_fwd_rope(const void *q, const void *k, const void *v, void *q_rot, void *k_rot, float *o, float *lse,
+                  const float *tab, int n_pos, int B, int H, int H_kv, int S, int D, float scale, int mask_mode,
+                  const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype, void *stream) {
+  int st = check_common(B, H, S, D, dtype);
+  if (st != ATTN_OK) return st;
+  if ((st = check_heads(H, H_kv)) != ATTN_OK) return st;
+  if (!q || !k || !v || !q_rot || !k_rot || !o) return ATTN_ERR_NULL;
+  if ((st = check_mask(B, H, S, mask_mode, cu_seqlens, n_seqs, max_seqlen)) != ATTN_OK) return st;
+  if ((st = check_scale(scale)) != ATTN_OK) return st;
+  if ((st = check_rope(tab, n_pos, S, mask_mode, max_seqlen)) != ATTN_OK) return st;
+  attn::Args a = make_args(B, H, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
+  a.H_kv = H_kv;
+  a.q = q;
+  a.k = k;
+  a.rope = tab;
+  a.rope_npos = n_pos;
+  hipError_t e = attn::launch_rope(a, q_rot, k_rot);
+  if (e != hipSuccess) return ATTN_ERR_HIP;
+  a.q = q_rot;
+  a.k = k_rot;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  return to_status(attn::launch_fwd(a));
+}
+
+int attn_bwd_rope(const void *q_rot, const void *k_rot, const void *v, const float *o, const void *dO,
+                  const float *lse, float *dq, float *dk, float *dv, float *delta, const float *tab, int n_pos, int B,
+                  int H, int H_kv, int S, int D, float scale, int mask_mode, const int32_t *cu_seqlens, int n_seqs,
+                  int max_seqlen, int dtype, void *stream) {
+  return bwd_all(q_rot, k_rot, v, o, dO, lse, dq, dk, dv, delta, true, tab, n_pos, B, H, H_kv, S, D, scale, mask_mode,
+                 cu_seqlens, n_seqs, max_seqlen, dtype, stream);
 }
 
 size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int D, int max_len) {

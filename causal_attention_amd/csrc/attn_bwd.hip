@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, float *__restrict__ dk,
     float *__restrict__ dv, int S, float c2, float scale, const int32_t *__restrict__ cu, int ntiles, int n_seqs,
-    int H, int G) {
+    int H, int G, const float *__restrict__ rope, int rope_npos) {
   constexpr int NW = 4;
   constexpr int NT = NW * kWaveSize;
   constexpr int BN = NW * 32;  // keys per workgroup
@@ -237,6 +237,9 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   if (!wave_active) return;
   const GBuf gdk(dk + base, (uint32_t)(t.r_end * D * sizeof(float)));
   const GBuf gdv(dv + base, (uint32_t)(t.r_end * D * sizeof(float)));
+  // RoPE: this key's table row (keys past the tile end are not stored)
+  const float *rrow =
+      rope == nullptr ? nullptr : rope + (size_t)min(min(key, t.r_end - 1) - t.seg_start, rope_npos - 1) * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -247,6 +250,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
         a4[i] = dkacc[db][4 * g + i] * scale;
         b4[i] = dvacc[db][4 * g + i];
       }
+      if (rope != nullptr) rope_back(a4, *reinterpret_cast<const f32x4 *>(rrow + db * 32 + 8 * g + 4 * hh));
       const uint32_t off = (uint32_t)(key * D + db * 32 + 8 * g + 4 * hh) * sizeof(float);
       gdk.store16(a4, off);
       gdv.store16(b4, off);
@@ -276,7 +280,8 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, const float *__restrict__ o,
     float *__restrict__ delta_out, float *__restrict__ dq, int S, float c2, float scale,
-    const int32_t *__restrict__ cu, int ntiles, int n_seqs, int H, int G) {
+    const int32_t *__restrict__ cu, int ntiles, int n_seqs, int H, int G, const float *__restrict__ rope,
+    int rope_npos) {
   constexpr int NW = 4;
   constexpr int NT = NW * kWaveSize;
   constexpr int BM = NW * 32;
@@ -422,6 +427,9 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
 
   if (!wave_active) return;
   const GBuf gdq(dq + base, (uint32_t)(t.r_end * D * sizeof(float)));
+  // RoPE: this query's table row (queries past the tile end are not stored)
+  const float *rrow =
+      rope == nullptr ? nullptr : rope + (size_t)min(min(qi, t.r_end - 1) - t.seg_start, rope_npos - 1) * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -429,6 +437,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
       f32x4 a4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) a4[i] = dqacc[db][4 * g + i] * scale;
+      if (rope != nullptr) rope_back(a4, *reinterpret_cast<const f32x4 *>(rrow + db * 32 + 8 * g + 4 * hh));
       gdq.store16(a4, (uint32_t)(qi * D + db * 32 + 8 * g + 4 * hh) * sizeof(float));
     }
   }
@@ -496,7 +505,7 @@ static hipError_t launch_dkdv_t(const Args &a) {
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, BMQ, MINB, DOC>), grid, dim3(256), 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
                      static_cast<const T *>(a.dO), a.lse_in, a.delta_in, a.dk, a.dv, a.S, c2, a.scale,
-                     a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv);
+                     a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv, a.rope, a.rope_npos);
   return hipGetLastError();
 }
 
@@ -518,7 +527,7 @@ static hipError_t launch_dq_t(const Args &a) {
   hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, MINB, DOC, FUSE_DELTA>), grid, dim3(256), 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
                      static_cast<const T *>(a.dO), a.lse_in, a.delta_in, a.o_in, a.delta, a.dq, a.S, c2, a.scale,
-                     a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv);
+                     a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv, a.rope, a.rope_npos);
   return hipGetLastError();
 }
 

@@ -573,6 +573,18 @@ struct RowTile {
 // b * H + h (queries) and b * (H / G) + h / G (keys and values).
 __device__ __forceinline__ int kv_head_of(int qhead, int H, int G) { return (qhead / H) * (H / G) + (qhead % H) / G; }
 
+// RoPE gradient: turn two interleaved pairs (a[0], a[1]) and (a[2], a[3])
+// back by their angles, cs = (cos, sin) of the first pair, then of the
+// second: (x0, x1) -> (x0 c + x1 s, x1 c - x0 s), the transpose of the
+// forward rotation (x0 c - x1 s, x0 s + x1 c).
+__device__ __forceinline__ void rope_back(f32x4 &a, const f32x4 cs) {
+  const float x0 = a[0], x1 = a[1], x2 = a[2], x3 = a[3];
+  a[0] = x0 * cs[0] + x1 * cs[1];
+  a[1] = x1 * cs[0] - x0 * cs[1];
+  a[2] = x2 * cs[2] + x3 * cs[3];
+  a[3] = x3 * cs[2] - x2 * cs[3];
+}
+
 // Tile schedule.  Workgroups are dealt to the 8 XCDs round-robin (block b
 // runs on XCD b % 8) and, within an XCD, to its 32 CUs round-robin (local
 // index l = b / 8 on CU l % 32), as measured on MI355X; when every workgroup

@@ -19,6 +19,8 @@ struct Args {
   int n_seqs, max_seqlen;
   int dtype;                // input dtype: ATTN_DTYPE_F32, _BF16 or _F16 (attn_api.h)
   bool half() const { return dtype != 0; }  // 16-bit inputs
+  const float *rope;        // RoPE table [rope_npos][D/2][2] (cos, sin), or NULL: dQ and dK
+  int rope_npos;            // epilogues turn the gradients back by the row's angles
   hipStream_t stream;
 };
 
@@ -43,5 +45,8 @@ hipError_t launch_bwd_dkdv(const Args &a);
 hipError_t launch_bwd_dq(const Args &a);
 // 16-bit inputs only: dQ that also computes Delta from O and dO (written to a.delta)
 hipError_t launch_bwd_dq_delta(const Args &a);
+// RoPE: the cos/sin table, and the rotation of a.q, a.k into q_rot, k_rot (table a.rope)
+hipError_t launch_rope_table(float *tab, int n_pos, int D, double base, hipStream_t stream);
+hipError_t launch_rope(const Args &a, void *q_rot, void *k_rot);
 
 }  // namespace attn

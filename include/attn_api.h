@@ -75,7 +75,9 @@ typedef enum attn_status {
   ATTN_ERR_UNIMPLEMENTED = -8, /* valid request this build does not implement      */
   ATTN_ERR_SCALE = -9,         /* scale not finite or not > 0                      */
   ATTN_ERR_HEADS = -10,        /* H_kv not a divisor of H (grouped-query calls)    */
-  ATTN_ERR_WORKSPACE = -11     /* decode workspace missing or too small            */
+  ATTN_ERR_WORKSPACE = -11,    /* decode workspace missing or too small            */
+  ATTN_ERR_ROPE = -12          /* RoPE table NULL or shorter than the positions,
+                                  or base not finite and > 0                       */
 } attn_status;
 
 enum { ATTN_MASK_CAUSAL = 0, ATTN_MASK_DOC_CAUSAL = 1 };
@@ -185,6 +187,66 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
                 void *workspace, size_t workspace_bytes,
                 int B, int H, int H_kv, int S_max, int D, float scale, int max_len,
                 int dtype, void *stream);
+
+/*
+ * Rotary position embedding (RoPE) of queries and keys: RoFormer (Su et al.
+ * 2021, cited by ARK, whose model applies it from precomputed sine/cosine
+ * tables: ARK, "Inference architecture (EKO)" and the model table's
+ * "Positional encoding" row; Forge, "Architecture": attention with GQA and
+ * RoPE).  Pair i = (x[2i], x[2i+1]) of a row at position p turns by the angle
+ * p * theta_i, theta_i = base^(-2i/D):
+ *
+ *   y[2i]   = x[2i] cos(p theta_i) - x[2i+1] sin(p theta_i)
+ *   y[2i+1] = x[2i] sin(p theta_i) + x[2i+1] cos(p theta_i)
+ *
+ * Positions are sequence indices 0 .. S-1 (ATTN_MASK_CAUSAL) or offsets from
+ * the start of the row's document (ATTN_MASK_DOC_CAUSAL: every document is
+ * its own sequence).  Values are not rotated.
+ *
+ * attn_rope_table: fills tab, DEVICE float32 [n_pos, D/2, 2], with
+ *   tab[p][i] = (cos(p theta_i), sin(p theta_i)), angles computed in double
+ *   precision.  A model builds it once and passes it to every call below.
+ *   Errors: ATTN_ERR_NULL, ATTN_ERR_HEAD_DIM, ATTN_ERR_SHAPE (n_pos < 1 or
+ *   n_pos * D >= 2^31), ATTN_ERR_ROPE (base not finite and > 0).
+ *
+ * attn_rope: q_rot = rotate(q) [B, H, S, D], k_rot = rotate(k) [B, H_kv, S, D],
+ *   computed in fp32 and stored in the input dtype (16-bit: round to nearest
+ *   even).  q_rot may equal q and k_rot may equal k (in place); other
+ *   overlaps are undefined.
+ *
+ * attn_fwd_rope: attn_rope, then attn_fwd_gqa on q_rot and k_rot.  The caller
+ *   keeps q_rot and k_rot (caller-owned, [B, H, S, D] and [B, H_kv, S, D] in
+ *   the input dtype) for the backward, as saved activations.
+ *
+ * attn_bwd_rope: attn_bwd_gqa on q_rot, k_rot (as written by attn_fwd_rope),
+ *   with dq and dk turned back by the opposite angles in the kernels'
+ *   epilogues: dq, dk are gradients with respect to the UNROTATED q and k
+ *   (the rotation's derivative; the dtype rounding of q_rot, k_rot passes the
+ *   gradient unchanged).  dv, delta as attn_bwd_gqa.
+ *
+ * tab must hold n_pos >= S positions (causal) or n_pos >= max_seqlen (packed
+ * documents), else ATTN_ERR_ROPE.  Other arguments, layouts, ownership and
+ * errors as attn_fwd_gqa / attn_bwd_gqa.
+ */
+int attn_rope_table(float *tab, int n_pos, int D, float base, void *stream);
+
+int attn_rope(const void *q, const void *k, void *q_rot, void *k_rot,
+              const float *tab, int n_pos, int B, int H, int H_kv, int S, int D,
+              int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen,
+              int dtype, void *stream);
+
+int attn_fwd_rope(const void *q, const void *k, const void *v, void *q_rot, void *k_rot,
+                  float *o, float *lse, const float *tab, int n_pos,
+                  int B, int H, int H_kv, int S, int D, float scale, int mask_mode,
+                  const int32_t *cu_seqlens, int n_seqs, int max_seqlen,
+                  int dtype, void *stream);
+
+int attn_bwd_rope(const void *q_rot, const void *k_rot, const void *v, const float *o,
+                  const void *dO, const float *lse, float *dq, float *dk, float *dv,
+                  float *delta, const float *tab, int n_pos,
+                  int B, int H, int H_kv, int S, int D, float scale, int mask_mode,
+                  const int32_t *cu_seqlens, int n_seqs, int max_seqlen,
+                  int dtype, void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *attn_status_string(int status);

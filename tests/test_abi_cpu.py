@@ -31,7 +31,7 @@ def test_header_status_codes_match_binding():
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 130
+    assert lib.attn_abi_version() == 140
 
 
 def test_status_strings(lib):
@@ -162,6 +162,62 @@ def test_decode_workspace_size(lib):
     assert _decode(lib, B=64, H=64, H_kv=64, S_max=32, max_len=32, ws=None, wsb=0) in (0, -7)
 
 
+def _rope(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, qr=FAKE, kr=FAKE, tab=FAKE, npos=64, B=1, H=4, H_kv=2, S=64, D=64, mask=0, cu=None,
+             n=0, mx=0, dtype=1, stream=None)
+    a.update(kw)
+    return lib.attn_rope(a["q"], a["k"], a["qr"], a["kr"], a["tab"], a["npos"], a["B"], a["H"], a["H_kv"], a["S"],
+                         a["D"], a["mask"], a["cu"], a["n"], a["mx"], a["dtype"], a["stream"])
+
+
+def _fwd_rope(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, qr=FAKE, kr=FAKE, o=FAKE, lse=FAKE, tab=FAKE, npos=64, B=1, H=4, H_kv=2, S=64,
+             D=64, scale=0.125, mask=0, cu=None, n=0, mx=0, dtype=1, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_rope(a["q"], a["k"], a["v"], a["qr"], a["kr"], a["o"], a["lse"], a["tab"], a["npos"], a["B"],
+                             a["H"], a["H_kv"], a["S"], a["D"], a["scale"], a["mask"], a["cu"], a["n"], a["mx"],
+                             a["dtype"], a["stream"])
+
+
+def _bwd_rope(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, delta=FAKE, tab=FAKE,
+             npos=64, B=1, H=4, H_kv=2, S=64, D=64, scale=0.125, mask=0, cu=None, n=0, mx=0, dtype=1, stream=None)
+    a.update(kw)
+    return lib.attn_bwd_rope(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                             a["delta"], a["tab"], a["npos"], a["B"], a["H"], a["H_kv"], a["S"], a["D"], a["scale"],
+                             a["mask"], a["cu"], a["n"], a["mx"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tab=None), -12), (dict(npos=63), -12), (dict(npos=0), -12),
+    (dict(mask=1, cu=FAKE, n=2, mx=40, npos=39), -12),
+    (dict(q=None), -1), (dict(D=48), -3), (dict(dtype=3), -4), (dict(H_kv=3), -10),
+    (dict(mask=2), -5), (dict(mask=1, cu=FAKE, n=2, mx=40, B=2), -6), (dict(S=0), -2),
+])
+def test_rope_entry_points_reject_invalid_arguments(lib, kw, code):
+    assert _rope(lib, **kw) == code
+    assert _fwd_rope(lib, **kw) == code
+    assert _bwd_rope(lib, **kw) == code
+
+
+def test_rope_entry_points_check_their_own_pointers(lib):
+    assert _rope(lib, qr=None) == -1 and _rope(lib, kr=None) == -1
+    assert _fwd_rope(lib, kr=None) == -1 and _fwd_rope(lib, o=None) == -1 and _fwd_rope(lib, v=None) == -1
+    assert _bwd_rope(lib, dk=None) == -1 and _bwd_rope(lib, delta=None) == -1
+    assert _fwd_rope(lib, scale=float("nan")) == -9 and _bwd_rope(lib, scale=-1.0) == -9
+    # packed documents need positions up to the longest document only
+    assert _rope(lib, mask=1, cu=FAKE, n=2, mx=40, npos=40) in (0, -7)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 64, 64, 10000.0), -1), ((FAKE, 0, 64, 10000.0), -2), ((FAKE, 64, 48, 10000.0), -3),
+    ((FAKE, 64, 64, 0.0), -12), ((FAKE, 64, 64, -2.0), -12), ((FAKE, 64, 64, float("inf")), -12),
+    ((FAKE, 64, 64, float("nan")), -12), ((FAKE, 1 << 25, 128, 10000.0), -2),
+])
+def test_rope_table_rejects_invalid_arguments(lib, args, code):
+    assert lib.attn_rope_table(*args, None) == code
+
+
 def test_no_device_reports_hip_error(lib):
     """A valid call with no GPU present fails with ATTN_ERR_HIP instead of aborting."""
     torch = pytest.importorskip("torch")
@@ -171,6 +227,8 @@ def test_no_device_reports_hip_error(lib):
     assert _decode(lib) == -7
     assert _fwd_gqa(lib, 2) == -7
     assert _bwd_gqa(lib, 1) == -7
+    assert _rope(lib) == -7 and _fwd_rope(lib) == -7 and _bwd_rope(lib) == -7
+    assert lib.attn_rope_table(FAKE, 64, 64, 10000.0, None) == -7
 
 
 def test_binding_refuses_host_tensors():

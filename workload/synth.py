@@ -47,6 +47,7 @@ class AttnConfig:
     doc_len_range: tuple | None = None  # (lo, hi) inclusive, packed mode only
     doc_seed: int = 500
     H_kv: int | None = None  # key/value heads (grouped-query attention); None = H
+    rope: bool = False       # rotary position embedding of q and k before attention
     note: str = field(default="", compare=False)
 
     @property
@@ -77,6 +78,10 @@ CONFIGS = {
     # context-1024 shape with 4 key/value heads for the 16 query heads.
     "lm237m_ctx1024_gqa4": AttnConfig("lm237m_ctx1024_gqa4", B=8, H=16, S=1024, D=64, dtype="bf16", H_kv=4,
                                       note="237M-class layer with grouped-query attention"),
+    # The same layer with rotary position embedding of q and k (ARK, model
+    # table: RoPE; Forge, "Architecture": attention with RoPE), base 10000.
+    "lm237m_ctx1024_rope": AttnConfig("lm237m_ctx1024_rope", B=8, H=16, S=1024, D=64, dtype="bf16", rope=True,
+                                      note="237M-class layer with RoPE on q and k"),
 }
 
 
