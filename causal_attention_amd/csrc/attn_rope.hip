@@ -13,9 +13,9 @@
 //    HBM-bound pass: attention tiles reach LDS by direct global->LDS copies
 //    that cannot transform data, and each key tile is read by many query
 //    workgroups, so rotating once beats rotating on every load; q_rot and
-//    k_rot are what the backward reads.  One thread owns 8 consecutive
-//    elements (4 pairs) of a row: a 16-byte load for 16-bit inputs, and the
-//    row's 32 bytes of table, which stay in L2 across heads.
+//    k_rot are what the backward reads.  A thread owns 8 consecutive elements
+//    (4 pairs) of one position in four heads: its 32 bytes of table are read
+//    once for the four 16-byte (16-bit inputs) loads.
 //  * The backward turns dQ and dK back in the epilogues of the dQ and dK/dV
 //    kernels (attn_bwd.hip), where every lane holds both elements of its pairs.
 #include "attn_device.h"
@@ -72,22 +72,24 @@ template <> struct Row8<float> {
   }
 };
 
-// Rows 0 .. q_rows-1 are q's (B*H*S of them), the rest k's (B*H_kv*S); row r
-// of either sits at sequence index r % S.  q_rot may be q and k_rot may be k
-// (each thread reads its elements before writing them), so no restrict.
-template <typename T, int D, bool DOC>
+// Grid (flat): position block fastest, then batch entry, then group of HPT heads.  A thread owns one
+// 8-element chunk of one position and rotates it in HPT heads (query heads
+// 0 .. H-1, then key heads H .. H+H_kv-1): the chunk's table values are read
+// once and the HPT loads are in flight together.  q_rot may be q and k_rot may
+// be k (each thread reads its elements before writing them), so no restrict.
+template <typename T, int D, bool DOC, int HPT>
 __global__ __launch_bounds__(256) void attn_rope_kernel(const T *q, const T *k, T *qr, T *kr,
-                                                        const float *__restrict__ tab, int n_pos, int64_t q_rows,
-                                                        int64_t rows, int S, const int32_t *__restrict__ cu,
+                                                        const float *__restrict__ tab, int n_pos, int H, int Hkv,
+                                                        int B, int S, int nsb, const int32_t *__restrict__ cu,
                                                         int n_seqs) {
   constexpr int CPR = D / 8;  // 8-element chunks per row
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= rows * CPR) return;
-  int64_t row = idx / CPR;
-  const int ch = (int)(idx % CPR);
-  const bool isq = row < q_rows;
-  if (!isq) row -= q_rows;
-  const int s = (int)(row % S);
+  const int pb = blockIdx.x % nsb;
+  const int b = (blockIdx.x / nsb) % B;
+  const int h0 = (int)(blockIdx.x / nsb / B) * HPT;
+  const int idx = pb * 256 + threadIdx.x;
+  if (idx >= S * CPR) return;
+  const int s = idx / CPR;
+  const int ch = idx % CPR;
   int pos = s;
   if constexpr (DOC) {  // the document holding s: cu[lo] <= s < cu[hi]
     int lo = 0, hi = n_seqs;
@@ -100,20 +102,29 @@ __global__ __launch_bounds__(256) void attn_rope_kernel(const T *q, const T *k, 
     }
     pos = min(s - cu[lo], n_pos - 1);  // a document past max_seqlen breaks the call's contract:
   }                                    // keep its reads inside the table
-  const size_t off = (size_t)row * D + ch * 8;
-  float x[8];
-  Row8<T>::load((isq ? q : k) + off, x);
   const f32x4 *t4 = reinterpret_cast<const f32x4 *>(tab + (size_t)pos * D + ch * 8);
   const f32x4 cs0 = t4[0], cs1 = t4[1];  // (cos, sin) of this chunk's four pairs
-  float y[8];
+
+  auto row = [&](int h) -> size_t {  // element offset of this chunk in head h's row s
+    return h < H ? ((size_t)(b * H + h) * S + s) * D + ch * 8 : ((size_t)(b * Hkv + h - H) * S + s) * D + ch * 8;
+  };
+  float x[HPT][8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float c = j < 2 ? cs0[2 * j] : cs1[2 * j - 4];
-    const float sn = j < 2 ? cs0[2 * j + 1] : cs1[2 * j - 3];
-    y[2 * j] = x[2 * j] * c - x[2 * j + 1] * sn;
-    y[2 * j + 1] = x[2 * j] * sn + x[2 * j + 1] * c;
+  for (int j = 0; j < HPT; ++j)
+    if (h0 + j < H + Hkv) Row8<T>::load((h0 + j < H ? q : k) + row(h0 + j), x[j]);
+#pragma unroll
+  for (int j = 0; j < HPT; ++j) {
+    if (h0 + j >= H + Hkv) break;
+    float y[8];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float c = p < 2 ? cs0[2 * p] : cs1[2 * p - 4];
+      const float sn = p < 2 ? cs0[2 * p + 1] : cs1[2 * p - 3];
+      y[2 * p] = x[j][2 * p] * c - x[j][2 * p + 1] * sn;
+      y[2 * p + 1] = x[j][2 * p] * sn + x[j][2 * p + 1] * c;
+    }
+    Row8<T>::store((h0 + j < H ? qr : kr) + row(h0 + j), y);
   }
-  Row8<T>::store((isq ? qr : kr) + off, y);
 }
 
 hipError_t launch_rope_table(float *tab, int n_pos, int D, double base, hipStream_t stream) {
@@ -126,20 +137,19 @@ hipError_t launch_rope_table(float *tab, int n_pos, int D, double base, hipStrea
 
 template <typename T, int D>
 static hipError_t launch_rope_t(const Args &a, void *q_rot, void *k_rot) {
-  const int64_t q_rows = (int64_t)a.B * a.H * a.S;
-  const int64_t rows = q_rows + (int64_t)a.B * a.H_kv * a.S;
-  const int64_t threads = rows * (D / 8);
-  const dim3 grid((unsigned)((threads + 255) / 256));
+  constexpr int HPT = 4;
+  const int nsb = (a.S * (D / 8) + 255) / 256;
+  const dim3 grid((unsigned)nsb * a.B * ((a.H + a.H_kv + HPT - 1) / HPT));
   const T *q = static_cast<const T *>(a.q);
   const T *k = static_cast<const T *>(a.k);
   T *qr = static_cast<T *>(q_rot);
   T *kr = static_cast<T *>(k_rot);
   if (a.doc)
-    hipLaunchKernelGGL((attn_rope_kernel<T, D, true>), grid, dim3(256), 0, a.stream, q, k, qr, kr, a.rope, a.rope_npos, q_rows,
-                       rows, a.S, a.cu_seqlens, a.n_seqs);
+    hipLaunchKernelGGL((attn_rope_kernel<T, D, true, HPT>), grid, dim3(256), 0, a.stream, q, k, qr, kr, a.rope,
+                       a.rope_npos, a.H, a.H_kv, a.B, a.S, nsb, a.cu_seqlens, a.n_seqs);
   else
-    hipLaunchKernelGGL((attn_rope_kernel<T, D, false>), grid, dim3(256), 0, a.stream, q, k, qr, kr, a.rope, a.rope_npos, q_rows,
-                       rows, a.S, a.cu_seqlens, a.n_seqs);
+    hipLaunchKernelGGL((attn_rope_kernel<T, D, false, HPT>), grid, dim3(256), 0, a.stream, q, k, qr, kr, a.rope,
+                       a.rope_npos, a.H, a.H_kv, a.B, a.S, nsb, a.cu_seqlens, a.n_seqs);
   return hipGetLastError();
 }
 
