@@ -12,7 +12,7 @@ accounting), divided by the measured time.  One JSON line is printed.
 Besides the headline workload the line carries:
   by_workload   the same measurement at the other full-size workloads
                 (context 512, 8192, packed documents, grouped-query heads,
-                RoPE on q and k),
+                RoPE on q and k, bf16 outputs),
                 fewer steps, and one decode step against a full 8192-token
                 K/V cache (time, GB/s against HBM peak);
   kernels       per-kernel mean duration from HIP events on the launch stream;
@@ -42,7 +42,7 @@ PEAK_FP32_TFLOPS = 157.3    # fp32 matrix/vector peak used for fp32 inputs
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "lm237m_ctx1024"
 SEEDS = {"tiny_f32": 1, "lm12m_ctx512": 2, "lm237m_ctx1024": 3, "long_ctx8192": 4, "packed_docs8192": 5,
-         "lm237m_ctx1024_gqa4": 6, "lm237m_ctx1024_rope": 7}
+         "lm237m_ctx1024_gqa4": 6, "lm237m_ctx1024_rope": 7, "lm237m_ctx1024_out16": 8}
 # algorithmic flops per allowed pair, per kernel (times D)
 KERNEL_FLOPS_PER_PAIR = {"fwd": 4, "dkdv": 8, "dq": 2}
 KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip"]
@@ -88,9 +88,10 @@ class Workload:
         B, H, S, D = x["B"], x["H"], x["S"], x["D"]
         self.grouped = self.k.shape[1] != H
         f32 = dict(dtype=torch.float32, device="cuda")
-        self.o = torch.empty((B, H, S, D), **f32)
+        out = dict(dtype=dt if cfg.out16 else torch.float32, device="cuda")
+        self.o = torch.empty((B, H, S, D), **out)
         self.dq = torch.empty_like(self.o)
-        self.dk = torch.empty(tuple(self.k.shape), **f32)
+        self.dk = torch.empty(tuple(self.k.shape), **out)
         self.dv = torch.empty_like(self.dk)
         self.lse = torch.empty((B, H, S), **f32)
         self.delta = torch.empty((B, H, S), **f32)
@@ -112,14 +113,19 @@ class Workload:
             self.k_rot = torch.empty_like(self.k)
 
     def fwd(self):
-        if self.cfg.rope:
+        if self.cfg.out16:
+            self.ca.attn_fwd_ex(self.q, self.k, self.v, self.o, self.lse, self.x["scale"], **self.sargs)
+        elif self.cfg.rope:
             self.ca.attn_fwd_rope(self.q, self.k, self.v, self.q_rot, self.k_rot, self.o, self.lse, self.tab,
                                   self.x["scale"], **self.sargs)
         else:
             self.ca.attn_fwd(self.q, self.k, self.v, self.o, self.lse, self.x["scale"], **self.sargs)
 
     def bwd(self):
-        if self.cfg.rope:
+        if self.cfg.out16:
+            self.ca.attn_bwd_ex(self.q, self.k, self.v, self.o, self.do, self.lse, self.dq, self.dk, self.dv,
+                                self.delta, self.x["scale"], **self.sargs)
+        elif self.cfg.rope:
             self.ca.attn_bwd_rope(self.q_rot, self.k_rot, self.v, self.o, self.do, self.lse, self.dq, self.dk,
                                   self.dv, self.delta, self.tab, self.x["scale"], **self.sargs)
         else:
@@ -162,7 +168,7 @@ class Workload:
         if self.cfg.rope:  # the rotation pass alone (it is part of the forward above)
             stages.append(("rope", lambda: self.ca.attn_rope(self.q, self.k, self.q_rot, self.k_rot, self.tab,
                                                              stream=self.stream)))
-        elif not self.grouped:  # the staged entry points take plain multi-head inputs
+        elif not self.grouped and not self.cfg.out16:  # the staged entry points: fp32 outputs, plain heads
             stages += [("pre", self.pre), ("dkdv", self.dkdv), ("dq", self.dqk)]
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(reps)]
         for _ in range(3):
@@ -419,7 +425,7 @@ def main():
     by_workload = {a.workload: summary}
     if not a.no_others:
         for name in ("lm12m_ctx512", "long_ctx8192", "packed_docs8192", "lm237m_ctx1024_gqa4",
-                     "lm237m_ctx1024_rope", "lm237m_ctx1024"):
+                     "lm237m_ctx1024_rope", "lm237m_ctx1024_out16", "lm237m_ctx1024"):
             if name == a.workload:
                 continue
             _, _, _, s = measure(name, max(10, a.steps // 4), max(3, a.warmup // 2), max(10, a.kernel_reps // 2))
@@ -453,7 +459,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "S": cfg.S, "D": cfg.D,
                    "mask": "packed_documents" if cfg.mask_mode else "causal",
-                   "outputs": "fp32", "parallelism": "single GPU"},
+                   "outputs": cfg.dtype if cfg.out16 else "fp32", "parallelism": "single GPU"},
         "pct_peak": summary["pct_peak"],
         "fwd_tflops": summary["fwd_tflops"],
         "bwd_tflops": summary["bwd_tflops"],

@@ -12,14 +12,17 @@ from ._binding import (  # noqa: F401
     ATTN_MASK_CAUSAL,
     ATTN_MASK_DOC_CAUSAL,
     AttnError,
+    AttnParams,
     LIB_PATH,
     attn_bwd,
     attn_bwd_dkdv,
+    attn_bwd_ex,
     attn_bwd_dq,
     attn_bwd_preprocess,
     attn_bwd_rope,
     attn_decode,
     attn_fwd,
+    attn_fwd_ex,
     attn_fwd_rope,
     attn_rope,
     attn_rope_table,

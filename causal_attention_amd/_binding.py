@@ -41,6 +41,15 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
 
+
+class AttnParams(ctypes.Structure):
+    """attn_params of include/attn_api.h, field for field."""
+    _fields_ = [("q", _P), ("k", _P), ("v", _P), ("dO", _P), ("o", _P), ("lse", _P), ("dq", _P), ("dk", _P),
+                ("dv", _P), ("delta", _P), ("B", _I), ("H", _I), ("H_kv", _I), ("S", _I), ("D", _I),
+                ("scale", _F), ("mask_mode", _I), ("cu_seqlens", _P), ("n_seqs", _I), ("max_seqlen", _I),
+                ("dtype", _I), ("out_dtype", _I), ("rope_table", _P), ("rope_npos", _I), ("q_rot", _P),
+                ("k_rot", _P)]
+
 # argtypes of every exported function, in the header's order
 SIGNATURES = {
     "attn_fwd": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
@@ -57,6 +66,8 @@ SIGNATURES = {
     "attn_fwd_rope": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
     "attn_bwd_rope": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _I, _I,
                       _I, _P],
+    "attn_fwd_ex": [ctypes.POINTER(AttnParams), _P],
+    "attn_bwd_ex": [ctypes.POINTER(AttnParams), _P],
     "attn_status_string": [_I],
     "attn_abi_version": [],
 }
@@ -321,6 +332,58 @@ def attn_bwd_rope(q_rot, k_rot, v, o, dO, lse, dq, dk, dv, delta, tab, scale, ma
         B, H, H_kv, S, D, float(scale), int(mask_mode), cu, ns, ms, dt, _stream(stream)))
 
 
+def _out_code(o, q):
+    """Output dtype code from the output tensor: fp32, or q's 16-bit dtype."""
+    torch = _torch()
+    if o.dtype == torch.float32:
+        return ATTN_DTYPE_F32
+    if o.dtype == q.dtype and q.dtype in (torch.bfloat16, torch.float16):
+        return _dtype_code(q)
+    raise TypeError(f"outputs must be float32 or the inputs' 16-bit dtype, not {o.dtype}")
+
+
+def _params(q, k, v, o, lse, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, rope_table, q_rot, k_rot):
+    B, H, H_kv, S, D, dt = _qkv_info(q, k, v)
+    dev = q.device
+    cu, ns, ms = _mask_args(mask_mode, cu_seqlens, n_seqs, max_seqlen, dev)
+    p = AttnParams()
+    p.q, p.k, p.v = _ptr(q, "q", device=dev), _ptr(k, "k", device=dev), _ptr(v, "v", device=dev)
+    out = _out_code(o, q)
+    p.o = _ptr(o, "o", (B, H, S, D), o.dtype, dev)
+    p.lse = _ptr(lse, "lse", (B, H, S), _torch().float32, dev)
+    p.B, p.H, p.H_kv, p.S, p.D = B, H, H_kv, S, D
+    p.scale, p.mask_mode, p.cu_seqlens, p.n_seqs, p.max_seqlen = float(scale), int(mask_mode), cu, ns, ms
+    p.dtype, p.out_dtype = dt, out
+    if rope_table is not None:
+        p.rope_table, p.rope_npos = _rope_table_ptr(rope_table, D, dev)
+        p.q_rot = _ptr(q_rot, "q_rot", tuple(q.shape), q.dtype, dev)
+        p.k_rot = _ptr(k_rot, "k_rot", tuple(k.shape), k.dtype, dev)
+    return p, (B, H, H_kv, S, D, dev)
+
+
+def attn_fwd_ex(q, k, v, o, lse, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None, n_seqs=None, max_seqlen=None,
+                rope_table=None, q_rot=None, k_rot=None, stream=None):
+    """Forward with every option: grouped K/V heads (k, v with fewer heads),
+    RoPE (rope_table given: q, k rotated into q_rot, k_rot), and 16-bit
+    outputs (o in the inputs' bf16/fp16 dtype instead of float32)."""
+    p, _ = _params(q, k, v, o, lse, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, rope_table, q_rot, k_rot)
+    _check(load_library().attn_fwd_ex(ctypes.byref(p), _stream(stream)))
+
+
+def attn_bwd_ex(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None,
+                n_seqs=None, max_seqlen=None, rope_table=None, q_rot=None, k_rot=None, stream=None):
+    """Backward with every option (see attn_fwd_ex).  With RoPE the kernels read
+    q_rot, k_rot (q, k only give shapes); dq, dk, dv in o's dtype."""
+    p, (B, H, H_kv, S, D, dev) = _params(q, k, v, o, lse, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen,
+                                         rope_table, q_rot, k_rot)
+    p.dO = _ptr(dO, "dO", (B, H, S, D), q.dtype, dev)
+    p.dq = _ptr(dq, "dq", (B, H, S, D), o.dtype, dev)
+    p.dk = _ptr(dk, "dk", (B, H_kv, S, D), o.dtype, dev)
+    p.dv = _ptr(dv, "dv", (B, H_kv, S, D), o.dtype, dev)
+    p.delta = _ptr(delta, "delta", (B, H, S), _torch().float32, dev)
+    _check(load_library().attn_bwd_ex(ctypes.byref(p), _stream(stream)))
+
+
 def decode_workspace_bytes(B, H, H_kv, D, max_len):
     return int(load_library().attn_decode_workspace_bytes(int(B), int(H), int(H_kv), int(D), int(max_len)))
 
@@ -366,26 +429,36 @@ def decode(q, k_cache, v_cache, cache_lens, scale, max_len, stream=None):
     attn_decode(q, k_cache, v_cache, cache_lens, o, lse, ws, scale, max_len, stream)
     return o, lse
 
-def forward(q, k, v, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None, max_seqlen=None, stream=None):
-    """Returns (o, lse) as new fp32 device tensors."""
+def forward(q, k, v, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None, max_seqlen=None, stream=None,
+            out_dtype=None):
+    """Returns (o, lse) as new device tensors: o in ``out_dtype`` (float32 by
+    default, or q's bf16/fp16 dtype), lse float32."""
     torch = _torch()
     B, H, S, D = q.shape
-    o = torch.empty((B, H, S, D), dtype=torch.float32, device=q.device)
+    o = torch.empty((B, H, S, D), dtype=out_dtype or torch.float32, device=q.device)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    attn_fwd(q, k, v, o, lse, scale, mask_mode, cu_seqlens, None, max_seqlen, stream)
+    if o.dtype == torch.float32:
+        attn_fwd(q, k, v, o, lse, scale, mask_mode, cu_seqlens, None, max_seqlen, stream)
+    else:
+        attn_fwd_ex(q, k, v, o, lse, scale, mask_mode, cu_seqlens, None, max_seqlen, stream=stream)
     return o, lse
 
 
 def backward(q, k, v, o, dO, lse, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None, max_seqlen=None,
              stream=None):
-    """Returns (dq, dk, dv, delta) as new fp32 device tensors."""
+    """Returns (dq, dk, dv, delta) as new device tensors: gradients in o's dtype
+    (float32, or q's bf16/fp16 dtype), delta float32."""
     torch = _torch()
     B, H, S, D = q.shape
-    dq = torch.empty((B, H, S, D), dtype=torch.float32, device=q.device)
-    dk = torch.empty(tuple(k.shape), dtype=torch.float32, device=q.device)
+    dq = torch.empty((B, H, S, D), dtype=o.dtype, device=q.device)
+    dk = torch.empty(tuple(k.shape), dtype=o.dtype, device=q.device)
     dv = torch.empty_like(dk)
     delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode, cu_seqlens, None, max_seqlen, stream)
+    if o.dtype == torch.float32:
+        attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode, cu_seqlens, None, max_seqlen, stream)
+    else:
+        attn_bwd_ex(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode, cu_seqlens, None, max_seqlen,
+                    stream=stream)
     return dq, dk, dv, delta
 
 

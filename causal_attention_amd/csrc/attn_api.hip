@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 140;  // 1.40: grouped-query, decode and RoPE entry points, fp16 inputs
+constexpr int kAbiVersion = 150;  // 1.50: grouped-query, decode, RoPE, fp16 inputs, attn_params calls with 16-bit outputs
 
 int check_common(int B, int H, int S, int D, int dtype) {
   if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_DTYPE;
@@ -53,6 +53,13 @@ int check_rope(const float *tab, int n_pos, int S, int mask_mode, int max_seqlen
   const int need = mask_mode == ATTN_MASK_DOC_CAUSAL ? max_seqlen : S;
   if (n_pos < need) return ATTN_ERR_ROPE;
   return ATTN_OK;
+}
+
+// Outputs are fp32, or 16-bit in the (16-bit) input dtype.
+int check_out(int dtype, int out_dtype) {
+  if (out_dtype == ATTN_DTYPE_F32) return ATTN_OK;
+  if (out_dtype == dtype && dtype != ATTN_DTYPE_F32) return ATTN_OK;
+  return ATTN_ERR_DTYPE;
 }
 
 attn::Args make_args(int B, int H, int S, int D, float scale, int mask_mode, const int32_t *cu_seqlens,
@@ -100,23 +107,44 @@ const char *attn_status_string(int status) {
   }
 }
 
-int attn_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int H_kv, int S,
-                 int D, float scale, int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype,
-                 void *stream) {
+// Whole forward (optionally rotating q and k first): argument checks, then
+// the kernels on one stream.
+static int fwd_all(const void *q, const void *k, const void *v, void *o, float *lse, bool with_rope,
+                   const float *rope, int rope_npos, void *q_rot, void *k_rot, int B, int H, int H_kv, int S, int D,
+                   float scale, int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype,
+                   int out_dtype, void *stream) {
   int st = check_common(B, H, S, D, dtype);
   if (st != ATTN_OK) return st;
+  if ((st = check_out(dtype, out_dtype)) != ATTN_OK) return st;
   if ((st = check_heads(H, H_kv)) != ATTN_OK) return st;
   if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+  if (with_rope && (!q_rot || !k_rot)) return ATTN_ERR_NULL;
   if ((st = check_mask(B, H, S, mask_mode, cu_seqlens, n_seqs, max_seqlen)) != ATTN_OK) return st;
   if ((st = check_scale(scale)) != ATTN_OK) return st;
+  if (with_rope && (st = check_rope(rope, rope_npos, S, mask_mode, max_seqlen)) != ATTN_OK) return st;
   attn::Args a = make_args(B, H, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
   a.H_kv = H_kv;
+  a.out16 = out_dtype != ATTN_DTYPE_F32;
   a.q = q;
   a.k = k;
+  if (with_rope) {
+    a.rope = rope;
+    a.rope_npos = rope_npos;
+    if (attn::launch_rope(a, q_rot, k_rot) != hipSuccess) return ATTN_ERR_HIP;
+    a.q = q_rot;
+    a.k = k_rot;
+  }
   a.v = v;
   a.o = o;
   a.lse = lse;
   return to_status(attn::launch_fwd(a));
+}
+
+int attn_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int H_kv, int S,
+                 int D, float scale, int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype,
+                 void *stream) {
+  return fwd_all(q, k, v, o, lse, false, nullptr, 0, nullptr, nullptr, B, H, H_kv, S, D, scale, mask_mode,
+                 cu_seqlens, n_seqs, max_seqlen, dtype, ATTN_DTYPE_F32, stream);
 }
 
 int attn_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int S, int D,
@@ -179,12 +207,13 @@ int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dO, con
 
 // Whole backward (optionally with RoPE gradients turned back in the dQ and dK
 // epilogues): argument checks, then the kernels on one stream.
-static int bwd_all(const void *q, const void *k, const void *v, const float *o, const void *dO, const float *lse,
-                   float *dq, float *dk, float *dv, float *delta, bool with_rope, const float *rope, int rope_npos,
+static int bwd_all(const void *q, const void *k, const void *v, const void *o, const void *dO, const float *lse,
+                   void *dq, void *dk, void *dv, float *delta, bool with_rope, const float *rope, int rope_npos,
                    int B, int H, int H_kv, int S, int D, float scale, int mask_mode, const int32_t *cu_seqlens,
-                   int n_seqs, int max_seqlen, int dtype, void *stream) {
+                   int n_seqs, int max_seqlen, int dtype, int out_dtype, void *stream) {
   int st = check_common(B, H, S, D, dtype);
   if (st != ATTN_OK) return st;
+  if ((st = check_out(dtype, out_dtype)) != ATTN_OK) return st;
   if ((st = check_heads(H, H_kv)) != ATTN_OK) return st;
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL;
   if ((st = check_mask(B, H, S, mask_mode, cu_seqlens, n_seqs, max_seqlen)) != ATTN_OK) return st;
@@ -192,6 +221,7 @@ static int bwd_all(const void *q, const void *k, const void *v, const float *o, 
   if (with_rope && (st = check_rope(rope, rope_npos, S, mask_mode, max_seqlen)) != ATTN_OK) return st;
   attn::Args a = make_args(B, H, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
   a.H_kv = H_kv;
+  a.out16 = out_dtype != ATTN_DTYPE_F32;
   a.rope = rope;
   a.rope_npos = rope_npos;
   a.q = q;
@@ -223,7 +253,7 @@ int attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o, co
                  float *dq, float *dk, float *dv, float *delta, int B, int H, int H_kv, int S, int D, float scale,
                  int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype, void *stream) {
   return bwd_all(q, k, v, o, dO, lse, dq, dk, dv, delta, false, nullptr, 0, B, H, H_kv, S, D, scale, mask_mode,
-                 cu_seqlens, n_seqs, max_seqlen, dtype, stream);
+                 cu_seqlens, n_seqs, max_seqlen, dtype, ATTN_DTYPE_F32, stream);
 }
 
 int attn_bwd(const void *q, const void *k, const void *v, const float *o, const void *dO, const float *lse,
@@ -262,35 +292,34 @@ int attn_rope(const void *q, const void *k, void *q_rot, void *k_rot, const floa
 int attn_fwd_rope(const void *q, const void *k, const void *v, void *q_rot, void *k_rot, float *o, float *lse,
                   const float *tab, int n_pos, int B, int H, int H_kv, int S, int D, float scale, int mask_mode,
                   const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype, void *stream) {
-  int st = check_common(B, H, S, D, dtype);
-  if (st != ATTN_OK) return st;
-  if ((st = check_heads(H, H_kv)) != ATTN_OK) return st;
-  if (!q || !k || !v || !q_rot || !k_rot || !o) return ATTN_ERR_NULL;
-  if ((st = check_mask(B, H, S, mask_mode, cu_seqlens, n_seqs, max_seqlen)) != ATTN_OK) return st;
-  if ((st = check_scale(scale)) != ATTN_OK) return st;
-  if ((st = check_rope(tab, n_pos, S, mask_mode, max_seqlen)) != ATTN_OK) return st;
-  attn::Args a = make_args(B, H, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
-  a.H_kv = H_kv;
-  a.q = q;
-  a.k = k;
-  a.rope = tab;
-  a.rope_npos = n_pos;
-  hipError_t e = attn::launch_rope(a, q_rot, k_rot);
-  if (e != hipSuccess) return ATTN_ERR_HIP;
-  a.q = q_rot;
-  a.k = k_rot;
-  a.v = v;
-  a.o = o;
-  a.lse = lse;
-  return to_status(attn::launch_fwd(a));
+  return fwd_all(q, k, v, o, lse, true, tab, n_pos, q_rot, k_rot, B, H, H_kv, S, D, scale, mask_mode, cu_seqlens,
+                 n_seqs, max_seqlen, dtype, ATTN_DTYPE_F32, stream);
 }
 
 int attn_bwd_rope(const void *q_rot, const void *k_rot, const void *v, const float *o, const void *dO,
                   const float *lse, float *dq, float *dk, float *dv, float *delta, const float *tab, int n_pos, int B,
                   int H, int H_kv, int S, int D, float scale, int mask_mode, const int32_t *cu_seqlens, int n_seqs,
                   int max_seqlen, int dtype, void *stream) {
-  return bwd_all(q_rot, k_rot, v, o, dO, lse, dq, dk, dv, delta, true, tab, n_pos, B, H, H_kv, S, D, scale, mask_mode,
-                 cu_seqlens, n_seqs, max_seqlen, dtype, stream);
+  return bwd_all(q_rot, k_rot, v, o, dO, lse, dq, dk, dv, delta, true, tab, n_pos, B, H, H_kv, S, D, scale,
+                 mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, ATTN_DTYPE_F32, stream);
+}
+
+int attn_fwd_ex(const attn_params *p, void *stream) {
+  if (p == nullptr) return ATTN_ERR_NULL;
+  const int H_kv = p->H_kv == 0 ? p->H : p->H_kv;
+  const bool rope = p->rope_table != nullptr;
+  return fwd_all(p->q, p->k, p->v, p->o, p->lse, rope, p->rope_table, p->rope_npos, p->q_rot, p->k_rot, p->B, p->H,
+                 H_kv, p->S, p->D, p->scale, p->mask_mode, p->cu_seqlens, p->n_seqs, p->max_seqlen, p->dtype,
+                 p->out_dtype, stream);
+}
+
+int attn_bwd_ex(const attn_params *p, void *stream) {
+  if (p == nullptr) return ATTN_ERR_NULL;
+  const int H_kv = p->H_kv == 0 ? p->H : p->H_kv;
+  const bool rope = p->rope_table != nullptr;
+  return bwd_all(rope ? p->q_rot : p->q, rope ? p->k_rot : p->k, p->v, p->o, p->dO, p->lse, p->dq, p->dk, p->dv,
+                 p->delta, rope, p->rope_table, p->rope_npos, p->B, p->H, H_kv, p->S, p->D, p->scale, p->mask_mode,
+                 p->cu_seqlens, p->n_seqs, p->max_seqlen, p->dtype, p->out_dtype, stream);
 }
 
 size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int D, int max_len) {

@@ -30,8 +30,8 @@ namespace attn {
 // Delta_i = sum_d dO_id * O_id.  Memory bound: each group of D/VEC lanes reads
 // one row of dO (input dtype) and O (fp32) with 16-byte loads and reduces
 // across the group.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const float *__restrict__ o,
+template <typename T, typename OT, int D>
+__global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const OT *__restrict__ o,
                                                                   const T *__restrict__ dO,
                                                                   float *__restrict__ delta, int rows) {
   constexpr int VEC = 16 / sizeof(T);  // dO elements per 16-byte load
@@ -44,15 +44,25 @@ __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const float *_
     float acc = 0.f;
     if (row < rows) {
       const T *dp = dO + (size_t)row * D + sub * VEC;
-      const float *op = o + (size_t)row * D + sub * VEC;
+      const OT *op = o + (size_t)row * D + sub * VEC;
       if constexpr (sizeof(T) == 2) {
         const typename Elem<T>::frag g = *reinterpret_cast<const typename Elem<T>::frag *>(dp);
-        const f32x4 o0 = *reinterpret_cast<const f32x4 *>(op);
-        const f32x4 o1 = *reinterpret_cast<const f32x4 *>(op + 4);
+        float ov[8];
+        if constexpr (sizeof(OT) == 4) {
+          const f32x4 o0 = *reinterpret_cast<const f32x4 *>(op);
+          const f32x4 o1 = *reinterpret_cast<const f32x4 *>(op + 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc += (float)g[i] * o0[i];
+          for (int i = 0; i < 4; ++i) {
+            ov[i] = o0[i];
+            ov[4 + i] = o1[i];
+          }
+        } else {
+          const typename Vec8Of<OT>::type h = *reinterpret_cast<const typename Vec8Of<OT>::type *>(op);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc += (float)g[4 + i] * o1[i];
+          for (int i = 0; i < 8; ++i) ov[i] = (float)h[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc += (float)g[i] * ov[i];
       } else {
         const f32x4 g = *reinterpret_cast<const f32x4 *>(dp);
         const f32x4 o0 = *reinterpret_cast<const f32x4 *>(op);
@@ -73,11 +83,11 @@ __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const float *_
 // global->LDS copies into two ring slots (separate LDS objects, loop unrolled
 // by two) one iteration ahead; Q and dO are read both as row fragments and,
 // through the transposing load, as Q^T and dO^T.
-template <typename T, int D, int BMQ, int MINB, bool DOC>
+template <typename T, typename OT, int D, int BMQ, int MINB, bool DOC>
 __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dO,
-    const float *__restrict__ lse, const float *__restrict__ delta, float *__restrict__ dk,
-    float *__restrict__ dv, int S, float c2, float scale, const int32_t *__restrict__ cu, int ntiles, int n_seqs,
+    const float *__restrict__ lse, const float *__restrict__ delta, OT *__restrict__ dk,
+    OT *__restrict__ dv, int S, float c2, float scale, const int32_t *__restrict__ cu, int ntiles, int n_seqs,
     int H, int G, const float *__restrict__ rope, int rope_npos) {
   constexpr int NW = 4;
   constexpr int NT = NW * kWaveSize;
@@ -235,8 +245,8 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   }
 
   if (!wave_active) return;
-  const GBuf gdk(dk + base, (uint32_t)(t.r_end * D * sizeof(float)));
-  const GBuf gdv(dv + base, (uint32_t)(t.r_end * D * sizeof(float)));
+  const GBuf gdk(dk + base, (uint32_t)(t.r_end * D * sizeof(OT)));
+  const GBuf gdv(dv + base, (uint32_t)(t.r_end * D * sizeof(OT)));
   // RoPE: this key's table row (keys past the tile end are not stored)
   const float *rrow =
       rope == nullptr ? nullptr : rope + (size_t)min(min(key, t.r_end - 1) - t.seg_start, rope_npos - 1) * D;
@@ -251,9 +261,9 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
         b4[i] = dvacc[db][4 * g + i];
       }
       if (rope != nullptr) rope_back(a4, *reinterpret_cast<const f32x4 *>(rrow + db * 32 + 8 * g + 4 * hh));
-      const uint32_t off = (uint32_t)(key * D + db * 32 + 8 * g + 4 * hh) * sizeof(float);
-      gdk.store16(a4, off);
-      gdv.store16(b4, off);
+      const uint32_t e = (uint32_t)(key * D + db * 32 + 8 * g + 4 * hh);
+      store_out4<OT>(gdk, a4, e);
+      store_out4<OT>(gdv, b4, e);
     }
   }
 }
@@ -275,11 +285,11 @@ __device__ __forceinline__ float delta_tree(const float (&part)[KB]) {
 // for its queries from O, in the same summation order as the preprocess
 // kernel (so the result is bitwise the same), uses it, and writes it to
 // `delta_out` for the dK/dV kernel that runs after it.
-template <typename T, int D, int BN, int MINB, bool DOC, bool FUSE_DELTA>
+template <typename T, typename OT, int D, int BN, int MINB, bool DOC, bool FUSE_DELTA>
 __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dO,
-    const float *__restrict__ lse, const float *__restrict__ delta, const float *__restrict__ o,
-    float *__restrict__ delta_out, float *__restrict__ dq, int S, float c2, float scale,
+    const float *__restrict__ lse, const float *__restrict__ delta, const OT *__restrict__ o,
+    float *__restrict__ delta_out, OT *__restrict__ dq, int S, float c2, float scale,
     const int32_t *__restrict__ cu, int ntiles, int n_seqs, int H, int G, const float *__restrict__ rope,
     int rope_npos) {
   constexpr int NW = 4;
@@ -348,18 +358,15 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
     // Fragment kb of this lane is sub-block 2*kb + hh, so the lane computes
     // the butterfly's tree over its own sub-blocks and one swap across the
     // halves adds the other half's.
-    const GBuf go(o + base, (uint32_t)(t.r_end * D * sizeof(float)));
+    const GBuf go(o + base, (uint32_t)(t.r_end * D * sizeof(OT)));
     float part[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const uint32_t off = (uint32_t)(qi * D + 16 * kb + 8 * hh) * sizeof(float);
-      const f32x4 o0 = __builtin_bit_cast(f32x4, go.load16(off));
-      const f32x4 o1 = __builtin_bit_cast(f32x4, go.load16(off + 16));
+      float ov[8];
+      load_out8<OT>(go, (uint32_t)(qi * D + 16 * kb + 8 * hh), ov);
       float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc += (float)df[kb][i] * o0[i];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc += (float)df[kb][4 + i] * o1[i];
+      for (int i = 0; i < 8; ++i) acc += (float)df[kb][i] * ov[i];
       part[kb] = acc;
     }
     const float mine = delta_tree<2 * KB, 2, 0, KB>(part);
@@ -426,7 +433,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
   }
 
   if (!wave_active) return;
-  const GBuf gdq(dq + base, (uint32_t)(t.r_end * D * sizeof(float)));
+  const GBuf gdq(dq + base, (uint32_t)(t.r_end * D * sizeof(OT)));
   // RoPE: this query's table row (queries past the tile end are not stored)
   const float *rrow =
       rope == nullptr ? nullptr : rope + (size_t)min(min(qi, t.r_end - 1) - t.seg_start, rope_npos - 1) * D;
@@ -438,7 +445,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) a4[i] = dqacc[db][4 * g + i] * scale;
       if (rope != nullptr) rope_back(a4, *reinterpret_cast<const f32x4 *>(rrow + db * 32 + 8 * g + 4 * hh));
-      gdq.store16(a4, (uint32_t)(qi * D + db * 32 + 8 * g + 4 * hh) * sizeof(float));
+      store_out4<OT>(gdq, a4, (uint32_t)(qi * D + db * 32 + 8 * g + 4 * hh));
     }
   }
 }
@@ -476,18 +483,18 @@ template <typename T, int D> struct BwdCfg {
   }
 };
 
-template <typename T, int D>
+template <typename T, typename OT, int D>
 static hipError_t launch_pre_t(const Args &a) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int RPB = 256 / (D / VEC);
   const int rows = a.B * a.H * a.S;
   const int blocks = min((rows + RPB - 1) / RPB, 65536);
-  hipLaunchKernelGGL((attn_bwd_preprocess_kernel<T, D>), dim3(blocks), dim3(256), 0, a.stream, a.o_in,
-                     static_cast<const T *>(a.dO), a.delta, rows);
+  hipLaunchKernelGGL((attn_bwd_preprocess_kernel<T, OT, D>), dim3(blocks), dim3(256), 0, a.stream,
+                     static_cast<const OT *>(a.o_in), static_cast<const T *>(a.dO), a.delta, rows);
   return hipGetLastError();
 }
 
-template <typename T, int D, bool DOC>
+template <typename T, typename OT, int D, bool DOC>
 static hipError_t launch_dkdv_t(const Args &a) {
   constexpr int BMQ = BwdCfg<T, D>::BMQ;
   constexpr int MINB = BwdCfg<T, D>::MINB_DKDV;
@@ -502,14 +509,15 @@ static hipError_t launch_dkdv_t(const Args &a) {
     ntiles = (a.S + BN - 1) / BN;
     grid = dim3(ntiles * a.B * a.H_kv);
   }
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, BMQ, MINB, DOC>), grid, dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, OT, D, BMQ, MINB, DOC>), grid, dim3(256), 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
-                     static_cast<const T *>(a.dO), a.lse_in, a.delta_in, a.dk, a.dv, a.S, c2, a.scale,
-                     a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv, a.rope, a.rope_npos);
+                     static_cast<const T *>(a.dO), a.lse_in, a.delta_in, static_cast<OT *>(a.dk),
+                     static_cast<OT *>(a.dv), a.S, c2, a.scale, a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv,
+                     a.rope, a.rope_npos);
   return hipGetLastError();
 }
 
-template <typename T, int D, bool DOC, bool FUSE_DELTA = false>
+template <typename T, typename OT, int D, bool DOC, bool FUSE_DELTA>
 static hipError_t launch_dq_t(const Args &a) {
   constexpr int BN = BwdCfg<T, D>::template dq_bn<DOC>();
   constexpr int MINB = BwdCfg<T, D>::MINB_DQ;
@@ -524,64 +532,80 @@ static hipError_t launch_dq_t(const Args &a) {
     ntiles = (a.S + BM - 1) / BM;
     grid = dim3(ntiles * a.B * a.H);
   }
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BN, MINB, DOC, FUSE_DELTA>), grid, dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, OT, D, BN, MINB, DOC, FUSE_DELTA>), grid, dim3(256), 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
-                     static_cast<const T *>(a.dO), a.lse_in, a.delta_in, a.o_in, a.delta, a.dq, a.S, c2, a.scale,
-                     a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv, a.rope, a.rope_npos);
+                     static_cast<const T *>(a.dO), a.lse_in, a.delta_in, static_cast<const OT *>(a.o_in), a.delta,
+                     static_cast<OT *>(a.dq), a.S, c2, a.scale, a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv,
+                     a.rope, a.rope_npos);
   return hipGetLastError();
 }
 
-#define ATTN_DISPATCH_D(FN, T, ...)                     \
-  switch (a.D) {                                        \
-    case 32: return FN<T, 32 __VA_OPT__(, ) __VA_ARGS__>(a);  \
-    case 64: return FN<T, 64 __VA_OPT__(, ) __VA_ARGS__>(a);  \
-    default: return FN<T, 128 __VA_OPT__(, ) __VA_ARGS__>(a); \
+// Dispatch on D, then on the mask.
+template <typename T, typename OT>
+static hipError_t launch_pre_dt(const Args &a) {
+  switch (a.D) {
+    case 32: return launch_pre_t<T, OT, 32>(a);
+    case 64: return launch_pre_t<T, OT, 64>(a);
+    default: return launch_pre_t<T, OT, 128>(a);
   }
+}
 
-template <typename T>
-static hipError_t launch_pre_dt(const Args &a) { ATTN_DISPATCH_D(launch_pre_t, T) }
-template <typename T, bool DOC>
-static hipError_t launch_dkdv_dt(const Args &a) { ATTN_DISPATCH_D(launch_dkdv_t, T, DOC) }
-template <typename T, bool DOC>
-static hipError_t launch_dq_dt(const Args &a) { ATTN_DISPATCH_D(launch_dq_t, T, DOC) }
+template <typename T, typename OT, bool DOC>
+static hipError_t launch_dkdv_d(const Args &a) {
+  switch (a.D) {
+    case 32: return launch_dkdv_t<T, OT, 32, DOC>(a);
+    case 64: return launch_dkdv_t<T, OT, 64, DOC>(a);
+    default: return launch_dkdv_t<T, OT, 128, DOC>(a);
+  }
+}
+
+template <typename T, typename OT, bool DOC, bool FUSE_DELTA>
+static hipError_t launch_dq_d(const Args &a) {
+  switch (a.D) {
+    case 32: return launch_dq_t<T, OT, 32, DOC, FUSE_DELTA>(a);
+    case 64: return launch_dq_t<T, OT, 64, DOC, FUSE_DELTA>(a);
+    default: return launch_dq_t<T, OT, 128, DOC, FUSE_DELTA>(a);
+  }
+}
+
+template <typename T, typename OT>
+static hipError_t launch_dkdv_dt(const Args &a) {
+  return a.doc ? launch_dkdv_d<T, OT, true>(a) : launch_dkdv_d<T, OT, false>(a);
+}
+
+template <typename T, typename OT, bool FUSE_DELTA>
+static hipError_t launch_dq_dt(const Args &a) {
+  return a.doc ? launch_dq_d<T, OT, true, FUSE_DELTA>(a) : launch_dq_d<T, OT, false, FUSE_DELTA>(a);
+}
 
 hipError_t launch_bwd_preprocess(const Args &a) {
   switch (a.dtype) {
-    case 1: return launch_pre_dt<bf16>(a);
-    case 2: return launch_pre_dt<f16>(a);
-    default: return launch_pre_dt<float>(a);
+    case 1: return a.out16 ? launch_pre_dt<bf16, bf16>(a) : launch_pre_dt<bf16, float>(a);
+    case 2: return a.out16 ? launch_pre_dt<f16, f16>(a) : launch_pre_dt<f16, float>(a);
+    default: return launch_pre_dt<float, float>(a);
   }
 }
 
 hipError_t launch_bwd_dkdv(const Args &a) {
   switch (a.dtype) {
-    case 1: return a.doc ? launch_dkdv_dt<bf16, true>(a) : launch_dkdv_dt<bf16, false>(a);
-    case 2: return a.doc ? launch_dkdv_dt<f16, true>(a) : launch_dkdv_dt<f16, false>(a);
-    default: return a.doc ? launch_dkdv_dt<float, true>(a) : launch_dkdv_dt<float, false>(a);
+    case 1: return a.out16 ? launch_dkdv_dt<bf16, bf16>(a) : launch_dkdv_dt<bf16, float>(a);
+    case 2: return a.out16 ? launch_dkdv_dt<f16, f16>(a) : launch_dkdv_dt<f16, float>(a);
+    default: return launch_dkdv_dt<float, float>(a);
   }
 }
 
 hipError_t launch_bwd_dq(const Args &a) {
   switch (a.dtype) {
-    case 1: return a.doc ? launch_dq_dt<bf16, true>(a) : launch_dq_dt<bf16, false>(a);
-    case 2: return a.doc ? launch_dq_dt<f16, true>(a) : launch_dq_dt<f16, false>(a);
-    default: return a.doc ? launch_dq_dt<float, true>(a) : launch_dq_dt<float, false>(a);
-  }
-}
-
-template <typename T, bool DOC>
-static hipError_t launch_dq_delta_d(const Args &a) {
-  switch (a.D) {
-    case 32: return launch_dq_t<T, 32, DOC, true>(a);
-    case 64: return launch_dq_t<T, 64, DOC, true>(a);
-    default: return launch_dq_t<T, 128, DOC, true>(a);
+    case 1: return a.out16 ? launch_dq_dt<bf16, bf16, false>(a) : launch_dq_dt<bf16, float, false>(a);
+    case 2: return a.out16 ? launch_dq_dt<f16, f16, false>(a) : launch_dq_dt<f16, float, false>(a);
+    default: return launch_dq_dt<float, float, false>(a);
   }
 }
 
 hipError_t launch_bwd_dq_delta(const Args &a) {
   switch (a.dtype) {
-    case 1: return a.doc ? launch_dq_delta_d<bf16, true>(a) : launch_dq_delta_d<bf16, false>(a);
-    case 2: return a.doc ? launch_dq_delta_d<f16, true>(a) : launch_dq_delta_d<f16, false>(a);
+    case 1: return a.out16 ? launch_dq_dt<bf16, bf16, true>(a) : launch_dq_dt<bf16, float, true>(a);
+    case 2: return a.out16 ? launch_dq_dt<f16, f16, true>(a) : launch_dq_dt<f16, float, true>(a);
     default: return hipErrorInvalidValue;  // Delta fusion follows the 16-bit preprocess layout
   }
 }

@@ -36,6 +36,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaveSize = 64;
@@ -258,7 +261,49 @@ struct GBuf {
   __device__ __forceinline__ void store4(float v, uint32_t off) const {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
   }
+  __device__ __forceinline__ void store8(const u32x2 &v, uint32_t off) const {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+  }
 };
+
+// Output element type OT: fp32, or the 16-bit input type (rounded to nearest
+// even once, at the store).  store_out4 writes four consecutive outputs at
+// element offset e; load_out8 reads eight as fp32.
+template <typename OT> struct Vec4Of;
+template <> struct Vec4Of<bf16> { using type = bf16x4; };
+template <> struct Vec4Of<f16> { using type = f16x4; };
+template <typename OT> struct Vec8Of;
+template <> struct Vec8Of<bf16> { using type = bf16x8; };
+template <> struct Vec8Of<f16> { using type = f16x8; };
+
+template <typename OT>
+__device__ __forceinline__ void load_out8(const GBuf &g, uint32_t e, float (&x)[8]) {
+  if constexpr (sizeof(OT) == 4) {
+    const f32x4 a = __builtin_bit_cast(f32x4, g.load16(e * 4u));
+    const f32x4 b = __builtin_bit_cast(f32x4, g.load16(e * 4u + 16u));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = a[i];
+      x[4 + i] = b[i];
+    }
+  } else {
+    const typename Vec8Of<OT>::type h = __builtin_bit_cast(typename Vec8Of<OT>::type, g.load16(e * 2u));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)h[i];
+  }
+}
+
+template <typename OT>
+__device__ __forceinline__ void store_out4(const GBuf &g, const f32x4 &v, uint32_t e) {
+  if constexpr (sizeof(OT) == 4) {
+    g.store16(v, e * 4u);
+  } else {
+    typename Vec4Of<OT>::type h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = (OT)v[i];
+    g.store8(__builtin_bit_cast(u32x2, h), e * 2u);
+  }
+}
 
 // An 8-slot fragment of row `row`, columns [col, col + 8), of a row-major
 // [*, D] array behind `g` (zeros past the resource's end).

@@ -34,9 +34,9 @@ namespace attn {
 
 constexpr float kRescaleLimit = 1.8446744e19f;  // 2^64: larger row sums take the exact path
 
-template <typename T, int D, int NW, int BN, int MINB, bool DOC>
+template <typename T, typename OT, int D, int NW, int BN, int MINB, bool DOC>
 __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                                                                 const T *__restrict__ v, float *__restrict__ o,
+                                                                 const T *__restrict__ v, OT *__restrict__ o,
                                                                  float *__restrict__ lse, int S, float c2,
                                                                  const int32_t *__restrict__ cu, int ntiles, int n_seqs, int H, int G) {
   constexpr int NT = NW * kWaveSize;
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
   }
 
   if (!wave_active) return;
-  const GBuf go(o + base, (uint32_t)(t.r_end * D * sizeof(float)));
+  const GBuf go(o + base, (uint32_t)(t.r_end * D * sizeof(OT)));
   const int qi = w0 + c;
   const float lt = l + swap_halves(l);
   const float inv = 1.0f / lt;
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
       f32x4 val;
 #pragma unroll
       for (int i = 0; i < 4; ++i) val[i] = oacc[db][4 * g + i] * inv;
-      go.store16(val, (uint32_t)(qi * D + db * 32 + 8 * g + 4 * hh) * sizeof(float));
+      store_out4<OT>(go, val, (uint32_t)(qi * D + db * 32 + 8 * g + 4 * hh));
     }
   }
   if (lse != nullptr && hh == 0 && qi < t.r_end) lse[(size_t)t.head * S + qi] = (m + __log2f(lt)) * kLn2;
@@ -240,7 +240,7 @@ template <typename T, int D> struct FwdCfg {
 #endif
 };
 
-template <typename T, int D, bool DOC>
+template <typename T, typename OT, int D, bool DOC>
 static hipError_t launch_fwd_t(const Args &a) {
   constexpr int BN = FwdCfg<T, D>::BN;
   constexpr int NW = FwdCfg<T, D>::NW;
@@ -257,31 +257,31 @@ static hipError_t launch_fwd_t(const Args &a) {
     ntiles = (a.S + BM - 1) / BM;
     grid = dim3(ntiles * a.B * a.H);
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW, BN, MINB, DOC>), grid, block, 0, a.stream,
+  hipLaunchKernelGGL((attn_fwd_kernel<T, OT, D, NW, BN, MINB, DOC>), grid, block, 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
-                     a.o, a.lse, a.S, c2, a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv);
+                     static_cast<OT *>(a.o), a.lse, a.S, c2, a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv);
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, typename OT, int D>
 static hipError_t launch_fwd_d(const Args &a) {
-  return a.doc ? launch_fwd_t<T, D, true>(a) : launch_fwd_t<T, D, false>(a);
+  return a.doc ? launch_fwd_t<T, OT, D, true>(a) : launch_fwd_t<T, OT, D, false>(a);
 }
 
-template <typename T>
+template <typename T, typename OT>
 static hipError_t launch_fwd_dt(const Args &a) {
   switch (a.D) {
-    case 32: return launch_fwd_d<T, 32>(a);
-    case 64: return launch_fwd_d<T, 64>(a);
-    default: return launch_fwd_d<T, 128>(a);
+    case 32: return launch_fwd_d<T, OT, 32>(a);
+    case 64: return launch_fwd_d<T, OT, 64>(a);
+    default: return launch_fwd_d<T, OT, 128>(a);
   }
 }
 
 hipError_t launch_fwd(const Args &a) {
   switch (a.dtype) {
-    case 1: return launch_fwd_dt<bf16>(a);
-    case 2: return launch_fwd_dt<f16>(a);
-    default: return launch_fwd_dt<float>(a);
+    case 1: return a.out16 ? launch_fwd_dt<bf16, bf16>(a) : launch_fwd_dt<bf16, float>(a);
+    case 2: return a.out16 ? launch_fwd_dt<f16, f16>(a) : launch_fwd_dt<f16, float>(a);
+    default: return launch_fwd_dt<float, float>(a);
   }
 }
 

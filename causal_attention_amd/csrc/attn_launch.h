@@ -9,8 +9,10 @@ namespace attn {
 // Validated arguments of one call (the C ABI fills this after checking them).
 struct Args {
   const void *q, *k, *v, *dO;
-  const float *o_in, *lse_in, *delta_in;
-  float *o, *lse, *dq, *dk, *dv, *delta;
+  const void *o_in;          // O as the backward reads it (output dtype)
+  const float *lse_in, *delta_in;
+  void *o, *dq, *dk, *dv;    // outputs: fp32, or the 16-bit input dtype when out16
+  float *lse, *delta;
   int B, H, S, D;
   int H_kv;                 // key/value heads (H for plain multi-head attention)
   float scale;
@@ -19,6 +21,7 @@ struct Args {
   int n_seqs, max_seqlen;
   int dtype;                // input dtype: ATTN_DTYPE_F32, _BF16 or _F16 (attn_api.h)
   bool half() const { return dtype != 0; }  // 16-bit inputs
+  bool out16;               // O, dQ, dK, dV in the input dtype (16-bit inputs only)
   const float *rope;        // RoPE table [rope_npos][D/2][2] (cos, sin), or NULL: dQ and dK
   int rope_npos;            // epilogues turn the gradients back by the row's angles
   hipStream_t stream;

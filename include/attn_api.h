@@ -248,6 +248,59 @@ int attn_bwd_rope(const void *q_rot, const void *k_rot, const void *v, const flo
                   const int32_t *cu_seqlens, int n_seqs, int max_seqlen,
                   int dtype, void *stream);
 
+/*
+ * One forward or backward call with every option at once: grouped key/value
+ * heads, RoPE, and 16-bit outputs.  Zero-initialise an attn_params, then set
+ * the fields the call uses; the plain entry points above are these calls with
+ * H_kv = H, no RoPE and fp32 outputs (same kernels, same results).
+ *
+ *   q, k, v       inputs, [B, H, S, D] and [B, H_kv, S, D] in `dtype`.  With
+ *                 RoPE these are the UNROTATED q and k: attn_fwd_ex rotates
+ *                 them into q_rot, k_rot; attn_bwd_ex does not read them.
+ *   dO            backward only: dL/dO, [B, H, S, D] in `dtype`.
+ *   o             [B, H, S, D] in `out_dtype`: forward output, backward input.
+ *   lse           [B, H, S] fp32: forward output (may be NULL there),
+ *                 backward input.
+ *   dq, dk, dv    backward outputs in `out_dtype`: [B, H, S, D] and
+ *                 [B, H_kv, S, D] twice; gradients of the unrotated q, k.
+ *   delta         backward workspace [B, H, S] fp32 (holds Delta on return),
+ *                 computed from `o` as stored.
+ *   B, H, H_kv, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen,
+ *   dtype         as attn_fwd_gqa (H_kv = 0 means H).
+ *   out_dtype     ATTN_DTYPE_F32 (0) for fp32 outputs, or `dtype` itself
+ *                 (bf16 or fp16 inputs only) to store O, dQ, dK and dV in the
+ *                 input type, rounded to nearest even once at the store.
+ *                 Anything else: ATTN_ERR_DTYPE.  LSE and Delta stay fp32.
+ *   rope_table    NULL: no RoPE.  Else a table from attn_rope_table with
+ *   rope_npos     rope_npos positions (>= S, or >= max_seqlen for packed
+ *                 documents; else ATTN_ERR_ROPE).
+ *   q_rot, k_rot  with RoPE: the rotated q and k in `dtype` (caller-owned),
+ *                 written by attn_fwd_ex and read by attn_bwd_ex.
+ *
+ * Errors, ownership and stream rules as the entry points above; a NULL
+ * params pointer returns ATTN_ERR_NULL.
+ */
+typedef struct attn_params {
+  const void *q, *k, *v, *dO;
+  void *o;
+  float *lse;
+  void *dq, *dk, *dv;
+  float *delta;
+  int B, H, H_kv, S, D;
+  float scale;
+  int mask_mode;
+  const int32_t *cu_seqlens;
+  int n_seqs, max_seqlen;
+  int dtype, out_dtype;
+  const float *rope_table;
+  int rope_npos;
+  void *q_rot, *k_rot;
+} attn_params;
+
+int attn_fwd_ex(const attn_params *p, void *stream);
+
+int attn_bwd_ex(const attn_params *p, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *attn_status_string(int status);
 

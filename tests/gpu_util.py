@@ -75,17 +75,30 @@ def errors(got, ref):
     return max_abs, rel_fro
 
 
+# significant bits of the 16-bit output formats
+_OUT_BITS = {"bf16": 8, "f16": 11}
+
+
+def half_ulp(x, fmt):
+    """Half the spacing of ``fmt`` ("bf16" or "f16") values at |x|: the error a
+    correctly rounded store of the exact value may make."""
+    _, e = np.frexp(np.abs(np.asarray(x, dtype=np.float64)))  # |x| = m 2^e, 1/2 <= m < 1
+    return np.ldexp(1.0, e - _OUT_BITS[fmt] - 1)
+
+
 def compare(out, ref, dtype, heads=None, names=("o", "lse", "dq", "dk", "dv", "delta"), tag="",
-            rel_to_max=None):
+            rel_to_max=None, out16=None):
     """Assert the GPU outputs match the oracle on the given heads (all if None).
 
     rel_to_max: if given, the max-abs bound of O/dQ/dK/dV is rel_to_max * max|ref|
     instead of the fixed absolute bound (for inputs far outside the workloads'
-    scale, where bf16 rounding error grows with the magnitudes)."""
+    scale, where bf16 rounding error grows with the magnitudes).
+    out16: "bf16" or "f16" when O, dQ, dK, dV are stored in that format; each
+    element's bound then grows by its own rounding, half_ulp(ref)."""
     tol = TOL[dtype]
     report = {}
     for name in names:
-        g = out[name].detach().cpu().numpy().astype(np.float64)
+        g = out[name].detach().float().cpu().numpy().astype(np.float64)
         r = ref[name]
         if heads is not None:
             g = np.stack([g[b, h] for b, h in heads])
@@ -100,6 +113,11 @@ def compare(out, ref, dtype, heads=None, names=("o", "lse", "dq", "dk", "dv", "d
             assert ma <= 10 * tol["max_abs"], f"{tag} {name}: max-abs {ma:.3e}"
         else:
             lim = tol["max_abs"] if rel_to_max is None else rel_to_max * float(np.max(np.abs(r)))
+            if out16 is not None:  # error beyond the store's own rounding
+                # the store rounds the kernel's value, which may sit in the binade above ref
+                ma = float(np.max(np.abs(g - r) - half_ulp(np.maximum(np.abs(g), np.abs(r)), out16))) \
+                    if g.size else 0.0
+                report[name] = (ma, rf)
             assert ma <= lim, f"{tag} {name}: max-abs {ma:.3e} > {lim}"
             if tol["rel_fro"] is not None:
                 assert rf <= tol["rel_fro"], f"{tag} {name}: rel-Frobenius {rf:.3e} > {tol['rel_fro']}"

@@ -31,7 +31,7 @@ def test_header_status_codes_match_binding():
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 140
+    assert lib.attn_abi_version() == 150
 
 
 def test_status_strings(lib):
@@ -218,6 +218,56 @@ def test_rope_table_rejects_invalid_arguments(lib, args, code):
     assert lib.attn_rope_table(*args, None) == code
 
 
+def _params(**kw):
+    p = _binding.AttnParams()
+    base = dict(q=FAKE, k=FAKE, v=FAKE, dO=FAKE, o=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, delta=FAKE, B=1, H=4,
+                H_kv=0, S=64, D=64, scale=0.125, mask_mode=0, cu_seqlens=None, n_seqs=0, max_seqlen=0, dtype=1,
+                out_dtype=0, rope_table=None, rope_npos=0, q_rot=None, k_rot=None)
+    base.update(kw)
+    for name, val in base.items():
+        setattr(p, name, val)
+    return ctypes.byref(p)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out_dtype=2), -4), (dict(out_dtype=7), -4), (dict(dtype=0, out_dtype=1), -4),
+    (dict(dtype=2, out_dtype=1), -4), (dict(q=None), -1), (dict(H_kv=3), -10), (dict(D=40), -3),
+    (dict(mask_mode=1, cu_seqlens=FAKE, n_seqs=2, max_seqlen=40, B=2), -6), (dict(scale=0.0), -9),
+    (dict(rope_table=FAKE, rope_npos=64, q_rot=None, k_rot=FAKE), -1),
+    (dict(rope_table=FAKE, rope_npos=63, q_rot=FAKE, k_rot=FAKE), -12),
+])
+def test_ex_entry_points_reject_invalid_arguments(lib, kw, code):
+    assert lib.attn_fwd_ex(_params(**kw), None) == code
+    assert lib.attn_bwd_ex(_params(**kw), None) == code
+
+
+def test_ex_entry_points_check_their_own_fields(lib):
+    assert lib.attn_fwd_ex(None, None) == -1 and lib.attn_bwd_ex(None, None) == -1
+    assert lib.attn_bwd_ex(_params(dO=None), None) == -1 and lib.attn_bwd_ex(_params(delta=None), None) == -1
+    assert lib.attn_fwd_ex(_params(dO=None, dq=None), None) in (0, -7)  # the forward reads neither
+
+
+def test_params_struct_layout_matches_the_header(tmp_path):
+    """Field offsets and size of attn_params as a C compiler lays them out
+    (gcc on the header) equal the ctypes mirror's."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f[0] for f in _binding.AttnParams._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"attn_api.h\"\nint main(void) {\n"
+                   + "".join(f'  printf("%zu\\n", offsetof(attn_params, {f}));\n' for f in fields)
+                   + '  printf("%zu\\n", sizeof(attn_params));\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    inc = str(__import__("pathlib").Path(_binding.HEADER_PATH).parent)
+    subprocess.run([cc, "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    want = [getattr(_binding.AttnParams, f).offset for f in fields] + [ctypes.sizeof(_binding.AttnParams)]
+    assert got == want
+
+
 def test_no_device_reports_hip_error(lib):
     """A valid call with no GPU present fails with ATTN_ERR_HIP instead of aborting."""
     torch = pytest.importorskip("torch")
@@ -229,6 +279,7 @@ def test_no_device_reports_hip_error(lib):
     assert _bwd_gqa(lib, 1) == -7
     assert _rope(lib) == -7 and _fwd_rope(lib) == -7 and _bwd_rope(lib) == -7
     assert lib.attn_rope_table(FAKE, 64, 64, 10000.0, None) == -7
+    assert lib.attn_fwd_ex(_params(out_dtype=1), None) == -7 and lib.attn_bwd_ex(_params(H_kv=2), None) == -7
 
 
 def test_binding_refuses_host_tensors():

@@ -48,6 +48,7 @@ class AttnConfig:
     doc_seed: int = 500
     H_kv: int | None = None  # key/value heads (grouped-query attention); None = H
     rope: bool = False       # rotary position embedding of q and k before attention
+    out16: bool = False      # O, dQ, dK, dV stored in the (16-bit) input dtype instead of fp32
     note: str = field(default="", compare=False)
 
     @property
@@ -82,6 +83,10 @@ CONFIGS = {
     # table: RoPE; Forge, "Architecture": attention with RoPE), base 10000.
     "lm237m_ctx1024_rope": AttnConfig("lm237m_ctx1024_rope", B=8, H=16, S=1024, D=64, dtype="bf16", rope=True,
                                       note="237M-class layer with RoPE on q and k"),
+    # The same layer with O, dQ, dK, dV stored in bf16 (what a bf16 model
+    # consumes next) instead of fp32.
+    "lm237m_ctx1024_out16": AttnConfig("lm237m_ctx1024_out16", B=8, H=16, S=1024, D=64, dtype="bf16", out16=True,
+                                       note="237M-class layer with bf16 outputs"),
 }
 
 
