@@ -27,7 +27,7 @@ STATUS_NAMES = {
     0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEAD_DIM",
     -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_MASK", -6: "ATTN_ERR_SEQLENS", -7: "ATTN_ERR_HIP",
     -8: "ATTN_ERR_UNIMPLEMENTED", -9: "ATTN_ERR_SCALE", -10: "ATTN_ERR_HEADS", -11: "ATTN_ERR_WORKSPACE",
-    -12: "ATTN_ERR_ROPE",
+    -12: "ATTN_ERR_ROPE", -13: "ATTN_ERR_STRIDE",
 }
 
 
@@ -48,7 +48,10 @@ class AttnParams(ctypes.Structure):
                 ("dv", _P), ("delta", _P), ("B", _I), ("H", _I), ("H_kv", _I), ("S", _I), ("D", _I),
                 ("scale", _F), ("mask_mode", _I), ("cu_seqlens", _P), ("n_seqs", _I), ("max_seqlen", _I),
                 ("dtype", _I), ("out_dtype", _I), ("rope_table", _P), ("rope_npos", _I), ("q_rot", _P),
-                ("k_rot", _P)]
+                ("k_rot", _P), ("strides", (ctypes.c_int64 * 3) * 8)]
+
+
+STRIDE_SLOT = {"q": 0, "k": 1, "v": 2, "o": 3, "dO": 4, "dq": 5, "dk": 6, "dv": 7}
 
 # argtypes of every exported function, in the header's order
 SIGNATURES = {
@@ -342,14 +345,31 @@ def _out_code(o, q):
     raise TypeError(f"outputs must be float32 or the inputs' 16-bit dtype, not {o.dtype}")
 
 
+def _view(p, t, name, shape, dtype, device):
+    """Pointer of a [B, H, S, D] view whose last dimension is contiguous, its
+    (batch, head, sequence) element strides recorded in p.strides."""
+    if t is None:
+        return None
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a device tensor on {device}")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {tuple(shape)} {dtype}, not {tuple(t.shape)} {t.dtype}")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    p.strides[STRIDE_SLOT[name]][:] = [t.stride(0), t.stride(1), t.stride(2)]
+    return t.data_ptr()
+
+
 def _params(q, k, v, o, lse, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, rope_table, q_rot, k_rot):
     B, H, H_kv, S, D, dt = _qkv_info(q, k, v)
     dev = q.device
     cu, ns, ms = _mask_args(mask_mode, cu_seqlens, n_seqs, max_seqlen, dev)
     p = AttnParams()
-    p.q, p.k, p.v = _ptr(q, "q", device=dev), _ptr(k, "k", device=dev), _ptr(v, "v", device=dev)
+    p.q = _view(p, q, "q", (B, H, S, D), q.dtype, dev)
+    p.k = _view(p, k, "k", (B, H_kv, S, D), q.dtype, dev)
+    p.v = _view(p, v, "v", (B, H_kv, S, D), q.dtype, dev)
     out = _out_code(o, q)
-    p.o = _ptr(o, "o", (B, H, S, D), o.dtype, dev)
+    p.o = _view(p, o, "o", (B, H, S, D), o.dtype, dev)
     p.lse = _ptr(lse, "lse", (B, H, S), _torch().float32, dev)
     p.B, p.H, p.H_kv, p.S, p.D = B, H, H_kv, S, D
     p.scale, p.mask_mode, p.cu_seqlens, p.n_seqs, p.max_seqlen = float(scale), int(mask_mode), cu, ns, ms
@@ -364,8 +384,10 @@ def _params(q, k, v, o, lse, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, r
 def attn_fwd_ex(q, k, v, o, lse, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None, n_seqs=None, max_seqlen=None,
                 rope_table=None, q_rot=None, k_rot=None, stream=None):
     """Forward with every option: grouped K/V heads (k, v with fewer heads),
-    RoPE (rope_table given: q, k rotated into q_rot, k_rot), and 16-bit
-    outputs (o in the inputs' bf16/fp16 dtype instead of float32)."""
+    RoPE (rope_table given: q, k rotated into contiguous q_rot, k_rot), 16-bit
+    outputs (o in the inputs' bf16/fp16 dtype instead of float32), and any
+    [B, H, S, D] views with a contiguous last dimension (e.g. x.transpose(1, 2)
+    of a [B, S, H, D] tensor), passed by their strides without copies."""
     p, _ = _params(q, k, v, o, lse, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, rope_table, q_rot, k_rot)
     _check(load_library().attn_fwd_ex(ctypes.byref(p), _stream(stream)))
 
@@ -376,10 +398,10 @@ def attn_bwd_ex(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode=ATTN_MA
     q_rot, k_rot (q, k only give shapes); dq, dk, dv in o's dtype."""
     p, (B, H, H_kv, S, D, dev) = _params(q, k, v, o, lse, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen,
                                          rope_table, q_rot, k_rot)
-    p.dO = _ptr(dO, "dO", (B, H, S, D), q.dtype, dev)
-    p.dq = _ptr(dq, "dq", (B, H, S, D), o.dtype, dev)
-    p.dk = _ptr(dk, "dk", (B, H_kv, S, D), o.dtype, dev)
-    p.dv = _ptr(dv, "dv", (B, H_kv, S, D), o.dtype, dev)
+    p.dO = _view(p, dO, "dO", (B, H, S, D), q.dtype, dev)
+    p.dq = _view(p, dq, "dq", (B, H, S, D), o.dtype, dev)
+    p.dk = _view(p, dk, "dk", (B, H_kv, S, D), o.dtype, dev)
+    p.dv = _view(p, dv, "dv", (B, H_kv, S, D), o.dtype, dev)
     p.delta = _ptr(delta, "delta", (B, H, S), _torch().float32, dev)
     _check(load_library().attn_bwd_ex(ctypes.byref(p), _stream(stream)))
 

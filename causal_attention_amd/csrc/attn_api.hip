@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 150;  // 1.50: grouped-query, decode, RoPE, fp16 inputs, attn_params calls with 16-bit outputs
+constexpr int kAbiVersion = 160;  // 1.60: grouped-query, decode, RoPE, fp16 inputs, attn_params calls (16-bit outputs, strides)
 
 int check_common(int B, int H, int S, int D, int dtype) {
   if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_DTYPE;
@@ -62,6 +62,34 @@ int check_out(int dtype, int out_dtype) {
   return ATTN_ERR_DTYPE;
 }
 
+// Caller strides (attn_params.strides, NULL for the contiguous layout): each
+// given row needs non-negative batch and head strides, rows at least D
+// apart, and a panel (plus tile overhang) within 32-bit byte offsets.
+int check_strides(const int64_t (*st)[3], int S, int D, int in_bytes, int out_bytes) {
+  if (st == nullptr) return ATTN_OK;
+  for (int i = 0; i < 8; ++i) {
+    if (st[i][0] == 0 && st[i][1] == 0 && st[i][2] == 0) continue;
+    const int esize = (i == ATTN_STRIDE_O || i >= ATTN_STRIDE_DQ) ? out_bytes : in_bytes;
+    if (st[i][0] < 0 || st[i][1] < 0 || st[i][2] < D) return ATTN_ERR_STRIDE;
+    if (st[i][2] >= ((int64_t)1 << 31)) return ATTN_ERR_STRIDE;
+    // kernels form row offsets up to 255 rows past the end (tile overhang, read
+    // as zeros by the range check): those must not wrap 32 bits either
+    if (((int64_t)(S + 255) * st[i][2] + D) * esize >= ((int64_t)1 << 31)) return ATTN_ERR_STRIDE;
+  }
+  return ATTN_OK;
+}
+
+int elem_bytes(int dtype) { return dtype == ATTN_DTYPE_F32 ? 4 : 2; }
+
+// Contiguous layouts for every tensor, then the caller's strides where given.
+void set_layouts(attn::Args &a, const int64_t (*st)[3]) {
+  a.contiguous();
+  if (st == nullptr) return;
+  attn::Layout *dst[8] = {&a.lq, &a.lk, &a.lv, &a.lo, &a.ldo, &a.ldq, &a.ldk, &a.ldv};
+  for (int i = 0; i < 8; ++i)
+    if (st[i][0] != 0 || st[i][1] != 0 || st[i][2] != 0) *dst[i] = attn::Layout{st[i][0], st[i][1], (int)st[i][2]};
+}
+
 attn::Args make_args(int B, int H, int S, int D, float scale, int mask_mode, const int32_t *cu_seqlens,
                      int n_seqs, int max_seqlen, int dtype, void *stream) {
   attn::Args a{};
@@ -77,6 +105,7 @@ attn::Args make_args(int B, int H, int S, int D, float scale, int mask_mode, con
   a.max_seqlen = max_seqlen;
   a.dtype = dtype;
   a.stream = static_cast<hipStream_t>(stream);
+  a.contiguous();
   return a;
 }
 
@@ -103,6 +132,7 @@ const char *attn_status_string(int status) {
     case ATTN_ERR_HEADS: return "H_kv must divide H (1 <= H_kv <= H)";
     case ATTN_ERR_WORKSPACE: return "workspace NULL or smaller than attn_decode_workspace_bytes()";
     case ATTN_ERR_ROPE: return "RoPE table NULL or shorter than the positions (S, or max_seqlen for documents), or base not finite and > 0";
+    case ATTN_ERR_STRIDE: return "strides: batch and head >= 0, sequence >= D, panel extent < 2^31 bytes";
     default: return "unknown status";
   }
 }
@@ -112,7 +142,7 @@ const char *attn_status_string(int status) {
 static int fwd_all(const void *q, const void *k, const void *v, void *o, float *lse, bool with_rope,
                    const float *rope, int rope_npos, void *q_rot, void *k_rot, int B, int H, int H_kv, int S, int D,
                    float scale, int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype,
-                   int out_dtype, void *stream) {
+                   int out_dtype, const int64_t (*strides)[3], void *stream) {
   int st = check_common(B, H, S, D, dtype);
   if (st != ATTN_OK) return st;
   if ((st = check_out(dtype, out_dtype)) != ATTN_OK) return st;
@@ -122,17 +152,23 @@ static int fwd_all(const void *q, const void *k, const void *v, void *o, float *
   if ((st = check_mask(B, H, S, mask_mode, cu_seqlens, n_seqs, max_seqlen)) != ATTN_OK) return st;
   if ((st = check_scale(scale)) != ATTN_OK) return st;
   if (with_rope && (st = check_rope(rope, rope_npos, S, mask_mode, max_seqlen)) != ATTN_OK) return st;
+  if ((st = check_strides(strides, S, D, elem_bytes(dtype), elem_bytes(out_dtype))) != ATTN_OK) return st;
   attn::Args a = make_args(B, H, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
   a.H_kv = H_kv;
   a.out16 = out_dtype != ATTN_DTYPE_F32;
+  set_layouts(a, strides);
   a.q = q;
   a.k = k;
   if (with_rope) {
     a.rope = rope;
     a.rope_npos = rope_npos;
     if (attn::launch_rope(a, q_rot, k_rot) != hipSuccess) return ATTN_ERR_HIP;
-    a.q = q_rot;
+    a.q = q_rot;  // contiguous from here on
     a.k = k_rot;
+    const attn::Layout lv = a.lv, lo = a.lo;
+    a.contiguous();
+    a.lv = lv;
+    a.lo = lo;
   }
   a.v = v;
   a.o = o;
@@ -144,7 +180,7 @@ int attn_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *l
                  int D, float scale, int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype,
                  void *stream) {
   return fwd_all(q, k, v, o, lse, false, nullptr, 0, nullptr, nullptr, B, H, H_kv, S, D, scale, mask_mode,
-                 cu_seqlens, n_seqs, max_seqlen, dtype, ATTN_DTYPE_F32, stream);
+                 cu_seqlens, n_seqs, max_seqlen, dtype, ATTN_DTYPE_F32, nullptr, stream);
 }
 
 int attn_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int S, int D,
@@ -210,7 +246,8 @@ int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dO, con
 static int bwd_all(const void *q, const void *k, const void *v, const void *o, const void *dO, const float *lse,
                    void *dq, void *dk, void *dv, float *delta, bool with_rope, const float *rope, int rope_npos,
                    int B, int H, int H_kv, int S, int D, float scale, int mask_mode, const int32_t *cu_seqlens,
-                   int n_seqs, int max_seqlen, int dtype, int out_dtype, void *stream) {
+                   int n_seqs, int max_seqlen, int dtype, int out_dtype, const int64_t (*strides)[3],
+                   void *stream) {
   int st = check_common(B, H, S, D, dtype);
   if (st != ATTN_OK) return st;
   if ((st = check_out(dtype, out_dtype)) != ATTN_OK) return st;
@@ -219,9 +256,15 @@ static int bwd_all(const void *q, const void *k, const void *v, const void *o, c
   if ((st = check_mask(B, H, S, mask_mode, cu_seqlens, n_seqs, max_seqlen)) != ATTN_OK) return st;
   if ((st = check_scale(scale)) != ATTN_OK) return st;
   if (with_rope && (st = check_rope(rope, rope_npos, S, mask_mode, max_seqlen)) != ATTN_OK) return st;
+  if ((st = check_strides(strides, S, D, elem_bytes(dtype), elem_bytes(out_dtype))) != ATTN_OK) return st;
   attn::Args a = make_args(B, H, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
   a.H_kv = H_kv;
   a.out16 = out_dtype != ATTN_DTYPE_F32;
+  set_layouts(a, strides);
+  if (with_rope) {  // the kernels read the contiguous q_rot and k_rot
+    a.lq = attn::Layout{(int64_t)H * S * D, (int64_t)S * D, D};
+    a.lk = attn::Layout{(int64_t)H_kv * S * D, (int64_t)S * D, D};
+  }
   a.rope = rope;
   a.rope_npos = rope_npos;
   a.q = q;
@@ -253,7 +296,7 @@ int attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o, co
                  float *dq, float *dk, float *dv, float *delta, int B, int H, int H_kv, int S, int D, float scale,
                  int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype, void *stream) {
   return bwd_all(q, k, v, o, dO, lse, dq, dk, dv, delta, false, nullptr, 0, B, H, H_kv, S, D, scale, mask_mode,
-                 cu_seqlens, n_seqs, max_seqlen, dtype, ATTN_DTYPE_F32, stream);
+                 cu_seqlens, n_seqs, max_seqlen, dtype, ATTN_DTYPE_F32, nullptr, stream);
 }
 
 int attn_bwd(const void *q, const void *k, const void *v, const float *o, const void *dO, const float *lse,
@@ -282,6 +325,7 @@ int attn_rope(const void *q, const void *k, void *q_rot, void *k_rot, const floa
   if ((st = check_rope(tab, n_pos, S, mask_mode, max_seqlen)) != ATTN_OK) return st;
   attn::Args a = make_args(B, H, S, D, 1.f, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
   a.H_kv = H_kv;
+  a.contiguous();
   a.q = q;
   a.k = k;
   a.rope = tab;
@@ -293,7 +337,7 @@ int attn_fwd_rope(const void *q, const void *k, const void *v, void *q_rot, void
                   const float *tab, int n_pos, int B, int H, int H_kv, int S, int D, float scale, int mask_mode,
                   const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype, void *stream) {
   return fwd_all(q, k, v, o, lse, true, tab, n_pos, q_rot, k_rot, B, H, H_kv, S, D, scale, mask_mode, cu_seqlens,
-                 n_seqs, max_seqlen, dtype, ATTN_DTYPE_F32, stream);
+                 n_seqs, max_seqlen, dtype, ATTN_DTYPE_F32, nullptr, stream);
 }
 
 int attn_bwd_rope(const void *q_rot, const void *k_rot, const void *v, const float *o, const void *dO,
@@ -301,7 +345,7 @@ int attn_bwd_rope(const void *q_rot, const void *k_rot, const void *v, const flo
                   int H, int H_kv, int S, int D, float scale, int mask_mode, const int32_t *cu_seqlens, int n_seqs,
                   int max_seqlen, int dtype, void *stream) {
   return bwd_all(q_rot, k_rot, v, o, dO, lse, dq, dk, dv, delta, true, tab, n_pos, B, H, H_kv, S, D, scale,
-                 mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, ATTN_DTYPE_F32, stream);
+                 mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, ATTN_DTYPE_F32, nullptr, stream);
 }
 
 int attn_fwd_ex(const attn_params *p, void *stream) {
@@ -310,7 +354,7 @@ int attn_fwd_ex(const attn_params *p, void *stream) {
   const bool rope = p->rope_table != nullptr;
   return fwd_all(p->q, p->k, p->v, p->o, p->lse, rope, p->rope_table, p->rope_npos, p->q_rot, p->k_rot, p->B, p->H,
                  H_kv, p->S, p->D, p->scale, p->mask_mode, p->cu_seqlens, p->n_seqs, p->max_seqlen, p->dtype,
-                 p->out_dtype, stream);
+                 p->out_dtype, p->strides, stream);
 }
 
 int attn_bwd_ex(const attn_params *p, void *stream) {
@@ -319,7 +363,7 @@ int attn_bwd_ex(const attn_params *p, void *stream) {
   const bool rope = p->rope_table != nullptr;
   return bwd_all(rope ? p->q_rot : p->q, rope ? p->k_rot : p->k, p->v, p->o, p->dO, p->lse, p->dq, p->dk, p->dv,
                  p->delta, rope, p->rope_table, p->rope_npos, p->B, p->H, H_kv, p->S, p->D, p->scale, p->mask_mode,
-                 p->cu_seqlens, p->n_seqs, p->max_seqlen, p->dtype, p->out_dtype, stream);
+                 p->cu_seqlens, p->n_seqs, p->max_seqlen, p->dtype, p->out_dtype, p->strides, stream);
 }
 
 size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int D, int max_len) {

@@ -33,7 +33,8 @@ namespace attn {
 template <typename T, typename OT, int D>
 __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const OT *__restrict__ o,
                                                                   const T *__restrict__ dO,
-                                                                  float *__restrict__ delta, int rows) {
+                                                                  float *__restrict__ delta, int rows, int S, int H,
+                                                                  Layout lo, Layout ldo) {
   constexpr int VEC = 16 / sizeof(T);  // dO elements per 16-byte load
   constexpr int LPR = D / VEC;         // lanes per row
   constexpr int RPB = 256 / LPR;       // rows per block per step
@@ -43,8 +44,10 @@ __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const OT *__re
     const int row = row0 + tid / LPR;
     float acc = 0.f;
     if (row < rows) {
-      const T *dp = dO + (size_t)row * D + sub * VEC;
-      const OT *op = o + (size_t)row * D + sub * VEC;
+      const int bh = row / S;  // row of Delta [B, H, S] -> (batch, head, position)
+      const int s = row - bh * S;
+      const T *dp = dO + panel_off(ldo, bh / H, bh % H) + (size_t)s * ldo.ss + sub * VEC;
+      const OT *op = o + panel_off(lo, bh / H, bh % H) + (size_t)s * lo.ss + sub * VEC;
       if constexpr (sizeof(T) == 2) {
         const typename Elem<T>::frag g = *reinterpret_cast<const typename Elem<T>::frag *>(dp);
         float ov[8];
@@ -88,7 +91,8 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, OT *__restrict__ dk,
     OT *__restrict__ dv, int S, float c2, float scale, const int32_t *__restrict__ cu, int ntiles, int n_seqs,
-    int H, int G, const float *__restrict__ rope, int rope_npos) {
+    int H, int G, const float *__restrict__ rope, int rope_npos, Layout lq, Layout lk, Layout lv, Layout ldo,
+    Layout ldk, Layout ldv) {
   constexpr int NW = 4;
   constexpr int NT = NW * kWaveSize;
   constexpr int BN = NW * 32;  // keys per workgroup
@@ -120,10 +124,11 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   // t.head is a key/value head; its G query heads are qh0 .. qh0 + G - 1, and
   // dK, dV sum over all of them (the query-tile loop runs over the group).
   const int Hkv = H / G;
-  const int qh0 = (t.head / Hkv) * H + (t.head % Hkv) * G;
-  const size_t base = (size_t)t.head * S * D;
-  const GBuf gk(k + base, (uint32_t)(t.r_end * D * sizeof(T)));
-  const GBuf gv(v + base, (uint32_t)(t.r_end * D * sizeof(T)));
+  const int bi = t.head / Hkv;   // batch entry
+  const int hk = t.head % Hkv;   // key/value head; its query heads are hk*G .. hk*G + G - 1
+  const int qh0 = bi * H + hk * G;  // the first one's (batch, head) index into LSE and Delta
+  const GBuf gk(k + panel_off(lk, bi, hk), panel_bytes(lk, t.r_end, D, sizeof(T)));
+  const GBuf gv(v + panel_off(lv, bi, hk), panel_bytes(lv, t.r_end, D, sizeof(T)));
 
   const int w0 = t.r_start + wave * 32;  // first key of this wave
   const bool wave_active = w0 < t.r_end;
@@ -137,18 +142,21 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   auto oslot = [&]<int P>() { return lds_cast(P == 0 ? sO0 : sO1); };
   auto lslot = [&]<int P>() { return lds_cast(P == 0 ? sL0 : sL1); };
   auto dslot = [&]<int P>() { return lds_cast(P == 0 ? sD0 : sD1); };
+  uint32_t qoff[QTile::kPerWave], dooff[QTile::kPerWave];
+  QTile::lane_offsets(qoff, wave, lane, lq.ss);
+  QTile::lane_offsets(dooff, wave, lane, ldo.ss);
   auto issue = [&]<int P>(int it) {
     const int g = it / ntq;
     const int q0 = q_lo + (it - g * ntq) * BMQ;
     const size_t rbase = (size_t)(qh0 + g) * S;
     // Queries past the segment read as zeros (Q, dO, LSE, Delta all 0): their
     // P is 1 but dO and Q are 0, so they add nothing to dV or dK.
-    const GBuf gq(q + rbase * D, (uint32_t)(t.seg_end * D * sizeof(T)));
-    const GBuf gdo(dO + rbase * D, (uint32_t)(t.seg_end * D * sizeof(T)));
+    const GBuf gq(q + panel_off(lq, bi, hk * G + g), panel_bytes(lq, t.seg_end, D, sizeof(T)));
+    const GBuf gdo(dO + panel_off(ldo, bi, hk * G + g), panel_bytes(ldo, t.seg_end, D, sizeof(T)));
     const GBuf glse(lse + rbase, (uint32_t)(t.seg_end * sizeof(float)));
     const GBuf gdel(delta + rbase, (uint32_t)(t.seg_end * sizeof(float)));
-    QTile::issue(gq, qslot.template operator()<P>(), q0, wave, lane);
-    QTile::issue(gdo, oslot.template operator()<P>(), q0, wave, lane);
+    QTile::issue_at(gq, qslot.template operator()<P>(), QTile::row0_bytes(q0, lq.ss), qoff, wave);
+    QTile::issue_at(gdo, oslot.template operator()<P>(), QTile::row0_bytes(q0, ldo.ss), dooff, wave);
     if (wave == 0) dma_vec64(glse, lslot.template operator()<P>(), q0, lane);
     if (wave == 1) dma_vec64(gdel, dslot.template operator()<P>(), q0, lane);
   };
@@ -163,12 +171,16 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   if constexpr (kKVRegs) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      kf[kb] = global_frag<T, D>(gk, key, 16 * kb + 8 * hh);
-      vf[kb] = global_frag<T, D>(gv, key, 16 * kb + 8 * hh);
+      kf[kb] = global_frag_rs<T>(gk, key, 16 * kb + 8 * hh, lk.ss);
+      vf[kb] = global_frag_rs<T>(gv, key, 16 * kb + 8 * hh, lv.ss);
     }
   }
-  auto kfrag = [&](int kb) { return kKVRegs ? kf[kKVRegs ? kb : 0] : global_frag<T, D>(gk, key, 16 * kb + 8 * hh); };
-  auto vfrag = [&](int kb) { return kKVRegs ? vf[kKVRegs ? kb : 0] : global_frag<T, D>(gv, key, 16 * kb + 8 * hh); };
+  auto kfrag = [&](int kb) {
+    return kKVRegs ? kf[kKVRegs ? kb : 0] : global_frag_rs<T>(gk, key, 16 * kb + 8 * hh, lk.ss);
+  };
+  auto vfrag = [&](int kb) {
+    return kKVRegs ? vf[kKVRegs ? kb : 0] : global_frag_rs<T>(gv, key, 16 * kb + 8 * hh, lv.ss);
+  };
   f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -245,8 +257,8 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   }
 
   if (!wave_active) return;
-  const GBuf gdk(dk + base, (uint32_t)(t.r_end * D * sizeof(OT)));
-  const GBuf gdv(dv + base, (uint32_t)(t.r_end * D * sizeof(OT)));
+  const GBuf gdk(dk + panel_off(ldk, bi, hk), panel_bytes(ldk, t.r_end, D, sizeof(OT)));
+  const GBuf gdv(dv + panel_off(ldv, bi, hk), panel_bytes(ldv, t.r_end, D, sizeof(OT)));
   // RoPE: this key's table row (keys past the tile end are not stored)
   const float *rrow =
       rope == nullptr ? nullptr : rope + (size_t)min(min(key, t.r_end - 1) - t.seg_start, rope_npos - 1) * D;
@@ -261,9 +273,9 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
         b4[i] = dvacc[db][4 * g + i];
       }
       if (rope != nullptr) rope_back(a4, *reinterpret_cast<const f32x4 *>(rrow + db * 32 + 8 * g + 4 * hh));
-      const uint32_t e = (uint32_t)(key * D + db * 32 + 8 * g + 4 * hh);
-      store_out4<OT>(gdk, a4, e);
-      store_out4<OT>(gdv, b4, e);
+      const uint32_t col = (uint32_t)(db * 32 + 8 * g + 4 * hh);
+      store_out4<OT>(gdk, a4, (uint32_t)key * ldk.ss + col);
+      store_out4<OT>(gdv, b4, (uint32_t)key * ldv.ss + col);
     }
   }
 }
@@ -291,7 +303,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
     const float *__restrict__ lse, const float *__restrict__ delta, const OT *__restrict__ o,
     float *__restrict__ delta_out, OT *__restrict__ dq, int S, float c2, float scale,
     const int32_t *__restrict__ cu, int ntiles, int n_seqs, int H, int G, const float *__restrict__ rope,
-    int rope_npos) {
+    int rope_npos, Layout lq, Layout lk, Layout lv, Layout ldo, Layout lo, Layout ldq) {
   constexpr int NW = 4;
   constexpr int NT = NW * kWaveSize;
   constexpr int BM = NW * 32;
@@ -316,13 +328,13 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
   const int lane = tid % kWaveSize;
   const int hh = lane / 32;
   const int c = lane % 32;
-  const size_t base = (size_t)t.head * S * D;                      // this query head
-  const size_t kvbase = (size_t)kv_head_of(t.head, H, G) * S * D;  // its key/value head
+  const int bi = t.head / H;  // batch entry
+  const int hq = t.head % H;  // query head, and its key/value head hq / G
   const size_t rbase = (size_t)t.head * S;
-  const GBuf gq(q + base, (uint32_t)(t.r_end * D * sizeof(T)));
-  const GBuf gdo(dO + base, (uint32_t)(t.r_end * D * sizeof(T)));
-  const GBuf gk(k + kvbase, (uint32_t)(t.seg_end * D * sizeof(T)));
-  const GBuf gv(v + kvbase, (uint32_t)(t.seg_end * D * sizeof(T)));
+  const GBuf gq(q + panel_off(lq, bi, hq), panel_bytes(lq, t.r_end, D, sizeof(T)));
+  const GBuf gdo(dO + panel_off(ldo, bi, hq), panel_bytes(ldo, t.r_end, D, sizeof(T)));
+  const GBuf gk(k + panel_off(lk, bi, hq / G), panel_bytes(lk, t.seg_end, D, sizeof(T)));
+  const GBuf gv(v + panel_off(lv, bi, hq / G), panel_bytes(lv, t.seg_end, D, sizeof(T)));
   const GBuf glse(lse + rbase, (uint32_t)(t.r_end * sizeof(float)));
   const GBuf gdel(delta + rbase, (uint32_t)(t.r_end * sizeof(float)));
 
@@ -337,17 +349,21 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
 
   auto kslot = [&]<int P>() { return lds_cast(P == 0 ? sK0 : sK1); };
   auto vslot = [&]<int P>() { return lds_cast(P == 0 ? sV0 : sV1); };
+  uint32_t koff[KTile::kPerWave], voff[KTile::kPerWave];
+  KTile::lane_offsets(koff, wave, lane, lk.ss);
+  KTile::lane_offsets(voff, wave, lane, lv.ss);
   auto issue = [&]<int P>(int j) {
-    KTile::issue(gk, kslot.template operator()<P>(), kv_lo + j * BN, wave, lane);
-    KTile::issue(gv, vslot.template operator()<P>(), kv_lo + j * BN, wave, lane);
+    const int r0 = kv_lo + j * BN;
+    KTile::issue_at(gk, kslot.template operator()<P>(), KTile::row0_bytes(r0, lk.ss), koff, wave);
+    KTile::issue_at(gv, vslot.template operator()<P>(), KTile::row0_bytes(r0, lv.ss), voff, wave);
   };
   issue.template operator()<0>(0);
 
   frag qf[KB], df[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    qf[kb] = global_frag<T, D>(gq, qi, 16 * kb + 8 * hh);
-    df[kb] = global_frag<T, D>(gdo, qi, 16 * kb + 8 * hh);
+    qf[kb] = global_frag_rs<T>(gq, qi, 16 * kb + 8 * hh, lq.ss);
+    df[kb] = global_frag_rs<T>(gdo, qi, 16 * kb + 8 * hh, ldo.ss);
   }
   const float l2 = glse.load4((uint32_t)qi * 4) * kLog2e;
   float dl;
@@ -358,12 +374,12 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
     // Fragment kb of this lane is sub-block 2*kb + hh, so the lane computes
     // the butterfly's tree over its own sub-blocks and one swap across the
     // halves adds the other half's.
-    const GBuf go(o + base, (uint32_t)(t.r_end * D * sizeof(OT)));
+    const GBuf go(o + panel_off(lo, bi, hq), panel_bytes(lo, t.r_end, D, sizeof(OT)));
     float part[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       float ov[8];
-      load_out8<OT>(go, (uint32_t)(qi * D + 16 * kb + 8 * hh), ov);
+      load_out8<OT>(go, (uint32_t)(qi * lo.ss + 16 * kb + 8 * hh), ov);
       float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc += (float)df[kb][i] * ov[i];
@@ -433,7 +449,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
   }
 
   if (!wave_active) return;
-  const GBuf gdq(dq + base, (uint32_t)(t.r_end * D * sizeof(OT)));
+  const GBuf gdq(dq + panel_off(ldq, bi, hq), panel_bytes(ldq, t.r_end, D, sizeof(OT)));
   // RoPE: this query's table row (queries past the tile end are not stored)
   const float *rrow =
       rope == nullptr ? nullptr : rope + (size_t)min(min(qi, t.r_end - 1) - t.seg_start, rope_npos - 1) * D;
@@ -445,7 +461,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) a4[i] = dqacc[db][4 * g + i] * scale;
       if (rope != nullptr) rope_back(a4, *reinterpret_cast<const f32x4 *>(rrow + db * 32 + 8 * g + 4 * hh));
-      store_out4<OT>(gdq, a4, (uint32_t)(qi * D + db * 32 + 8 * g + 4 * hh));
+      store_out4<OT>(gdq, a4, (uint32_t)(qi * ldq.ss + db * 32 + 8 * g + 4 * hh));
     }
   }
 }
@@ -490,7 +506,8 @@ static hipError_t launch_pre_t(const Args &a) {
   const int rows = a.B * a.H * a.S;
   const int blocks = min((rows + RPB - 1) / RPB, 65536);
   hipLaunchKernelGGL((attn_bwd_preprocess_kernel<T, OT, D>), dim3(blocks), dim3(256), 0, a.stream,
-                     static_cast<const OT *>(a.o_in), static_cast<const T *>(a.dO), a.delta, rows);
+                     static_cast<const OT *>(a.o_in), static_cast<const T *>(a.dO), a.delta, rows, a.S, a.H, a.lo,
+                     a.ldo);
   return hipGetLastError();
 }
 
@@ -513,7 +530,7 @@ static hipError_t launch_dkdv_t(const Args &a) {
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
                      static_cast<const T *>(a.dO), a.lse_in, a.delta_in, static_cast<OT *>(a.dk),
                      static_cast<OT *>(a.dv), a.S, c2, a.scale, a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv,
-                     a.rope, a.rope_npos);
+                     a.rope, a.rope_npos, a.lq, a.lk, a.lv, a.ldo, a.ldk, a.ldv);
   return hipGetLastError();
 }
 
@@ -536,7 +553,7 @@ static hipError_t launch_dq_t(const Args &a) {
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
                      static_cast<const T *>(a.dO), a.lse_in, a.delta_in, static_cast<const OT *>(a.o_in), a.delta,
                      static_cast<OT *>(a.dq), a.S, c2, a.scale, a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv,
-                     a.rope, a.rope_npos);
+                     a.rope, a.rope_npos, a.lq, a.lk, a.lv, a.ldo, a.lo, a.ldq);
   return hipGetLastError();
 }
 

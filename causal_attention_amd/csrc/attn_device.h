@@ -22,6 +22,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include "attn_launch.h"  // Layout
 
 namespace attn {
 
@@ -305,8 +306,28 @@ __device__ __forceinline__ void store_out4(const GBuf &g, const f32x4 &v, uint32
   }
 }
 
-// An 8-slot fragment of row `row`, columns [col, col + 8), of a row-major
-// [*, D] array behind `g` (zeros past the resource's end).
+// An 8-slot fragment of row `row`, columns [col, col + 8), of rows `ss`
+// elements apart behind `g` (zeros past the resource's end).
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::frag global_frag_rs(const GBuf &g, int row, int col, int ss) {
+  using frag = typename Elem<T>::frag;
+  const uint32_t off = (uint32_t)(row * ss + col) * sizeof(T);
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(frag, g.load16(off));
+  } else {
+    const u32x4 a = g.load16(off);
+    const u32x4 b = g.load16(off + 16);
+    u32x8 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[i] = a[i];
+      w[4 + i] = b[i];
+    }
+    return __builtin_bit_cast(frag, w);
+  }
+}
+
+// The same for a row-major [*, D] array (rows D elements apart).
 template <typename T, int D>
 __device__ __forceinline__ typename Elem<T>::frag global_frag(const GBuf &g, int row, int col) {
   using frag = typename Elem<T>::frag;
@@ -430,6 +451,36 @@ template <typename T, int R, int D, int NT, bool SWIZZLE> struct DmaTile {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           g.r, (lds_void *)(tile + blk * (1024 / sizeof(T))), 16,
           (((uint32_t)r0 + row) * D + col) * (uint32_t)sizeof(T), 0, 0, 0);
+    }
+  }
+
+  // The same copy from rows `ss` elements apart (a strided view of the rows),
+  // in two parts: lane_offsets() gives each lane's byte offset inside a tile
+  // (row times ss, plus the swizzled column), once per kernel; issue_at()
+  // adds the tile's first-row offset, which is uniform and kept in a scalar
+  // register (row0_bytes() makes it one), so each copy costs one vector add.
+  // The whole offset still goes through the range-checked vector offset.
+  __device__ __forceinline__ static void lane_offsets(uint32_t (&off)[kPerWave], int wave, int lane, uint32_t ss) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int blk = wave * kPerWave + i;
+      const int p = blk * kWaveSize + lane;
+      const uint32_t row = (uint32_t)p / kCPR;
+      const uint32_t chunk = (uint32_t)(p % kCPR) ^ (SWIZZLE ? swz_mask<T, D>(row) : 0u);
+      off[i] = (row * ss + chunk * kVec) * (uint32_t)sizeof(T);
+    }
+  }
+  __device__ __forceinline__ static uint32_t row0_bytes(int r0, uint32_t ss) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)r0 * ss * (uint32_t)sizeof(T));
+  }
+  __device__ __forceinline__ static void issue_at(const GBuf &g, lds_t<T> *tile, uint32_t r0_bytes,
+                                                  const uint32_t (&off)[kPerWave], int wave) {
+    typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int blk = wave * kPerWave + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g.r, (lds_void *)(tile + blk * (1024 / sizeof(T))), 16,
+                                               off[i] + r0_bytes, 0, 0, 0);
     }
   }
 };
@@ -628,6 +679,15 @@ __device__ __forceinline__ void rope_back(f32x4 &a, const f32x4 cs) {
   a[1] = x1 * cs[0] - x0 * cs[1];
   a[2] = x2 * cs[2] + x3 * cs[3];
   a[3] = x3 * cs[2] - x2 * cs[3];
+}
+
+// Offset of the (b, h) panel of a tensor with layout L (Layout: attn_launch.h).
+__device__ __forceinline__ size_t panel_off(const Layout &L, int b, int h) {
+  return (size_t)((int64_t)b * L.sb + (int64_t)h * L.sh);
+}
+// Bytes from a panel's first element to the end of row `rows - 1`.
+__device__ __forceinline__ uint32_t panel_bytes(const Layout &L, int rows, int D, int esize) {
+  return (uint32_t)(((rows - 1) * L.ss + D) * esize);
 }
 
 // Tile schedule.  Workgroups are dealt to the 8 XCDs round-robin (block b

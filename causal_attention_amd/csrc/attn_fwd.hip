@@ -38,7 +38,8 @@ template <typename T, typename OT, int D, int NW, int BN, int MINB, bool DOC>
 __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                                  const T *__restrict__ v, OT *__restrict__ o,
                                                                  float *__restrict__ lse, int S, float c2,
-                                                                 const int32_t *__restrict__ cu, int ntiles, int n_seqs, int H, int G) {
+                                                                 const int32_t *__restrict__ cu, int ntiles, int n_seqs, int H, int G,
+                                                                 Layout lq, Layout lk, Layout lv, Layout lo) {
   constexpr int NT = NW * kWaveSize;
   constexpr int BM = NW * 32;  // query rows per workgroup
   constexpr int KB = D / 16;   // k-blocks over the head dimension
@@ -67,11 +68,11 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
   const int lane = tid % kWaveSize;
   const int hh = lane / 32;
   const int c = lane % 32;
-  const size_t base = (size_t)t.head * S * D;                      // this query head
-  const size_t kvbase = (size_t)kv_head_of(t.head, H, G) * S * D;  // its key/value head
-  const GBuf gq(q + base, (uint32_t)(t.r_end * D * sizeof(T)));
-  const GBuf gk(k + kvbase, (uint32_t)(t.seg_end * D * sizeof(T)));
-  const GBuf gv(v + kvbase, (uint32_t)(t.seg_end * D * sizeof(T)));
+  const int bi = t.head / H;  // batch entry
+  const int hq = t.head % H;  // query head, and its key/value head hq / G
+  const GBuf gq(q + panel_off(lq, bi, hq), panel_bytes(lq, t.r_end, D, sizeof(T)));
+  const GBuf gk(k + panel_off(lk, bi, hq / G), panel_bytes(lk, t.seg_end, D, sizeof(T)));
+  const GBuf gv(v + panel_off(lv, bi, hq / G), panel_bytes(lv, t.seg_end, D, sizeof(T)));
 
   const int w0 = t.r_start + wave * 32;  // first query of this wave
   const bool wave_active = w0 < t.r_end;
@@ -83,15 +84,19 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
 
   auto kslot = [&]<int P>() { return lds_cast(P == 0 ? sK0 : sK1); };
   auto vslot = [&]<int P>() { return lds_cast(P == 0 ? sV0 : sV1); };
+  uint32_t koff[KTile::kPerWave], voff[VTile::kPerWave];
+  KTile::lane_offsets(koff, wave, lane, lk.ss);
+  VTile::lane_offsets(voff, wave, lane, lv.ss);
   auto issue = [&]<int P>(int tile) {
-    KTile::issue(gk, kslot.template operator()<P>(), kv_lo + tile * BN, wave, lane);
-    VTile::issue(gv, vslot.template operator()<P>(), kv_lo + tile * BN, wave, lane);
+    const int r0 = kv_lo + tile * BN;
+    KTile::issue_at(gk, kslot.template operator()<P>(), KTile::row0_bytes(r0, lk.ss), koff, wave);
+    VTile::issue_at(gv, vslot.template operator()<P>(), VTile::row0_bytes(r0, lv.ss), voff, wave);
   };
   issue.template operator()<0>(0);
 
   frag qf[KB];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) qf[kb] = global_frag<T, D>(gq, w0 + c, 16 * kb + 8 * hh);
+  for (int kb = 0; kb < KB; ++kb) qf[kb] = global_frag_rs<T>(gq, w0 + c, 16 * kb + 8 * hh, lq.ss);
 
   f32x16 oacc[DB];
   float m = -INFINITY;  // reference max (scaled, base 2)
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
   }
 
   if (!wave_active) return;
-  const GBuf go(o + base, (uint32_t)(t.r_end * D * sizeof(OT)));
+  const GBuf go(o + panel_off(lo, bi, hq), panel_bytes(lo, t.r_end, D, sizeof(OT)));
   const int qi = w0 + c;
   const float lt = l + swap_halves(l);
   const float inv = 1.0f / lt;
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
       f32x4 val;
 #pragma unroll
       for (int i = 0; i < 4; ++i) val[i] = oacc[db][4 * g + i] * inv;
-      store_out4<OT>(go, val, (uint32_t)(qi * D + db * 32 + 8 * g + 4 * hh));
+      store_out4<OT>(go, val, (uint32_t)(qi * lo.ss + db * 32 + 8 * g + 4 * hh));
     }
   }
   if (lse != nullptr && hh == 0 && qi < t.r_end) lse[(size_t)t.head * S + qi] = (m + __log2f(lt)) * kLn2;
@@ -259,7 +264,8 @@ static hipError_t launch_fwd_t(const Args &a) {
   }
   hipLaunchKernelGGL((attn_fwd_kernel<T, OT, D, NW, BN, MINB, DOC>), grid, block, 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
-                     static_cast<OT *>(a.o), a.lse, a.S, c2, a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv);
+                     static_cast<OT *>(a.o), a.lse, a.S, c2, a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv,
+                     a.lq, a.lk, a.lv, a.lo);
   return hipGetLastError();
 }
 

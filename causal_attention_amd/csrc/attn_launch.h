@@ -5,6 +5,16 @@
 #include <stdint.h>
 
 namespace attn {
+// Element strides of one [B, H, S, D] tensor whose D elements are
+// contiguous: batch, head and row (sequence position).  The contiguous layout
+// is {H*S*D, S*D, D}.
+struct Layout {
+  int64_t sb, sh;
+  int ss;
+};
+}  // namespace attn
+
+namespace attn {
 
 // Validated arguments of one call (the C ABI fills this after checking them).
 struct Args {
@@ -24,7 +34,16 @@ struct Args {
   bool out16;               // O, dQ, dK, dV in the input dtype (16-bit inputs only)
   const float *rope;        // RoPE table [rope_npos][D/2][2] (cos, sin), or NULL: dQ and dK
   int rope_npos;            // epilogues turn the gradients back by the row's angles
+  // element strides of each [B, H(_kv), S, D] tensor (contiguous unless the caller gives others)
+  Layout lq, lk, lv, lo, ldo, ldq, ldk, ldv;
   hipStream_t stream;
+  // the contiguous layout for every tensor (k, v, dk, dv with H_kv heads)
+  void contiguous() {
+    const Layout qs{(int64_t)H * S * D, (int64_t)S * D, D};
+    const Layout ks{(int64_t)H_kv * S * D, (int64_t)S * D, D};
+    lq = lo = ldo = ldq = qs;
+    lk = lv = ldk = ldv = ks;
+  }
 };
 
 // Decode step against a key/value cache (attn_decode).

@@ -75,13 +75,14 @@ template <> struct Row8<float> {
 // Grid (flat): position block fastest, then batch entry, then group of HPT heads.  A thread owns one
 // 8-element chunk of one position and rotates it in HPT heads (query heads
 // 0 .. H-1, then key heads H .. H+H_kv-1): the chunk's table values are read
-// once and the HPT loads are in flight together.  q_rot may be q and k_rot may
-// be k (each thread reads its elements before writing them), so no restrict.
+// once and the HPT loads are in flight together.  q_rot and k_rot are
+// contiguous; with contiguous q and k they may be q and k themselves (each
+// thread reads its elements before writing them), so no restrict.
 template <typename T, int D, bool DOC, int HPT>
 __global__ __launch_bounds__(256) void attn_rope_kernel(const T *q, const T *k, T *qr, T *kr,
                                                         const float *__restrict__ tab, int n_pos, int H, int Hkv,
                                                         int B, int S, int nsb, const int32_t *__restrict__ cu,
-                                                        int n_seqs) {
+                                                        int n_seqs, Layout lq, Layout lk) {
   constexpr int CPR = D / 8;  // 8-element chunks per row
   const int pb = blockIdx.x % nsb;
   const int b = (blockIdx.x / nsb) % B;
@@ -105,13 +106,17 @@ __global__ __launch_bounds__(256) void attn_rope_kernel(const T *q, const T *k, 
   const f32x4 *t4 = reinterpret_cast<const f32x4 *>(tab + (size_t)pos * D + ch * 8);
   const f32x4 cs0 = t4[0], cs1 = t4[1];  // (cos, sin) of this chunk's four pairs
 
-  auto row = [&](int h) -> size_t {  // element offset of this chunk in head h's row s
-    return h < H ? ((size_t)(b * H + h) * S + s) * D + ch * 8 : ((size_t)(b * Hkv + h - H) * S + s) * D + ch * 8;
+  auto src = [&](int h) -> const T * {  // this chunk of head h's row s (q and k may be strided views)
+    return h < H ? q + panel_off(lq, b, h) + (size_t)s * lq.ss + ch * 8
+                 : k + panel_off(lk, b, h - H) + (size_t)s * lk.ss + ch * 8;
+  };
+  auto dst = [&](int h) -> T * {  // q_rot and k_rot are contiguous
+    return h < H ? qr + ((size_t)(b * H + h) * S + s) * D + ch * 8 : kr + ((size_t)(b * Hkv + h - H) * S + s) * D + ch * 8;
   };
   float x[HPT][8];
 #pragma unroll
   for (int j = 0; j < HPT; ++j)
-    if (h0 + j < H + Hkv) Row8<T>::load((h0 + j < H ? q : k) + row(h0 + j), x[j]);
+    if (h0 + j < H + Hkv) Row8<T>::load(src(h0 + j), x[j]);
 #pragma unroll
   for (int j = 0; j < HPT; ++j) {
     if (h0 + j >= H + Hkv) break;
@@ -123,7 +128,7 @@ __global__ __launch_bounds__(256) void attn_rope_kernel(const T *q, const T *k, 
       y[2 * p] = x[j][2 * p] * c - x[j][2 * p + 1] * sn;
       y[2 * p + 1] = x[j][2 * p] * sn + x[j][2 * p + 1] * c;
     }
-    Row8<T>::store((h0 + j < H ? qr : kr) + row(h0 + j), y);
+    Row8<T>::store(dst(h0 + j), y);
   }
 }
 
@@ -146,10 +151,10 @@ static hipError_t launch_rope_t(const Args &a, void *q_rot, void *k_rot) {
   T *kr = static_cast<T *>(k_rot);
   if (a.doc)
     hipLaunchKernelGGL((attn_rope_kernel<T, D, true, HPT>), grid, dim3(256), 0, a.stream, q, k, qr, kr, a.rope,
-                       a.rope_npos, a.H, a.H_kv, a.B, a.S, nsb, a.cu_seqlens, a.n_seqs);
+                       a.rope_npos, a.H, a.H_kv, a.B, a.S, nsb, a.cu_seqlens, a.n_seqs, a.lq, a.lk);
   else
     hipLaunchKernelGGL((attn_rope_kernel<T, D, false, HPT>), grid, dim3(256), 0, a.stream, q, k, qr, kr, a.rope,
-                       a.rope_npos, a.H, a.H_kv, a.B, a.S, nsb, a.cu_seqlens, a.n_seqs);
+                       a.rope_npos, a.H, a.H_kv, a.B, a.S, nsb, a.cu_seqlens, a.n_seqs, a.lq, a.lk);
   return hipGetLastError();
 }
 

@@ -76,8 +76,9 @@ typedef enum attn_status {
   ATTN_ERR_SCALE = -9,         /* scale not finite or not > 0                      */
   ATTN_ERR_HEADS = -10,        /* H_kv not a divisor of H (grouped-query calls)    */
   ATTN_ERR_WORKSPACE = -11,    /* decode workspace missing or too small            */
-  ATTN_ERR_ROPE = -12          /* RoPE table NULL or shorter than the positions,
+  ATTN_ERR_ROPE = -12,         /* RoPE table NULL or shorter than the positions,
                                   or base not finite and > 0                       */
+  ATTN_ERR_STRIDE = -13        /* attn_params strides out of range                 */
 } attn_status;
 
 enum { ATTN_MASK_CAUSAL = 0, ATTN_MASK_DOC_CAUSAL = 1 };
@@ -274,8 +275,22 @@ int attn_bwd_rope(const void *q_rot, const void *k_rot, const void *v, const flo
  *   rope_table    NULL: no RoPE.  Else a table from attn_rope_table with
  *   rope_npos     rope_npos positions (>= S, or >= max_seqlen for packed
  *                 documents; else ATTN_ERR_ROPE).
- *   q_rot, k_rot  with RoPE: the rotated q and k in `dtype` (caller-owned),
- *                 written by attn_fwd_ex and read by attn_bwd_ex.
+ *   q_rot, k_rot  with RoPE: the rotated q and k in `dtype` (caller-owned,
+ *                 contiguous), written by attn_fwd_ex and read by
+ *                 attn_bwd_ex.
+ *   strides       element strides {batch, head, sequence} of q, k, v, o, dO,
+ *                 dq, dk, dv (ATTN_STRIDE_Q ... ATTN_STRIDE_DV); the D
+ *                 elements of a row are always contiguous.  A row of zeros
+ *                 means that tensor is contiguous [B, H, S, D] (H_kv heads
+ *                 for k, v, dk, dv), so a zero-initialised struct is the
+ *                 contiguous layout.  This is how [B, S, H, D] tensors
+ *                 ({S*H*D, D, H*D}) or q, k, v slices of a fused projection
+ *                 are passed without copies.  Each given row needs batch and
+ *                 head strides >= 0, a sequence stride >= D, and
+ *                 ((S + 255) * sequence stride + D) * element size < 2^31
+ *                 bytes; else ATTN_ERR_STRIDE.  Inputs may overlap (a zero
+ *                 head stride broadcasts one head); outputs must not overlap
+ *                 one another or the inputs (not checked).
  *
  * Errors, ownership and stream rules as the entry points above; a NULL
  * params pointer returns ATTN_ERR_NULL.
@@ -295,7 +310,13 @@ typedef struct attn_params {
   const float *rope_table;
   int rope_npos;
   void *q_rot, *k_rot;
+  int64_t strides[8][3];
 } attn_params;
+
+enum {
+  ATTN_STRIDE_Q = 0, ATTN_STRIDE_K, ATTN_STRIDE_V, ATTN_STRIDE_O, ATTN_STRIDE_DO, ATTN_STRIDE_DQ,
+  ATTN_STRIDE_DK, ATTN_STRIDE_DV
+};
 
 int attn_fwd_ex(const attn_params *p, void *stream);
 

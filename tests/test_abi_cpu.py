@@ -31,7 +31,7 @@ def test_header_status_codes_match_binding():
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 150
+    assert lib.attn_abi_version() == 160
 
 
 def test_status_strings(lib):
@@ -239,6 +239,31 @@ def _params(**kw):
 def test_ex_entry_points_reject_invalid_arguments(lib, kw, code):
     assert lib.attn_fwd_ex(_params(**kw), None) == code
     assert lib.attn_bwd_ex(_params(**kw), None) == code
+
+
+def _strided(slot, triple, **kw):
+    ref = _params(**kw)
+    ref._obj.strides[slot][:] = list(triple)
+    return ref
+
+
+@pytest.mark.parametrize("slot,triple", [
+    (0, (0, 0, 63)), (1, (-1, 64, 64)), (2, (4096, -64, 64)), (3, (0, 0, 32)), (7, (1, 1, 1)),
+    (0, (0, 0, 1 << 31)), (4, (0, 0, 1 << 26)),   # a panel past 2^31 bytes (S = 64 rows)
+])
+def test_ex_rejects_invalid_strides(lib, slot, triple):
+    # both calls check every row (one attn_params serves the pair)
+    assert lib.attn_fwd_ex(_strided(slot, triple), None) == -13
+    assert lib.attn_bwd_ex(_strided(slot, triple), None) == -13
+
+
+def test_ex_accepts_strided_layouts(lib):
+    """[B, S, H, D] views ({S*H*D, D, H*D}), head broadcast (head stride 0) and
+    padded rows pass validation (and fail later only for lack of a GPU)."""
+    for slot in range(8):
+        assert lib.attn_bwd_ex(_strided(slot, (64 * 4 * 64, 64, 4 * 64)), None) in (0, -7)
+    assert lib.attn_fwd_ex(_strided(1, (64 * 64, 0, 64)), None) in (0, -7)
+    assert lib.attn_fwd_ex(_strided(0, (4 * 64 * 128, 64 * 128, 128)), None) in (0, -7)
 
 
 def test_ex_entry_points_check_their_own_fields(lib):
