@@ -25,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -45,7 +46,7 @@ SEEDS = {"tiny_f32": 1, "lm12m_ctx512": 2, "lm237m_ctx1024": 3, "long_ctx8192": 
          "lm237m_ctx1024_gqa4": 6, "lm237m_ctx1024_rope": 7, "lm237m_ctx1024_out16": 8}
 # algorithmic flops per allowed pair, per kernel (times D)
 KERNEL_FLOPS_PER_PAIR = {"fwd": 4, "dkdv": 8, "dq": 2}
-KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip"]
+KERNEL_SOURCES = ["attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_bwd.hip"]
 
 
 def log(msg):
@@ -222,7 +223,7 @@ def kernel_key(name):
     """Short name of a kernel from its (mangled or demangled) name; the dQ kernel
     with Delta fused (last template flag set) is 'dq_delta'."""
     key = next((v for k, v in KERNEL_NAMES.items() if k in name), None)
-    if key == "dq" and ("Lb1EEEv" in name or name.rstrip(")").endswith("true>")):
+    if key == "dq" and ("Lb1EEEv" in name or re.search(r"attn_bwd_dq_kernel<[^(]*,\s*true>", name)):
         key = "dq_delta"
     return key
 
