@@ -86,6 +86,20 @@ def header_functions(path: str = HEADER_PATH):
     return re.findall(r"^\s*(?:const\s+)?(?:int|char|void|size_t)\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)
 
 
+def _init_device_runtime():
+    """Bring up the HIP runtime and torch's device context before the library's
+    code objects register with it: kernels of a library loaded into a process
+    whose runtime was not yet initialised failed to launch (ATTN_ERR_HIP, then
+    hipErrorOutOfMemory).  Without a GPU this does nothing (the library still
+    loads, e.g. to check its exports and argument validation)."""
+    try:
+        import torch
+    except ImportError:
+        return
+    if torch.cuda.is_available():
+        torch.cuda.init()
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load the HIP library (once).  Raises if it has not been built."""
     global _lib
@@ -95,6 +109,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(
             f"{path} not found: build the HIP library first "
             "(python -m causal_attention_amd.build or __graft_entry__.build())")
+    _init_device_runtime()
     lib = ctypes.CDLL(path)
     for name, args in SIGNATURES.items():
         fn = getattr(lib, name)
