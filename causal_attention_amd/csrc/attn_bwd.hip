@@ -419,7 +419,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
         float p = fast_exp2(__builtin_fmaf(sacc[r], c2, -l2));
         if constexpr (MASK) {
           const int kj = k0 + 32 * nb + 8 * (r / 4) + 4 * hh + (r % 4);
-          p = (kj > qi || kj >= t.seg_end) ? 0.f : p;
+          p = kj > qi ? 0.f : p;  // also keys past the segment end: stored rows have qi < seg_end
         }
         pacc[r] = p * (pacc[r] - dl);
       }

@@ -136,7 +136,9 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + 32 * nb + 8 * (r / 4) + 4 * hh + (r % 4);
-        sacc[nb][r] = (key > qi || key >= t.seg_end) ? -INFINITY : sacc[nb][r];
+        // key > qi also covers keys past the sequence or document end: every
+        // stored row has qi < r_end <= seg_end (those keys read as zeros)
+        sacc[nb][r] = key > qi ? -INFINITY : sacc[nb][r];
       }
   };
 
