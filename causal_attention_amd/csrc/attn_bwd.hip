@@ -216,13 +216,13 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
         E::mma(sacc, rf(sq, qb, kb), kfrag(kb));
         E::mma(pacc, rf(so, qb, kb), vfrag(kb));
       }
+      // query q0 + 32 qb + off < key, off = 8 (r / 4) + 4 hh + r % 4: one
+      // per-lane limit, compared with compile-time offsets
+      const int lim = key - q0 - qb * 32 - 4 * hh;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(sacc[r] * c2);
-        if constexpr (MASK) {
-          const int qi = q0 + qb * 32 + 8 * (r / 4) + 4 * hh + (r % 4);
-          p = qi < key ? 0.f : p;
-        }
+        if constexpr (MASK) p = (8 * (r / 4) + (r % 4)) < lim ? 0.f : p;
         sacc[r] = p;
         pacc[r] = p * pacc[r];
       }
@@ -405,6 +405,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
     const lds_t<T> *sv = vslot.template operator()<P>();
     const TrSwz<T, D> tr = tr0.pinned();
     const RowFrag<T, D> rf = rf0.pinned();
+    const int lim = qi - k0 - 4 * hh;  // the mask's per-lane limit
     ATTN_SCHED_HINT();
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -417,10 +418,9 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(__builtin_fmaf(sacc[r], c2, -l2));
-        if constexpr (MASK) {
-          const int kj = k0 + 32 * nb + 8 * (r / 4) + 4 * hh + (r % 4);
-          p = kj > qi ? 0.f : p;  // also keys past the segment end: stored rows have qi < seg_end
-        }
+        // key k0 + 32 nb + 8 (r / 4) + 4 hh + r % 4 > qi (also keys past the
+        // segment end: stored rows have qi < seg_end); lim is per lane
+        if constexpr (MASK) p = (32 * nb + 8 * (r / 4) + (r % 4)) > lim ? 0.f : p;
         pacc[r] = p * (pacc[r] - dl);
       }
       const frag s0 = E::pack(pacc, 0), s1 = E::pack(pacc, 1);

@@ -130,15 +130,16 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
   };
 
   auto apply_mask = [&](f32x16 (&sacc)[NB], int k0) {
-    const int qi = w0 + c;
+    // key k0 + off > query qi, off = 32 nb + 8 (r / 4) + 4 hh + r % 4: one
+    // per-lane limit, compared with compile-time offsets.  key > qi also
+    // covers keys past the sequence or document end: every stored row has
+    // qi < r_end <= seg_end (those keys read as zeros).
+    const int lim = (w0 + c) - k0 - 4 * hh;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 32 * nb + 8 * (r / 4) + 4 * hh + (r % 4);
-        // key > qi also covers keys past the sequence or document end: every
-        // stored row has qi < r_end <= seg_end (those keys read as zeros)
-        sacc[nb][r] = key > qi ? -INFINITY : sacc[nb][r];
+        sacc[nb][r] = (32 * nb + 8 * (r / 4) + (r % 4)) > lim ? -INFINITY : sacc[nb][r];
       }
   };
 
