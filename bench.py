@@ -408,7 +408,7 @@ def main():
         print(json.dumps(rec, indent=1))
         return
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported in this build "
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
               "(attention shards by batch and head with no communication; see the design notes)",
               file=sys.stderr)
         sys.exit(2)

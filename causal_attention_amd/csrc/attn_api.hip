@@ -111,35 +111,9 @@ attn::Args make_args(int B, int H, int S, int D, float scale, int mask_mode, con
 
 int to_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
-}  // namespace
-
-extern "C" {
-
-int attn_abi_version(void) { return kAbiVersion; }
-
-const char *attn_status_string(int status) {
-  switch (status) {
-    case ATTN_OK: return "ok";
-    case ATTN_ERR_NULL: return "a required pointer is NULL";
-    case ATTN_ERR_SHAPE: return "B, H or S out of range (each >= 1, B*H*S*D < 2^31)";
-    case ATTN_ERR_HEAD_DIM: return "head dimension D must be 32, 64 or 128";
-    case ATTN_ERR_DTYPE: return "unknown input dtype (ATTN_DTYPE_F32, ATTN_DTYPE_BF16 or ATTN_DTYPE_F16)";
-    case ATTN_ERR_MASK: return "unknown mask mode (ATTN_MASK_CAUSAL or ATTN_MASK_DOC_CAUSAL)";
-    case ATTN_ERR_SEQLENS: return "packed-document mode needs B == 1, 1 <= n_seqs <= S and 1 <= max_seqlen <= S";
-    case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
-    case ATTN_ERR_UNIMPLEMENTED: return "not implemented in this build";
-    case ATTN_ERR_SCALE: return "scale must be finite and > 0";
-    case ATTN_ERR_HEADS: return "H_kv must divide H (1 <= H_kv <= H)";
-    case ATTN_ERR_WORKSPACE: return "workspace NULL or smaller than attn_decode_workspace_bytes()";
-    case ATTN_ERR_ROPE: return "RoPE table NULL or shorter than the positions (S, or max_seqlen for documents), or base not finite and > 0";
-    case ATTN_ERR_STRIDE: return "strides: batch and head >= 0, sequence >= D, panel extent < 2^31 bytes";
-    default: return "unknown status";
-  }
-}
-
 // Whole forward (optionally rotating q and k first): argument checks, then
 // the kernels on one stream.
-static int fwd_all(const void *q, const void *k, const void *v, void *o, float *lse, bool with_rope,
+int fwd_all(const void *q, const void *k, const void *v, void *o, float *lse, bool with_rope,
                    const float *rope, int rope_npos, void *q_rot, void *k_rot, int B, int H, int H_kv, int S, int D,
                    float scale, int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype,
                    int out_dtype, const int64_t (*strides)[3], void *stream) {
@@ -174,6 +148,83 @@ static int fwd_all(const void *q, const void *k, const void *v, void *o, float *
   a.o = o;
   a.lse = lse;
   return to_status(attn::launch_fwd(a));
+}
+
+// Whole backward (optionally with RoPE gradients turned back in the dQ and dK
+// epilogues): argument checks, then the kernels on one stream.
+int bwd_all(const void *q, const void *k, const void *v, const void *o, const void *dO, const float *lse,
+                   void *dq, void *dk, void *dv, float *delta, bool with_rope, const float *rope, int rope_npos,
+                   int B, int H, int H_kv, int S, int D, float scale, int mask_mode, const int32_t *cu_seqlens,
+                   int n_seqs, int max_seqlen, int dtype, int out_dtype, const int64_t (*strides)[3],
+                   void *stream) {
+  int st = check_common(B, H, S, D, dtype);
+  if (st != ATTN_OK) return st;
+  if ((st = check_out(dtype, out_dtype)) != ATTN_OK) return st;
+  if ((st = check_heads(H, H_kv)) != ATTN_OK) return st;
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL;
+  if ((st = check_mask(B, H, S, mask_mode, cu_seqlens, n_seqs, max_seqlen)) != ATTN_OK) return st;
+  if ((st = check_scale(scale)) != ATTN_OK) return st;
+  if (with_rope && (st = check_rope(rope, rope_npos, S, mask_mode, max_seqlen)) != ATTN_OK) return st;
+  if ((st = check_strides(strides, S, D, elem_bytes(dtype), elem_bytes(out_dtype))) != ATTN_OK) return st;
+  attn::Args a = make_args(B, H, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
+  a.H_kv = H_kv;
+  a.out16 = out_dtype != ATTN_DTYPE_F32;
+  set_layouts(a, strides);
+  if (with_rope) {  // the kernels read the contiguous q_rot and k_rot
+    a.lq = attn::Layout{(int64_t)H * S * D, (int64_t)S * D, D};
+    a.lk = attn::Layout{(int64_t)H_kv * S * D, (int64_t)S * D, D};
+  }
+  a.rope = rope;
+  a.rope_npos = rope_npos;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dO = dO;
+  a.o_in = o;
+  a.lse_in = lse;
+  a.delta = delta;
+  a.delta_in = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  hipError_t e;
+  if (a.half()) {
+    // 16-bit inputs: dQ computes Delta on the way (bitwise equal to the
+    // preprocess kernel's) and writes it for dK/dV: one pass over O and dO fewer.
+    e = attn::launch_bwd_dq_delta(a);
+    if (e == hipSuccess) e = attn::launch_bwd_dkdv(a);
+  } else {
+    e = attn::launch_bwd_preprocess(a);
+    if (e == hipSuccess) e = attn::launch_bwd_dkdv(a);
+    if (e == hipSuccess) e = attn::launch_bwd_dq(a);
+  }
+  return to_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return kAbiVersion; }
+
+const char *attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "B, H or S out of range (each >= 1, B*H*S*D < 2^31)";
+    case ATTN_ERR_HEAD_DIM: return "head dimension D must be 32, 64 or 128";
+    case ATTN_ERR_DTYPE: return "unknown input dtype (ATTN_DTYPE_F32, ATTN_DTYPE_BF16 or ATTN_DTYPE_F16)";
+    case ATTN_ERR_MASK: return "unknown mask mode (ATTN_MASK_CAUSAL or ATTN_MASK_DOC_CAUSAL)";
+    case ATTN_ERR_SEQLENS: return "packed-document mode needs B == 1, 1 <= n_seqs <= S and 1 <= max_seqlen <= S";
+    case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case ATTN_ERR_UNIMPLEMENTED: return "valid request that this library does not implement";
+    case ATTN_ERR_SCALE: return "scale must be finite and > 0";
+    case ATTN_ERR_HEADS: return "H_kv must divide H (1 <= H_kv <= H)";
+    case ATTN_ERR_WORKSPACE: return "workspace NULL or smaller than attn_decode_workspace_bytes()";
+    case ATTN_ERR_ROPE: return "RoPE table NULL or shorter than the positions (S, or max_seqlen for documents), or base not finite and > 0";
+    case ATTN_ERR_STRIDE: return "strides: batch and head >= 0, sequence >= D, panel extent < 2^31 bytes";
+    default: return "unknown status";
+  }
 }
 
 int attn_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int H_kv, int S,
@@ -239,57 +290,6 @@ int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dO, con
   a.delta_in = delta;
   a.dq = dq;
   return to_status(attn::launch_bwd_dq(a));
-}
-
-// Whole backward (optionally with RoPE gradients turned back in the dQ and dK
-// epilogues): argument checks, then the kernels on one stream.
-static int bwd_all(const void *q, const void *k, const void *v, const void *o, const void *dO, const float *lse,
-                   void *dq, void *dk, void *dv, float *delta, bool with_rope, const float *rope, int rope_npos,
-                   int B, int H, int H_kv, int S, int D, float scale, int mask_mode, const int32_t *cu_seqlens,
-                   int n_seqs, int max_seqlen, int dtype, int out_dtype, const int64_t (*strides)[3],
-                   void *stream) {
-  int st = check_common(B, H, S, D, dtype);
-  if (st != ATTN_OK) return st;
-  if ((st = check_out(dtype, out_dtype)) != ATTN_OK) return st;
-  if ((st = check_heads(H, H_kv)) != ATTN_OK) return st;
-  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL;
-  if ((st = check_mask(B, H, S, mask_mode, cu_seqlens, n_seqs, max_seqlen)) != ATTN_OK) return st;
-  if ((st = check_scale(scale)) != ATTN_OK) return st;
-  if (with_rope && (st = check_rope(rope, rope_npos, S, mask_mode, max_seqlen)) != ATTN_OK) return st;
-  if ((st = check_strides(strides, S, D, elem_bytes(dtype), elem_bytes(out_dtype))) != ATTN_OK) return st;
-  attn::Args a = make_args(B, H, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
-  a.H_kv = H_kv;
-  a.out16 = out_dtype != ATTN_DTYPE_F32;
-  set_layouts(a, strides);
-  if (with_rope) {  // the kernels read the contiguous q_rot and k_rot
-    a.lq = attn::Layout{(int64_t)H * S * D, (int64_t)S * D, D};
-    a.lk = attn::Layout{(int64_t)H_kv * S * D, (int64_t)S * D, D};
-  }
-  a.rope = rope;
-  a.rope_npos = rope_npos;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.dO = dO;
-  a.o_in = o;
-  a.lse_in = lse;
-  a.delta = delta;
-  a.delta_in = delta;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  hipError_t e;
-  if (a.half()) {
-    // 16-bit inputs: dQ computes Delta on the way (bitwise equal to the
-    // preprocess kernel's) and writes it for dK/dV: one pass over O and dO fewer.
-    e = attn::launch_bwd_dq_delta(a);
-    if (e == hipSuccess) e = attn::launch_bwd_dkdv(a);
-  } else {
-    e = attn::launch_bwd_preprocess(a);
-    if (e == hipSuccess) e = attn::launch_bwd_dkdv(a);
-    if (e == hipSuccess) e = attn::launch_bwd_dq(a);
-  }
-  return to_status(e);
 }
 
 int attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o, const void *dO, const float *lse,
