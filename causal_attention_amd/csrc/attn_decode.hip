@@ -3,7 +3,7 @@
 // Each (batch entry b, query head h) has one new query, the newest token,
 // whose own key is already in the cache; it attends keys 0 .. len_b - 1 of its
 // K/V head (causality admits every cached key).  This is the generation step
-// Forge's roadmap lists ("KV cache for generation").  The work is reading the
+// that Forge plans next (Forge, "Roadmap").  The work is reading the
 // cache: 2 * len * D elements per K/V head against ~4 * len * D * G flops for
 // the G query heads of that K/V head, so the kernel is bound by HBM bandwidth.
 //

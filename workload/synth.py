@@ -192,7 +192,7 @@ class DecodeConfig:
 
 
 # Generation with the long-context model shape (16 heads of 128) over a full
-# 8192-token cache (Forge, "Roadmap": KV cache for generation; Cort33x: 2K-8K
+# 8192-token cache (Forge, "Roadmap": generation with a key/value cache; Cort33x: 2K-8K
 # training contexts), eight sequences at once.
 DECODE_CONFIGS = {
     "decode_ctx8192": DecodeConfig("decode_ctx8192", B=8, H=16, H_kv=16, S_max=8192, D=128, dtype="bf16",
