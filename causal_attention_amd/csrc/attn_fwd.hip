@@ -49,7 +49,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
   using E = Elem<T>;
   using frag = typename E::frag;
   using KTile = DmaTile<T, BN, D, NT, true>;   // read as row fragments: swizzled
-  using VTile = DmaTile<T, BN, D, NT, false>;  // read through the transposing load
+  using VTile = DmaTile<T, BN, D, NT, true>;   // read through the transposing load: swizzled too
 
   // Two ring slots for K and for V, each its own LDS object: the slot an
   // access touches is known at compile time (the loop is unrolled by two),
@@ -105,6 +105,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
 
   const RowFrag<T, D> rf0(lane);  // row fragments of the K tiles
+  const TrSwz<T, D> trv0(lane);   // transposed reads of the V tiles
 
   // S^T = K Q^T for the key tile in `ks`.
   auto scores = [&](const lds_t<T> *ks, f32x16 (&sacc)[NB]) {
@@ -120,13 +121,14 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
       }
   };
 
-  // O^T += V^T P^T for the value tile in `vs`.
+  // O^T += V^T P^T for the value tile in `vs` (transposed reads of the
+  // swizzled tile: free of LDS bank conflicts, like the backward's).
   auto pv = [&](const lds_t<T> *vs, const frag (&pf)[PB]) {
-    const TrRead<T, D> vr(vs, lane);
+    const TrSwz<T, D> tr = trv0.pinned();
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int j = 0; j < PB; ++j) E::mma(oacc[db], vr(16 * j, 32 * db), pf[j]);
+      for (int j = 0; j < PB; ++j) E::mma(oacc[db], tr(vs, 16 * j, db), pf[j]);
   };
 
   auto apply_mask = [&](f32x16 (&sacc)[NB], int k0) {
