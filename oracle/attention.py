@@ -235,7 +235,14 @@ def attention_dkdv_rows_ref(q, k, v, do, scale, b, h, cols, mask_mode=MASK_CAUSA
     cols = list(cols)
     dk = np.zeros((len(cols), qh.shape[1]))
     dv = np.zeros((len(cols), qh.shape[1]))
-    for i in range(S):
+    if not cols:
+        return dk, dv
+    # Only queries at or after the first requested key, in one of its
+    # documents, give these keys a nonzero weight; every other row adds zero.
+    rows = np.arange(min(cols), S)
+    if doc is not None:
+        rows = rows[np.isin(doc[rows], doc[cols])]
+    for i in rows:
         allowed = jj <= i
         if doc is not None:
             allowed = allowed & (doc == doc[i])
