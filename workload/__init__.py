@@ -14,6 +14,7 @@ from .synth import (  # noqa: F401
     round_to_f16,
     make_cu_seqlens,
     make_inputs,
+    make_inputs_device,
     make_decode_inputs,
     allowed_pair_count,
 )

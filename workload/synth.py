@@ -22,6 +22,14 @@ Recipe (stated once so that every consumer draws the same numbers):
   ``default_rng(doc_seed)``: integers uniform in [lo, hi] (both inclusive) are
   drawn until their sum reaches the total; the last length is cut so the sum
   is exactly the total.
+
+Inputs of billions of elements (the largest shapes the kernels accept) are too
+big to draw on the host; ``make_inputs_device`` draws them on the GPU instead:
+a ``torch.Generator`` on that device seeded with ``seed``, float32
+``torch.randn`` tensors in the order Q, K, V, dO, Q/K/V multiplied by
+``qkv_scale``, then converted (round-to-nearest-even) to the input dtype.  The
+oracle is given slices of those tensors copied to the host, which are exactly
+the values the kernels read.
 """
 from __future__ import annotations
 
@@ -174,6 +182,27 @@ def make_inputs(cfg: AttnConfig, seed: int, shape=None):
         cu = make_cu_seqlens(S, lo, hi, cfg.doc_seed)
     out.update(cu_seqlens=cu, B=B, H=H, S=S, D=D, scale=1.0 / math.sqrt(D),
                mask_mode=cfg.mask_mode, dtype=cfg.dtype)
+    return out
+
+
+def make_inputs_device(cfg: AttnConfig, seed: int, shape, device="cuda", H_kv=None):
+    """Q, K, V, dO of ``shape`` = (B, H, S, D) drawn on ``device`` (torch tensors
+    in the input dtype, K and V with ``H_kv`` heads if given), by the device
+    recipe in the module docstring."""
+    import torch
+    B, H, S, D = shape
+    H_kv = H if H_kv is None else H_kv
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[cfg.dtype]
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = {}
+    for name in ("q", "k", "v", "do"):
+        x = torch.randn((B, H_kv if name in ("k", "v") else H, S, D), generator=g, device=device,
+                        dtype=torch.float32)
+        if name != "do":
+            x.mul_(cfg.qkv_scale)
+        out[name] = x.to(dt)
+        del x
     return out
 
 
