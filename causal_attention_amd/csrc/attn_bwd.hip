@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   // dK^T += Q^T dS.
   const typename E::rows_frag ones = E::rows_b(hh);
   const float rscale = 1.0f / scale;
-  auto tile = [&]<int P, bool MASK>(int q0) {
+  auto tile = [&]<int P>(int q0, bool masked) {
     const lds_t<T> *sq = qslot.template operator()<P>();
     const lds_t<T> *so = oslot.template operator()<P>();
     const lds_t<float> *sl = lslot.template operator()<P>();
@@ -218,14 +218,15 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
       }
       // query q0 + 32 qb + off < key, off = 8 (r / 4) + 4 hh + r % 4: one
       // per-lane limit, compared with compile-time offsets
-      const int lim = key - q0 - qb * 32 - 4 * hh;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(sacc[r] * c2);
-        if constexpr (MASK) p = (8 * (r / 4) + (r % 4)) < lim ? 0.f : p;
-        sacc[r] = p;
-        pacc[r] = p * pacc[r];
+      for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(sacc[r] * c2);
+      if (masked) {
+        const int lim = key - q0 - qb * 32 - 4 * hh;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = (8 * (r / 4) + (r % 4)) < lim ? 0.f : sacc[r];
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pacc[r] = sacc[r] * pacc[r];
       const frag p0 = E::pack(sacc, 0), p1 = E::pack(sacc, 1);
       const frag s0 = E::pack(pacc, 0), s1 = E::pack(pacc, 1);
 #pragma unroll
@@ -246,10 +247,10 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     if (it + 1 < ntile) issue.template operator()<1 - P>(it + 1);
     const int q0 = q_lo + (it % ntq) * BMQ;
     if (!wave_active || q0 + BMQ - 1 < w0) return;  // every query precedes every key here
-    if (q0 < wave_last)
-      tile.template operator()<P, true>(q0);
-    else
-      tile.template operator()<P, false>(q0);
+    // One tile body with a uniform branch around the masking: two
+    // instantiations would give the accumulators different registers in
+    // each and cost copies where they join.
+    tile.template operator()<P>(q0, q0 < wave_last);
   };
   for (int it = 0; it < ntile; it += 2) {
     step.template operator()<0>(it);
@@ -400,7 +401,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
 
   // One key tile: per 32-key block, S^T = K Q^T and dP^T = V dO^T (lane c owns
   // query w0 + c), P, dS = P (dP - Delta), then dQ^T += K^T dS^T.
-  auto tile = [&]<int P, bool MASK>(int k0) {
+  auto tile = [&]<int P>(int k0, bool masked) {
     const lds_t<T> *sk = kslot.template operator()<P>();
     const lds_t<T> *sv = vslot.template operator()<P>();
     const TrSwz<T, D> tr = tr0.pinned();
@@ -416,13 +417,15 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
         E::mma(pacc, rf(sv, nb, kb), df[kb]);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(__builtin_fmaf(sacc[r], c2, -l2));
+      for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(__builtin_fmaf(sacc[r], c2, -l2));
+      if (masked) {
         // key k0 + 32 nb + 8 (r / 4) + 4 hh + r % 4 > qi (also keys past the
         // segment end: stored rows have qi < seg_end); lim is per lane
-        if constexpr (MASK) p = (32 * nb + 8 * (r / 4) + (r % 4)) > lim ? 0.f : p;
-        pacc[r] = p * (pacc[r] - dl);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = (32 * nb + 8 * (r / 4) + (r % 4)) > lim ? 0.f : sacc[r];
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pacc[r] = sacc[r] * (pacc[r] - dl);
       const frag s0 = E::pack(pacc, 0), s1 = E::pack(pacc, 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -438,10 +441,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
     if (j + 1 < ntile) issue.template operator()<1 - P>(j + 1);
     if (j >= jw) return;
     const int k0 = kv_lo + j * BN;
-    if ((k0 + BN - 1 > w0) || (k0 + BN > t.seg_end))
-      tile.template operator()<P, true>(k0);
-    else
-      tile.template operator()<P, false>(k0);
+    tile.template operator()<P>(k0, (k0 + BN - 1 > w0) || (k0 + BN > t.seg_end));
   };
   for (int j = 0; j < ntile; j += 2) {
     step.template operator()<0>(j);

@@ -502,8 +502,9 @@ template <typename T, int D> struct TrSwz;
 template <typename T, int D> struct TrSwz16 {
   using frag = typename Elem<T>::frag;
   static constexpr int DB = D / 32;
-  // [read][db]: the first read covers rows 0-7 of the 16, the second rows 8-15.
-  int off[2][DB];
+  // [read][db]: the first read covers rows 0-7 of the 16, the second rows
+  // 8-15.  Byte offsets, so an address is one add (often folded away).
+  uint32_t off[2][DB];
   __device__ __forceinline__ explicit TrSwz16(int lane) {
     const int g = lane / 16, i = lane % 16;
     const int rl = 4 * (g / 2) + i / 4;             // row within an 8-row group
@@ -514,7 +515,7 @@ template <typename T, int D> struct TrSwz16 {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int r = rl + 8 * k;
-        off[k][db] = r * D + 8 * (int)((uint32_t)(4 * db + x) ^ swz_mask<T, D>(r)) + e;
+        off[k][db] = (uint32_t)(r * D + 8 * (int)((uint32_t)(4 * db + x) ^ swz_mask<T, D>(r)) + e) * sizeof(T);
       }
   }
   // A copy whose offsets the compiler cannot trace back to the loop-invariant
@@ -531,8 +532,9 @@ template <typename T, int D> struct TrSwz16 {
   }
   __device__ __forceinline__ frag operator()(const lds_t<T> *tile, int row0, int db) const {
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tile + row0 * D + off[0][db]));
-    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tile + row0 * D + off[1][db]));
+    const lds_t<char> *p = (const lds_t<char> *)(tile + row0 * D);
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + off[0][db]));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + off[1][db]));
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     s16x8 v;
 #pragma unroll
@@ -559,11 +561,11 @@ template <int D> struct TrSwz<float, D> {
   using frag = f32x8;
   // 4-float chunks, mask row & 7; rows 4h + u (u < 4) of an 8-row group,
   // column c: chunk (8*db + c/4) ^ (4h + u) = 8*db + ((c/4) ^ (4h + u)).
-  int off[4];
+  uint32_t off[4];  // byte offsets
   __device__ __forceinline__ explicit TrSwz(int lane) {
     const int h = lane / 32, c = lane % 32;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) off[u] = (4 * h + u) * D + 4 * ((c / 4) ^ (4 * h + u)) + c % 4;
+    for (int u = 0; u < 4; ++u) off[u] = (uint32_t)((4 * h + u) * D + 4 * ((c / 4) ^ (4 * h + u)) + c % 4) * 4u;
   }
   __device__ __forceinline__ TrSwz pinned() const {
     TrSwz t = *this;
@@ -574,7 +576,8 @@ template <int D> struct TrSwz<float, D> {
   __device__ __forceinline__ frag operator()(const lds_t<float> *tile, int row0, int db) const {
     frag f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) f[s] = tile[row0 * D + 32 * db + 8 * D * (s / 4) + off[s % 4]];
+    for (int s = 0; s < 8; ++s)
+      f[s] = *(const lds_t<float> *)((const lds_t<char> *)(tile + row0 * D + 32 * db + 8 * D * (s / 4)) + off[s % 4]);
     return f;
   }
 };
@@ -588,7 +591,7 @@ template <typename T, int D> struct RowFrag {
   static constexpr int KB = D / 16;
   static constexpr int kVec = 16 / sizeof(T);  // elements per 16-byte chunk
   static constexpr int kReads = sizeof(T) == 2 ? 1 : 2;
-  int off[KB][kReads];
+  uint32_t off[KB][kReads];  // byte offsets
   __device__ __forceinline__ explicit RowFrag(int lane) {
     const int c = lane % 32, hh = lane / 32;
     const uint32_t m = swz_mask<T, D>((uint32_t)c);
@@ -597,7 +600,7 @@ template <typename T, int D> struct RowFrag {
 #pragma unroll
       for (int i = 0; i < kReads; ++i) {
         const uint32_t chunk = (uint32_t)((16 * kb + 8 * hh) / kVec + i);
-        off[kb][i] = c * D + (int)((chunk ^ m) * kVec);
+        off[kb][i] = (uint32_t)(c * D + (int)((chunk ^ m) * kVec)) * sizeof(T);
       }
   }
   // See TrSwz::pinned.
@@ -610,7 +613,7 @@ template <typename T, int D> struct RowFrag {
     return t;
   }
   __device__ __forceinline__ frag operator()(const lds_t<T> *tile, int blk, int kb) const {
-    const lds_t<T> *p = tile + blk * 32 * D;
+    const lds_t<char> *p = (const lds_t<char> *)(tile + blk * 32 * D);
     if constexpr (sizeof(T) == 2) {
       return *(const lds_t<frag> *)(p + off[kb][0]);
     } else {
