@@ -209,6 +209,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       f32x16 sacc = f32x16{}, pacc = f32x16{};
+      mma_priority_hi();
       E::mma_rows(sacc, E::rows_a(-sl[qb * 32 + c] * rscale, hh), ones);
       E::mma_rows(pacc, E::rows_a(-sd[qb * 32 + c], hh), ones);
 #pragma unroll
@@ -216,6 +217,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
         E::mma(sacc, rf(sq, qb, kb), kfrag(kb));
         E::mma(pacc, rf(so, qb, kb), vfrag(kb));
       }
+      mma_priority_lo();
       // query q0 + 32 qb + off < key, off = 8 (r / 4) + 4 hh + r % 4: one
       // per-lane limit, compared with compile-time offsets
 #pragma unroll
@@ -229,6 +231,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
       for (int r = 0; r < 16; ++r) pacc[r] = sacc[r] * pacc[r];
       const frag p0 = E::pack(sacc, 0), p1 = E::pack(sacc, 1);
       const frag s0 = E::pack(pacc, 0), s1 = E::pack(pacc, 1);
+      mma_priority_hi();
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         E::mma(dvacc[db], tr(so, 32 * qb, db), p0);
@@ -236,6 +239,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
         E::mma(dkacc[db], tr(sq, 32 * qb, db), s0);
         E::mma(dkacc[db], tr(sq, 32 * qb + 16, db), s1);
       }
+      mma_priority_lo();
     }
   };
 
@@ -411,11 +415,13 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       f32x16 sacc = f32x16{}, pacc = f32x16{};
+      mma_priority_hi();
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         E::mma(sacc, rf(sk, nb, kb), qf[kb]);
         E::mma(pacc, rf(sv, nb, kb), df[kb]);
       }
+      mma_priority_lo();
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(__builtin_fmaf(sacc[r], c2, -l2));
       if (masked) {
@@ -427,11 +433,13 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) pacc[r] = sacc[r] * (pacc[r] - dl);
       const frag s0 = E::pack(pacc, 0), s1 = E::pack(pacc, 1);
+      mma_priority_hi();
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         E::mma(dqacc[db], tr(sk, 32 * nb, db), s0);
         E::mma(dqacc[db], tr(sk, 32 * nb + 16, db), s1);
       }
+      mma_priority_lo();
     }
   };
 

@@ -61,6 +61,13 @@ constexpr int kWaveSize = 64;
 // keeps track of which LDS object an access touches, and waits for an
 // in-flight direct-to-LDS copy only when a read can overlap its destination.
 template <typename T> using lds_t = __attribute__((address_space(3))) T;
+// Wave priority around a group of matrix-core instructions: while a wave
+// issues its products it goes ahead of the other waves of its SIMD, which
+// meanwhile run their vector work (measured: 3 % faster at S = 8192, equal
+// at 1024).
+__device__ __forceinline__ void mma_priority_hi() { __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void mma_priority_lo() { __builtin_amdgcn_s_setprio(0); }
+
 template <typename T> __device__ __forceinline__ lds_t<T> *lds_cast(T *p) { return (lds_t<T> *)p; }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

@@ -197,7 +197,9 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
     f32x16 sacc[NB];
     frag pf[PB];
     float psum;
+    mma_priority_hi();
     scores(ks, sacc);
+    mma_priority_lo();
     if (masked) apply_mask(sacc, k0);
     if (m == -INFINITY) {
       softmax_exact(sacc, pf, psum);
@@ -209,7 +211,9 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
       softmax_exact(sacc, pf, psum);
     }
     l += psum;
+    mma_priority_hi();
     pv(vslot.template operator()<P>(), pf);
+    mma_priority_lo();
   };
 
   for (int j = 0; j < ntile; j += 2) {
