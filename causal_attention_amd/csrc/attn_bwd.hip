@@ -86,7 +86,14 @@ __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const OT *__re
 // global->LDS copies into two ring slots (separate LDS objects, loop unrolled
 // by two) one iteration ahead; Q and dO are read both as row fragments and,
 // through the transposing load, as Q^T and dO^T.
-template <typename T, typename OT, int D, int BMQ, int MINB, bool DOC>
+//
+// SPLIT = 2 (grouped heads, G even): the workgroup owns 64 keys, and each key
+// group of 32 has two waves, each running the query-tile loop over half of
+// the G query heads with a ring of its own; at the end the second wave hands
+// its partial dK, dV to the first through LDS, which adds them (first half +
+// second half, a fixed order) and stores.  Twice the workgroups of SPLIT = 1
+// for the same keys, so grouped heads fill twice the wave slots.
+template <typename T, typename OT, int D, int BMQ, int MINB, bool DOC, int SPLIT>
 __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, OT *__restrict__ dk,
@@ -95,22 +102,26 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     Layout ldk, Layout ldv) {
   constexpr int NW = 4;
   constexpr int NT = NW * kWaveSize;
-  constexpr int BN = NW * 32;  // keys per workgroup
+  constexpr int NWH = NW / SPLIT;  // waves per half: one per 32-key group
+  constexpr int BN = NWH * 32;     // keys per workgroup
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
   constexpr int QB = BMQ / 32;  // 32-query blocks per tile
   using E = Elem<T>;
   using frag = typename E::frag;
-  using QTile = DmaTile<T, BMQ, D, NT, true>;
+  using QTile = DmaTile<T, BMQ, D, NT / SPLIT, true>;  // copied by the half's waves
+  static_assert(SPLIT == 1 || SPLIT == 2, "one or two halves");
+  static_assert(SPLIT == 1 || DB * 16 * kWaveSize * 4 <= SPLIT * BMQ * D * (int)sizeof(T),
+                "a wave's partial dK (or dV) fits one ring slot");
 
-  __shared__ __attribute__((aligned(1024))) T sQ0[BMQ * D];
-  __shared__ __attribute__((aligned(1024))) T sQ1[BMQ * D];
-  __shared__ __attribute__((aligned(1024))) T sO0[BMQ * D];  // dO
-  __shared__ __attribute__((aligned(1024))) T sO1[BMQ * D];
-  __shared__ __attribute__((aligned(256))) float sL0[64];    // LSE (natural log)
-  __shared__ __attribute__((aligned(256))) float sL1[64];
-  __shared__ __attribute__((aligned(256))) float sD0[64];    // Delta
-  __shared__ __attribute__((aligned(256))) float sD1[64];
+  __shared__ __attribute__((aligned(1024))) T sQ0[SPLIT * BMQ * D];  // [half][row][col]
+  __shared__ __attribute__((aligned(1024))) T sQ1[SPLIT * BMQ * D];
+  __shared__ __attribute__((aligned(1024))) T sO0[SPLIT * BMQ * D];  // dO
+  __shared__ __attribute__((aligned(1024))) T sO1[SPLIT * BMQ * D];
+  __shared__ __attribute__((aligned(256))) float sL0[SPLIT * 64];    // LSE (natural log)
+  __shared__ __attribute__((aligned(256))) float sL1[SPLIT * 64];
+  __shared__ __attribute__((aligned(256))) float sD0[SPLIT * 64];    // Delta
+  __shared__ __attribute__((aligned(256))) float sD1[SPLIT * 64];
 
   const RowTile t = DOC ? doc_tile(cu, blockIdx.x, gridDim.x, ntiles, n_seqs, BN, false)
                         : causal_tile(blockIdx.x, gridDim.x, ntiles, BN, S, false);
@@ -118,11 +129,14 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
 
   const int tid = threadIdx.x;
   const int wave = wave_id();
+  const int half = wave % SPLIT;  // which half of the query heads
+  const int kg = wave / SPLIT;    // which 32 keys; also the wave's index in its half
   const int lane = tid % kWaveSize;
   const int hh = lane / 32;
   const int c = lane % 32;
   // t.head is a key/value head; its G query heads are qh0 .. qh0 + G - 1, and
-  // dK, dV sum over all of them (the query-tile loop runs over the group).
+  // dK, dV sum over all of them (the query-tile loop runs over the group, or
+  // over half of it in each half).
   const int Hkv = H / G;
   const int bi = t.head / Hkv;   // batch entry
   const int hk = t.head % Hkv;   // key/value head; its query heads are hk*G .. hk*G + G - 1
@@ -130,24 +144,25 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   const GBuf gk(k + panel_off(lk, bi, hk), panel_bytes(lk, t.r_end, D, sizeof(T)));
   const GBuf gv(v + panel_off(lv, bi, hk), panel_bytes(lv, t.r_end, D, sizeof(T)));
 
-  const int w0 = t.r_start + wave * 32;  // first key of this wave
+  const int w0 = t.r_start + kg * 32;  // first key of this wave
   const bool wave_active = w0 < t.r_end;
   const int wave_last = min(w0 + 32, t.r_end) - 1;
   const int key = w0 + c;
   const int q_lo = t.r_start;  // the first query that sees any of these keys
   const int ntq = (t.seg_end - q_lo + BMQ - 1) / BMQ;  // query tiles per query head
-  const int ntile = G * ntq;                            // over the whole group
+  const int GH = G / SPLIT;                             // query heads per half
+  const int ntile = GH * ntq;                           // over the half's heads
 
-  auto qslot = [&]<int P>() { return lds_cast(P == 0 ? sQ0 : sQ1); };
-  auto oslot = [&]<int P>() { return lds_cast(P == 0 ? sO0 : sO1); };
-  auto lslot = [&]<int P>() { return lds_cast(P == 0 ? sL0 : sL1); };
-  auto dslot = [&]<int P>() { return lds_cast(P == 0 ? sD0 : sD1); };
+  auto qslot = [&]<int P>() { return lds_cast(P == 0 ? sQ0 : sQ1) + half * BMQ * D; };
+  auto oslot = [&]<int P>() { return lds_cast(P == 0 ? sO0 : sO1) + half * BMQ * D; };
+  auto lslot = [&]<int P>() { return lds_cast(P == 0 ? sL0 : sL1) + half * 64; };
+  auto dslot = [&]<int P>() { return lds_cast(P == 0 ? sD0 : sD1) + half * 64; };
   uint32_t qoff[QTile::kPerWave], dooff[QTile::kPerWave];
-  QTile::lane_offsets(qoff, wave, lane, lq.ss);
-  QTile::lane_offsets(dooff, wave, lane, ldo.ss);
+  QTile::lane_offsets(qoff, kg, lane, lq.ss);
+  QTile::lane_offsets(dooff, kg, lane, ldo.ss);
   auto issue = [&]<int P>(int it) {
-    const int g = it / ntq;
-    const int q0 = q_lo + (it - g * ntq) * BMQ;
+    const int g = half * GH + it / ntq;
+    const int q0 = q_lo + (it % ntq) * BMQ;
     const size_t rbase = (size_t)(qh0 + g) * S;
     // Queries past the segment read as zeros (Q, dO, LSE, Delta all 0): their
     // P is 1 but dO and Q are 0, so they add nothing to dV or dK.
@@ -155,10 +170,10 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     const GBuf gdo(dO + panel_off(ldo, bi, hk * G + g), panel_bytes(ldo, t.seg_end, D, sizeof(T)));
     const GBuf glse(lse + rbase, (uint32_t)(t.seg_end * sizeof(float)));
     const GBuf gdel(delta + rbase, (uint32_t)(t.seg_end * sizeof(float)));
-    QTile::issue_at(gq, qslot.template operator()<P>(), QTile::row0_bytes(q0, lq.ss), qoff, wave);
-    QTile::issue_at(gdo, oslot.template operator()<P>(), QTile::row0_bytes(q0, ldo.ss), dooff, wave);
-    if (wave == 0) dma_vec64(glse, lslot.template operator()<P>(), q0, lane);
-    if (wave == 1) dma_vec64(gdel, dslot.template operator()<P>(), q0, lane);
+    QTile::issue_at(gq, qslot.template operator()<P>(), QTile::row0_bytes(q0, lq.ss), qoff, kg);
+    QTile::issue_at(gdo, oslot.template operator()<P>(), QTile::row0_bytes(q0, ldo.ss), dooff, kg);
+    if (kg == 0) dma_vec64(glse, lslot.template operator()<P>(), q0, lane);
+    if (kg == 1) dma_vec64(gdel, dslot.template operator()<P>(), q0, lane);
   };
   issue.template operator()<0>(0);
 
@@ -208,6 +223,8 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     ATTN_SCHED_HINT();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      // a block whose queries all precede this wave's first key adds nothing
+      if (masked && q0 + qb * 32 + 31 < w0) continue;
       f32x16 sacc = f32x16{}, pacc = f32x16{};
       mma_priority_hi();
       E::mma_rows(sacc, E::rows_a(-sl[qb * 32 + c] * rscale, hh), ones);
@@ -259,6 +276,46 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   for (int it = 0; it < ntile; it += 2) {
     step.template operator()<0>(it);
     if (it + 1 < ntile) step.template operator()<1>(it + 1);
+  }
+
+  if constexpr (SPLIT == 2) {
+    // The second half's partial sums go through the ring slots (free once
+    // every wave has passed this barrier), lane-major so each lane reads
+    // back its own elements; the first half adds them and stores.
+    wg_barrier();
+    lds_t<f32x4> *pk = (lds_t<f32x4> *)lds_cast(kg == 0 ? sQ0 : sO0);
+    lds_t<f32x4> *pv = (lds_t<f32x4> *)lds_cast(kg == 0 ? sQ1 : sO1);
+    if (half == 1 && wave_active) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 a4, b4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            a4[i] = dkacc[db][4 * g + i];
+            b4[i] = dvacc[db][4 * g + i];
+          }
+          pk[(db * 4 + g) * kWaveSize + lane] = a4;
+          pv[(db * 4 + g) * kWaveSize + lane] = b4;
+        }
+    }
+    wg_barrier();
+    if (half == 1) return;
+    if (wave_active) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 a4 = pk[(db * 4 + g) * kWaveSize + lane];
+          const f32x4 b4 = pv[(db * 4 + g) * kWaveSize + lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dkacc[db][4 * g + i] += a4[i];
+            dvacc[db][4 * g + i] += b4[i];
+          }
+        }
+    }
   }
 
   if (!wave_active) return;
@@ -519,11 +576,11 @@ static hipError_t launch_pre_t(const Args &a) {
   return hipGetLastError();
 }
 
-template <typename T, typename OT, int D, bool DOC>
-static hipError_t launch_dkdv_t(const Args &a) {
+template <typename T, typename OT, int D, bool DOC, int SPLIT>
+static hipError_t launch_dkdv_split(const Args &a) {
   constexpr int BMQ = BwdCfg<T, D>::BMQ;
   constexpr int MINB = BwdCfg<T, D>::MINB_DKDV;
-  constexpr int BN = 4 * 32;
+  constexpr int BN = 4 * 32 / SPLIT;  // keys per workgroup
   const float c2 = a.scale * kLog2e;
   dim3 grid;
   int ntiles;
@@ -534,12 +591,22 @@ static hipError_t launch_dkdv_t(const Args &a) {
     ntiles = (a.S + BN - 1) / BN;
     grid = dim3(ntiles * a.B * a.H_kv);
   }
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, OT, D, BMQ, MINB, DOC>), grid, dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, OT, D, BMQ, MINB, DOC, SPLIT>), grid, dim3(256), 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
                      static_cast<const T *>(a.dO), a.lse_in, a.delta_in, static_cast<OT *>(a.dk),
                      static_cast<OT *>(a.dv), a.S, c2, a.scale, a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv,
                      a.rope, a.rope_npos, a.lq, a.lk, a.lv, a.ldo, a.ldk, a.ldv);
   return hipGetLastError();
+}
+
+// Grouped heads with an even group size, 16-bit inputs: two halves per key
+// group (twice the workgroups); otherwise one.
+template <typename T, typename OT, int D, bool DOC>
+static hipError_t launch_dkdv_t(const Args &a) {
+  if constexpr (sizeof(T) == 2) {
+    if ((a.H / a.H_kv) % 2 == 0) return launch_dkdv_split<T, OT, D, DOC, 2>(a);
+  }
+  return launch_dkdv_split<T, OT, D, DOC, 1>(a);
 }
 
 template <typename T, typename OT, int D, bool DOC, bool FUSE_DELTA>
