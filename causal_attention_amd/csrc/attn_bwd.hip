@@ -343,6 +343,233 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// dK/dV by wave pairs (16-bit inputs).  A workgroup owns 64 keys; each 32-key
+// group has a V-wave and a K-wave.  Per 32-query tile the V-wave computes
+// S' = Q K^T - LSE/scale and P = exp2(c2 S') (masked), hands P (fp32) to its
+// partner through LDS and adds P^T dO to dV; one tile later the K-wave
+// computes dP' = dO V^T - Delta, dS = P dP' with the P it was handed, and
+// adds dS^T Q to dK.  These are the one-wave kernel's products and
+// per-element arithmetic, in the same order, split into two halves of 17
+// matrix-core steps per tile; each wave keeps one accumulator and one of K,
+// V in registers, so twice as many waves fit.  Query tiles pass through a
+// three-slot ring: at step j the copy into slot (j+1) % 3 starts while the
+// V-wave reads slot j % 3 and the K-wave slot (j-1) % 3.
+template <typename T, typename OT, int D, int MINB, bool DOC>
+__global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_pair_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dO,
+    const float *__restrict__ lse, const float *__restrict__ delta, OT *__restrict__ dk,
+    OT *__restrict__ dv, int S, float c2, float scale, const int32_t *__restrict__ cu, int ntiles, int n_seqs,
+    int H, int G, const float *__restrict__ rope, int rope_npos, Layout lq, Layout lk, Layout lv, Layout ldo,
+    Layout ldk, Layout ldv) {
+  static_assert(sizeof(T) == 2, "wave pairs: 16-bit inputs");
+  constexpr int NW = 4;
+  constexpr int NT = NW * kWaveSize;
+  constexpr int BN = NW / 2 * 32;  // keys per workgroup
+  constexpr int BMQ = 32;          // queries per tile
+  constexpr int KB = D / 16;
+  constexpr int DB = D / 32;
+  using E = Elem<T>;
+  using frag = typename E::frag;
+  using QTile = DmaTile<T, BMQ, D, NT, true>;
+
+  __shared__ __attribute__((aligned(1024))) T sQ0[BMQ * D];
+  __shared__ __attribute__((aligned(1024))) T sQ1[BMQ * D];
+  __shared__ __attribute__((aligned(1024))) T sQ2[BMQ * D];
+  __shared__ __attribute__((aligned(1024))) T sO0[BMQ * D];  // dO
+  __shared__ __attribute__((aligned(1024))) T sO1[BMQ * D];
+  __shared__ __attribute__((aligned(1024))) T sO2[BMQ * D];
+  __shared__ __attribute__((aligned(256))) float sL0[64];  // LSE (natural log; 32 used)
+  __shared__ __attribute__((aligned(256))) float sL1[64];
+  __shared__ __attribute__((aligned(256))) float sL2[64];
+  __shared__ __attribute__((aligned(256))) float sD0[64];  // Delta
+  __shared__ __attribute__((aligned(256))) float sD1[64];
+  __shared__ __attribute__((aligned(256))) float sD2[64];
+  // P handed from V-wave to K-wave: [key group][buffer][4-slot group][lane]
+  __shared__ __attribute__((aligned(256))) f32x4 sP[NW / 2 * 2 * 4 * kWaveSize];
+
+  const RowTile t = DOC ? doc_tile(cu, blockIdx.x, gridDim.x, ntiles, n_seqs, BN, false)
+                        : causal_tile(blockIdx.x, gridDim.x, ntiles, BN, S, false);
+  if (!t.valid) return;
+
+  const int tid = threadIdx.x;
+  const int wave = wave_id();
+  const int kg = wave / 2;             // which 32 keys
+  const bool vwave = wave % 2 == 0;    // V-wave (S, P, dV) or K-wave (dP, dS, dK)
+  const int lane = tid % kWaveSize;
+  const int hh = lane / 32;
+  const int c = lane % 32;
+  // t.head is a key/value head; its G query heads are qh0 .. qh0 + G - 1, and
+  // dK, dV sum over all of them (the query-tile loop runs over the group).
+  const int Hkv = H / G;
+  const int bi = t.head / Hkv;
+  const int hk = t.head % Hkv;
+  const int qh0 = bi * H + hk * G;
+
+  const int w0 = t.r_start + kg * 32;  // first key of this wave
+  const bool wave_active = w0 < t.r_end;
+  const int wave_last = min(w0 + 32, t.r_end) - 1;
+  const int key = w0 + c;
+  const int q_lo = t.r_start;  // the first query that sees any of these keys
+  const int ntq = (t.seg_end - q_lo + BMQ - 1) / BMQ;  // query tiles per query head
+  const int ntile = G * ntq;                            // over the whole group
+
+  auto qslot = [&]<int P>() { return lds_cast(P == 0 ? sQ0 : P == 1 ? sQ1 : sQ2); };
+  auto oslot = [&]<int P>() { return lds_cast(P == 0 ? sO0 : P == 1 ? sO1 : sO2); };
+  auto lslot = [&]<int P>() { return lds_cast(P == 0 ? sL0 : P == 1 ? sL1 : sL2); };
+  auto dslot = [&]<int P>() { return lds_cast(P == 0 ? sD0 : P == 1 ? sD1 : sD2); };
+  uint32_t qoff[QTile::kPerWave], dooff[QTile::kPerWave];
+  QTile::lane_offsets(qoff, wave, lane, lq.ss);
+  QTile::lane_offsets(dooff, wave, lane, ldo.ss);
+  auto issue = [&]<int P>(int it) {
+    const int g = it / ntq;
+    const int q0 = q_lo + (it - g * ntq) * BMQ;
+    const size_t rbase = (size_t)(qh0 + g) * S;
+    // Queries past the segment read as zeros (Q, dO, LSE, Delta all 0): their
+    // P is 1 but dO and Q are 0, so they add nothing to dV or dK.
+    const GBuf gq(q + panel_off(lq, bi, hk * G + g), panel_bytes(lq, t.seg_end, D, sizeof(T)));
+    const GBuf gdo(dO + panel_off(ldo, bi, hk * G + g), panel_bytes(ldo, t.seg_end, D, sizeof(T)));
+    const GBuf glse(lse + rbase, (uint32_t)(t.seg_end * sizeof(float)));
+    const GBuf gdel(delta + rbase, (uint32_t)(t.seg_end * sizeof(float)));
+    QTile::issue_at(gq, qslot.template operator()<P>(), QTile::row0_bytes(q0, lq.ss), qoff, wave);
+    QTile::issue_at(gdo, oslot.template operator()<P>(), QTile::row0_bytes(q0, ldo.ss), dooff, wave);
+    if (wave == 0) dma_vec64(glse, lslot.template operator()<P>(), q0, lane);
+    if (wave == 1) dma_vec64(gdel, dslot.template operator()<P>(), q0, lane);
+  };
+  issue.template operator()<0>(0);
+
+  // K (V-wave) or V (K-wave) fragments of this wave's keys, in registers.
+  const GBuf gkv = vwave ? GBuf(k + panel_off(lk, bi, hk), panel_bytes(lk, t.r_end, D, sizeof(T)))
+                         : GBuf(v + panel_off(lv, bi, hk), panel_bytes(lv, t.r_end, D, sizeof(T)));
+  const int kvss = vwave ? lk.ss : lv.ss;
+  frag kvf[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) kvf[kb] = global_frag_rs<T>(gkv, key, 16 * kb + 8 * hh, kvss);
+  f32x16 acc[DB];  // dV (V-wave) or dK (K-wave)
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  const TrSwz<T, D> tr0(lane);    // transposed reads of the Q and dO tiles
+  const RowFrag<T, D> rf0(lane);  // row fragments of the same tiles
+  const typename E::rows_frag ones = E::rows_b(hh);
+  const float rscale = 1.0f / scale;
+  lds_t<f32x4> *const xp = lds_cast(sP) + kg * 2 * 4 * kWaveSize;  // this key group's two buffers
+
+  // V-wave, tile `it` in slot P: S', P (masked), P to the K-wave, dV.
+  auto vtile = [&]<int P>(int it) {
+    const int q0 = q_lo + (it % ntq) * BMQ;
+    if (q0 + BMQ - 1 < w0) return;  // every query precedes every key here
+    const lds_t<T> *sq = qslot.template operator()<P>();
+    const lds_t<T> *so = oslot.template operator()<P>();
+    const lds_t<float> *sl = lslot.template operator()<P>();
+    const TrSwz<T, D> tr = tr0.pinned();
+    const RowFrag<T, D> rf = rf0.pinned();
+    f32x16 sacc = f32x16{};
+    mma_priority_hi();
+    E::mma_rows(sacc, E::rows_a(-sl[c] * rscale, hh), ones);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) E::mma(sacc, rf(sq, 0, kb), kvf[kb]);
+    mma_priority_lo();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = fast_exp2(sacc[r] * c2);
+    if (q0 < wave_last) {
+      // query q0 + off < key, off = 8 (r / 4) + 4 hh + r % 4
+      const int lim = key - q0 - 4 * hh;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = (8 * (r / 4) + (r % 4)) < lim ? 0.f : sacc[r];
+    }
+    lds_t<f32x4> *xb = xp + (it & 1) * 4 * kWaveSize;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 p4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p4[i] = sacc[4 * g + i];
+      xb[g * kWaveSize + lane] = p4;
+    }
+    const frag p0 = E::pack(sacc, 0), p1 = E::pack(sacc, 1);
+    mma_priority_hi();
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      E::mma(acc[db], tr(so, 0, db), p0);
+      E::mma(acc[db], tr(so, 16, db), p1);
+    }
+    mma_priority_lo();
+  };
+
+  // K-wave, tile `it` in slot P (its P written one step earlier): dP', dS, dK.
+  auto ktile = [&]<int P>(int it) {
+    const int q0 = q_lo + (it % ntq) * BMQ;
+    if (q0 + BMQ - 1 < w0) return;
+    const lds_t<T> *sq = qslot.template operator()<P>();
+    const lds_t<T> *so = oslot.template operator()<P>();
+    const lds_t<float> *sd = dslot.template operator()<P>();
+    const TrSwz<T, D> tr = tr0.pinned();
+    const RowFrag<T, D> rf = rf0.pinned();
+    f32x16 pacc = f32x16{};
+    mma_priority_hi();
+    E::mma_rows(pacc, E::rows_a(-sd[c], hh), ones);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) E::mma(pacc, rf(so, 0, kb), kvf[kb]);
+    mma_priority_lo();
+    const lds_t<f32x4> *xb = xp + (it & 1) * 4 * kWaveSize;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 p4 = xb[g * kWaveSize + lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pacc[4 * g + i] = p4[i] * pacc[4 * g + i];
+    }
+    const frag s0 = E::pack(pacc, 0), s1 = E::pack(pacc, 1);
+    mma_priority_hi();
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      E::mma(acc[db], tr(sq, 0, db), s0);
+      E::mma(acc[db], tr(sq, 16, db), s1);
+    }
+    mma_priority_lo();
+  };
+
+  // Step j (slot P = j % 3): wait for tile j's copies and this wave's LDS
+  // writes, barrier, start the copy of tile j + 1, then the V-wave takes
+  // tile j and the K-wave tile j - 1.  ntile + 1 steps for every wave.
+  auto step = [&]<int P>(int j) {
+    wait_vmcnt_lgkm0<0>();
+    wg_barrier();
+    if (j + 1 < ntile) issue.template operator()<(P + 1) % 3>(j + 1);
+    if (!wave_active) return;
+    if (vwave) {
+      if (j < ntile) vtile.template operator()<P>(j);
+    } else {
+      if (j >= 1) ktile.template operator()<(P + 2) % 3>(j - 1);
+    }
+  };
+  for (int j = 0; j <= ntile; j += 3) {
+    step.template operator()<0>(j);
+    if (j + 1 <= ntile) step.template operator()<1>(j + 1);
+    if (j + 2 <= ntile) step.template operator()<2>(j + 2);
+  }
+
+  if (!wave_active) return;
+  OT *out = vwave ? dv : dk;
+  const Layout &lout = vwave ? ldv : ldk;
+  const GBuf gout(out + panel_off(lout, bi, hk), panel_bytes(lout, t.r_end, D, sizeof(OT)));
+  const float osc = vwave ? 1.0f : scale;
+  // RoPE (dK only): this key's table row (keys past the tile end are not stored)
+  const float *rrow = (rope == nullptr || vwave)
+                          ? nullptr
+                          : rope + (size_t)min(min(key, t.r_end - 1) - t.seg_start, rope_npos - 1) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 a4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a4[i] = acc[db][4 * g + i] * osc;
+      if (rrow != nullptr) rope_back(a4, *reinterpret_cast<const f32x4 *>(rrow + db * 32 + 8 * g + 4 * hh));
+      store_out4<OT>(gout, a4, (uint32_t)key * lout.ss + (uint32_t)(db * 32 + 8 * g + 4 * hh));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dQ.  A workgroup owns BM = 128 queries of one head (32 per wave) and loops
 // over key tiles of BN rows up to its causal diagonal.  K and V tiles arrive
 // by direct global->LDS copies into two ring slots one iteration ahead; K is
@@ -599,12 +826,38 @@ static hipError_t launch_dkdv_split(const Args &a) {
   return hipGetLastError();
 }
 
-// Grouped heads with an even group size, 16-bit inputs: two halves per key
-// group (twice the workgroups); otherwise one.
+template <typename T, typename OT, int D, bool DOC>
+static hipError_t launch_dkdv_pair(const Args &a) {
+  constexpr int BN = 64;  // keys per workgroup
+  const float c2 = a.scale * kLog2e;
+  dim3 grid;
+  int ntiles;
+  if (DOC) {
+    ntiles = (a.max_seqlen + BN - 1) / BN;
+    grid = dim3(ntiles * a.n_seqs * a.H_kv);
+  } else {
+    ntiles = (a.S + BN - 1) / BN;
+    grid = dim3(ntiles * a.B * a.H_kv);
+  }
+  hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<T, OT, D, 1, DOC>), grid, dim3(256), 0, a.stream,
+                     static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
+                     static_cast<const T *>(a.dO), a.lse_in, a.delta_in, static_cast<OT *>(a.dk),
+                     static_cast<OT *>(a.dv), a.S, c2, a.scale, a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv,
+                     a.rope, a.rope_npos, a.lq, a.lk, a.lv, a.ldo, a.ldk, a.ldv);
+  return hipGetLastError();
+}
+
+// 16-bit inputs: grouped heads with an even group size split the group over
+// two waves per key group; otherwise, at D = 128 (where one wave holding
+// both accumulators leaves room for one wave per SIMD) wave pairs; else one
+// wave per 32 keys.  Measured on MI355X: the pairs take S = 8192, D = 128
+// from 760 to 710 us but are slower at D = 64 (LDS for three workgroups per
+// CU, a barrier per 17 products) and than the group split.
 template <typename T, typename OT, int D, bool DOC>
 static hipError_t launch_dkdv_t(const Args &a) {
   if constexpr (sizeof(T) == 2) {
     if ((a.H / a.H_kv) % 2 == 0) return launch_dkdv_split<T, OT, D, DOC, 2>(a);
+    if constexpr (D == 128) return launch_dkdv_pair<T, OT, D, DOC>(a);
   }
   return launch_dkdv_split<T, OT, D, DOC, 1>(a);
 }

@@ -645,6 +645,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// The same, and also until every LDS access of this wave has completed (its
+// LDS writes are then visible to the workgroup after the next barrier).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
 // Workgroup barrier without the memory fence of __syncthreads (which would
 // wait for every copy in flight); LDS visibility of the copies a wave waited
 // for is what the barrier publishes.
