@@ -30,9 +30,10 @@ int check_mask(int B, int H, int S, int mask_mode, const int32_t *cu_seqlens, in
   if (cu_seqlens == nullptr) return ATTN_ERR_NULL;
   if (B != 1 || n_seqs < 1 || n_seqs > S) return ATTN_ERR_SEQLENS;
   if (max_seqlen < 1 || max_seqlen > S) return ATTN_ERR_SEQLENS;
-  // the launch has one workgroup per (128-row tile of the longest document,
-  // document, head)
-  if ((int64_t)((max_seqlen + 127) / 128) * n_seqs * H >= ((int64_t)1 << 31)) return ATTN_ERR_SEQLENS;
+  // a launch has one workgroup per (tile of the longest document, document,
+  // head), with tiles of 64 rows at the finest (the backward's 64-key
+  // workgroups)
+  if ((int64_t)((max_seqlen + 63) / 64) * n_seqs * H >= ((int64_t)1 << 31)) return ATTN_ERR_SEQLENS;
   return ATTN_OK;
 }
 

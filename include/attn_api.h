@@ -70,7 +70,7 @@ typedef enum attn_status {
   ATTN_ERR_DTYPE = -4,         /* unknown input dtype                              */
   ATTN_ERR_MASK = -5,          /* unknown mask mode                                */
   ATTN_ERR_SEQLENS = -6,       /* DOC_CAUSAL with B != 1, n_seqs outside 1..S, max_seqlen
-                                  outside 1..S, or ceil(max_seqlen/128)*n_seqs*H >= 2^31 */
+                                  outside 1..S, or ceil(max_seqlen/64)*n_seqs*H >= 2^31 */
   ATTN_ERR_HIP = -7,           /* a HIP runtime call or kernel launch failed       */
   ATTN_ERR_UNIMPLEMENTED = -8, /* valid request the library does not implement     */
   ATTN_ERR_SCALE = -9,         /* scale not finite or not > 0                      */

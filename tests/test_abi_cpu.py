@@ -233,6 +233,8 @@ def _params(**kw):
     (dict(out_dtype=2), -4), (dict(out_dtype=7), -4), (dict(dtype=0, out_dtype=1), -4),
     (dict(dtype=2, out_dtype=1), -4), (dict(q=None), -1), (dict(H_kv=3), -10), (dict(D=40), -3),
     (dict(mask_mode=1, cu_seqlens=FAKE, n_seqs=2, max_seqlen=40, B=2), -6), (dict(scale=0.0), -9),
+    # 2^18 tiles of 64 rows x 2^13 documents x 1 head = 2^31 workgroups
+    (dict(mask_mode=1, cu_seqlens=FAKE, n_seqs=1 << 13, max_seqlen=(1 << 24) - 1, S=(1 << 24) - 1, D=32, H=1), -6),
     (dict(rope_table=FAKE, rope_npos=64, q_rot=None, k_rot=FAKE), -1),
     (dict(rope_table=FAKE, rope_npos=63, q_rot=FAKE, k_rot=FAKE), -12),
 ])
