@@ -40,6 +40,9 @@ CASES = [
     ("bf16", 1, 16, 4, 1024, 64),  # the 237M-class shape with 4 K/V heads
     ("f32", 2, 4, 2, 100, 32),
     ("f32", 1, 4, 1, 129, 128),
+    ("bf16", 1, 6, 2, 300, 128),   # odd group (G = 3): dK/dV by wave pairs, three heads per key
+    ("f16", 1, 9, 3, 257, 128),
+    ("bf16", 2, 6, 2, 190, 64),    # odd group at D = 64: one wave per 32 keys
 ]
 
 
@@ -50,14 +53,14 @@ def test_gqa_parity(dtype, B, H, H_kv, S, D):
     compare(run_hip(x), oracle(x), dtype, tag=f"gqa {dtype} B{B} H{H}/{H_kv} S{S} D{D}")
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_gqa_packed_documents(D):
+@pytest.mark.parametrize("D,H", [(64, 8), (128, 8), (128, 6)])
+def test_gqa_packed_documents(D, H):
     cu = make_cu_seqlens(700, 1, 260, 41 + D)
-    log(f"[gqa] packed ({len(cu) - 1} docs) D{D}")
-    x = gqa_inputs("bf16", 1, 8, 2, int(cu[-1]), D, 42 + D)
+    log(f"[gqa] packed ({len(cu) - 1} docs) D{D} H{H}/2")
+    x = gqa_inputs("bf16", 1, H, 2, int(cu[-1]), D, 42 + D + H)
     x["cu_seqlens"] = cu
     x["mask_mode"] = MASK_DOC_CAUSAL
-    compare(run_hip(x), oracle(x), "bf16", tag=f"gqa packed D{D}")
+    compare(run_hip(x), oracle(x), "bf16", tag=f"gqa packed D{D} H{H}/2")
 
 
 def test_gqa_bitwise_reproducible():
