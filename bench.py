@@ -4,7 +4,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the whole path on resident inputs: attn_fwd (forward
-with LSE) then attn_bwd (Delta preprocess, dK/dV, dQ).  Throughput counts the
+with LSE) then attn_bwd (Delta preprocess, dK/dV, dQ), called on a stream of
+the workload's own.  (The same step captured as a HIP graph and replayed is
+slower on this stack: ms_per_step_graph.)  Throughput counts the
 causal FLOPs actually allowed by the mask: 4*D per allowed (query, key) pair
 forward and 10*D backward (the five products of the FlashAttention-2
 accounting), divided by the measured time.  One JSON line is printed.
@@ -105,7 +107,9 @@ class Workload:
         self.pairs = allowed_pair_count(S, B, H, cu)
         self.flops_fwd = 4 * D * self.pairs
         self.flops_bwd = 10 * D * self.pairs
-        self.stream = torch.cuda.current_stream()
+        # a stream of its own (default priority), so the step can be captured
+        self.stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
         self.sargs = dict(mask_mode=cfg.mask_mode, cu_seqlens=self.cu, max_seqlen=self.max_seqlen,
                           stream=self.stream)
         if cfg.rope:  # RoPE: the table is built once, as a model does; q_rot, k_rot are kept for the backward
@@ -148,14 +152,36 @@ class Workload:
         self.fwd()
         self.bwd()
 
-    def timed_steps(self, steps, warmup):
+    def capture(self):
+        """The step captured once as a HIP graph on the workload's stream (its
+        launches only: the entry points allocate, copy and clear nothing)."""
         import torch
-        for _ in range(warmup):
+        self.step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.stream):
             self.step()
+        torch.cuda.synchronize()
+        return g
+
+    def timed_steps(self, steps, warmup, graph=False):
+        """Seconds per step over `steps` steps after `warmup`: the entry points
+        called in turn, or (graph=True) one replay of the captured step."""
+        import torch
+        if graph:
+            g = self.capture()
+
+            def run():
+                with torch.cuda.stream(self.stream):
+                    g.replay()
+        else:
+            run = self.step
+        for _ in range(warmup):
+            run()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(steps):
-            self.step()
+            run()
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / steps
 
@@ -216,7 +242,8 @@ def measured_traffic(kernel, workload):
 
 
 KERNEL_NAMES = {"attn_fwd_kernel": "fwd", "attn_bwd_preprocess_kernel": "pre",
-                "attn_bwd_dkdv_kernel": "dkdv", "attn_bwd_dq_kernel": "dq", "neg_kernel": "copy"}
+                "attn_bwd_dkdv_kernel": "dkdv", "attn_bwd_dkdv_pair_kernel": "dkdv", "attn_bwd_dq_kernel": "dq",
+                "neg_kernel": "copy"}
 
 
 def kernel_key(name):
@@ -382,6 +409,7 @@ def measure_decode(name, reps):
 def measure(name, steps, warmup, reps):
     w = Workload(name)
     sec = w.timed_steps(steps, warmup)
+    sec_graph = w.timed_steps(steps, warmup, graph=True)
     total = w.flops_fwd + w.flops_bwd
     tflops = total / sec / 1e12
     times = w.kernel_times(reps)
@@ -390,6 +418,7 @@ def measure(name, steps, warmup, reps):
     ms_bwd = times["bwd"]["mean_ms"]
     summary = {
         "tflops": tflops, "pct_peak": 100.0 * tflops / peak, "ms_per_step": sec * 1e3,
+        "ms_per_step_graph": sec_graph * 1e3,
         "fwd_tflops": w.flops_fwd / (ms_fwd * 1e-3) / 1e12,
         "bwd_tflops": w.flops_bwd / (ms_bwd * 1e-3) / 1e12,
         "kernels_ms": {k: round(v["mean_ms"], 5) for k, v in times.items()},
@@ -462,6 +491,7 @@ def main():
                    "mask": "packed_documents" if cfg.mask_mode else "causal",
                    "outputs": cfg.dtype if cfg.out16 else "fp32", "parallelism": "single GPU"},
         "pct_peak": summary["pct_peak"],
+        "ms_per_step_graph": summary["ms_per_step_graph"],
         "fwd_tflops": summary["fwd_tflops"],
         "bwd_tflops": summary["bwd_tflops"],
         "kernels": {k: v["mean_ms"] for k, v in times.items()},
