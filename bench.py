@@ -6,7 +6,7 @@
 A step is one pass of the whole path on resident inputs: attn_fwd (forward
 with LSE) then attn_bwd (Delta preprocess, dK/dV, dQ), called on a stream of
 the workload's own.  (The same step captured as a HIP graph and replayed is
-slower on this stack: ms_per_step_graph.)  Throughput counts the
+no faster on this stack: ms_per_step_graph.)  Throughput counts the
 causal FLOPs actually allowed by the mask: 4*D per allowed (query, key) pair
 forward and 10*D backward (the five products of the FlashAttention-2
 accounting), divided by the measured time.  One JSON line is printed.
