@@ -28,7 +28,8 @@ int check_mask(int B, int H, int S, int mask_mode, const int32_t *cu_seqlens, in
   if (mask_mode == ATTN_MASK_CAUSAL) return ATTN_OK;
   if (mask_mode != ATTN_MASK_DOC_CAUSAL) return ATTN_ERR_MASK;
   if (cu_seqlens == nullptr) return ATTN_ERR_NULL;
-  if (B != 1 || n_seqs < 1 || n_seqs > S) return ATTN_ERR_SEQLENS;
+  // empty documents are allowed, so n_seqs may exceed S
+  if (B != 1 || n_seqs < 1) return ATTN_ERR_SEQLENS;
   if (max_seqlen < 1 || max_seqlen > S) return ATTN_ERR_SEQLENS;
   // a launch has one workgroup per (tile of the longest document, document,
   // head), with tiles of 64 rows at the finest (the backward's 64-key
@@ -216,7 +217,7 @@ const char *attn_status_string(int status) {
     case ATTN_ERR_HEAD_DIM: return "head dimension D must be 32, 64 or 128";
     case ATTN_ERR_DTYPE: return "unknown input dtype (ATTN_DTYPE_F32, ATTN_DTYPE_BF16 or ATTN_DTYPE_F16)";
     case ATTN_ERR_MASK: return "unknown mask mode (ATTN_MASK_CAUSAL or ATTN_MASK_DOC_CAUSAL)";
-    case ATTN_ERR_SEQLENS: return "packed-document mode needs B == 1, 1 <= n_seqs <= S and 1 <= max_seqlen <= S";
+    case ATTN_ERR_SEQLENS: return "packed-document mode needs B == 1, n_seqs >= 1, 1 <= max_seqlen <= S and ceil(max_seqlen/64)*n_seqs*H < 2^31";
     case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case ATTN_ERR_UNIMPLEMENTED: return "valid request that this library does not implement";
     case ATTN_ERR_SCALE: return "scale must be finite and > 0";

@@ -24,7 +24,8 @@
  *   ATTN_MASK_CAUSAL:     key j allowed for query i iff j <= i.
  *   ATTN_MASK_DOC_CAUSAL: packed documents (Cort33x, "Preserving context in
  *     the data"): the sequence is the concatenation of n_seqs documents with
- *     boundaries cu_seqlens[0] = 0 < cu_seqlens[1] < ... < cu_seqlens[n_seqs] = S;
+ *     boundaries cu_seqlens[0] = 0 <= cu_seqlens[1] <= ... <= cu_seqlens[n_seqs] = S
+ *     (a document may be empty: it owns no rows and adds nothing);
  *     key j allowed for query i iff j <= i and both lie in the same document.
  *
  * Layout.  Q, K, V, dO, O, dQ, dK, dV are contiguous [B, H, S, D] row-major
@@ -69,8 +70,9 @@ typedef enum attn_status {
   ATTN_ERR_HEAD_DIM = -3,      /* D not in {32, 64, 128}                           */
   ATTN_ERR_DTYPE = -4,         /* unknown input dtype                              */
   ATTN_ERR_MASK = -5,          /* unknown mask mode                                */
-  ATTN_ERR_SEQLENS = -6,       /* DOC_CAUSAL with B != 1, n_seqs outside 1..S, max_seqlen
-                                  outside 1..S, or ceil(max_seqlen/64)*n_seqs*H >= 2^31 */
+  ATTN_ERR_SEQLENS = -6,       /* DOC_CAUSAL with B != 1, n_seqs < 1, max_seqlen
+                                  outside 1..S, or ceil(max_seqlen/64)*n_seqs*H >= 2^31
+                                  (n_seqs may exceed S when documents are empty) */
   ATTN_ERR_HIP = -7,           /* a HIP runtime call or kernel launch failed       */
   ATTN_ERR_UNIMPLEMENTED = -8, /* valid request the library does not implement     */
   ATTN_ERR_SCALE = -9,         /* scale not finite or not > 0                      */

@@ -50,8 +50,10 @@ MASK_DOC_CAUSAL = 1
 
 def _doc_ids(S, cu_seqlens):
     cu = np.asarray(cu_seqlens, dtype=np.int64)
-    if cu.ndim != 1 or cu.size < 2 or cu[0] != 0 or cu[-1] != S or np.any(np.diff(cu) <= 0):
-        raise ValueError("cu_seqlens must start at 0, increase strictly and end at S")
+    if cu.ndim != 1 or cu.size < 2 or cu[0] != 0 or cu[-1] != S or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must start at 0, never decrease and end at S")
+    # row s belongs to the last document starting at or before it (an empty
+    # document starts where the next one does and owns no row)
     return np.searchsorted(cu, np.arange(S), side="right") - 1
 
 

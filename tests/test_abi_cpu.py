@@ -66,7 +66,7 @@ def _bwd(lib, **kw):
     (dict(mask=1, cu=None, n=1, mx=64), -1),
     (dict(mask=1, cu=FAKE, n=1, mx=64, B=2), -6),
     (dict(mask=1, cu=FAKE, n=0, mx=64), -6),
-    (dict(mask=1, cu=FAKE, n=65, mx=64), -6),
+    (dict(mask=1, cu=FAKE, n=-1, mx=64), -6),
     (dict(mask=1, cu=FAKE, n=2, mx=0), -6),
     (dict(mask=1, cu=FAKE, n=2, mx=65), -6),
     (dict(S=0), -2), (dict(S=-5), -2), (dict(B=0), -2), (dict(H=0), -2),

@@ -106,9 +106,12 @@ def test_mask_shapes():
     assert m.astype(int).tolist() == [[1, 0, 0, 0, 0], [1, 1, 0, 0, 0],
                                       [0, 0, 1, 0, 0], [0, 0, 1, 1, 0], [0, 0, 1, 1, 1]]
     with pytest.raises(ValueError):
-        allowed_mask(5, MASK_DOC_CAUSAL, [0, 3, 3, 5])
+        allowed_mask(5, MASK_DOC_CAUSAL, [0, 4, 3, 5])  # a boundary that goes back
     with pytest.raises(ValueError):
-        allowed_mask(5, MASK_DOC_CAUSAL, [0, 4])
+        allowed_mask(5, MASK_DOC_CAUSAL, [0, 4])        # does not end at S
+    # empty documents own no rows: the mask is that of the non-empty ones
+    for cu in ([0, 3, 3, 5], [0, 0, 3, 5], [0, 3, 5, 5], [0, 0, 0, 3, 3, 5, 5]):
+        assert (allowed_mask(5, MASK_DOC_CAUSAL, cu) == allowed_mask(5, MASK_DOC_CAUSAL, [0, 3, 5])).all()
 
 
 # ---------------------------------------------------------------- causality
@@ -163,6 +166,23 @@ def test_packed_equals_documents_run_alone():
         ri = attention_bwd_ref(q[:, :, sl], k[:, :, sl], v[:, :, sl], do[:, :, sl], scale)
         for name in ("o", "lse", "dq", "dk", "dv", "delta"):
             np.testing.assert_allclose(r[name][:, :, sl], ri[name], rtol=1e-13, atol=1e-14)
+
+
+def test_empty_documents_change_nothing():
+    """Empty documents (repeated boundaries, also first and last) leave every
+    output, and the RoPE positions, as without them."""
+    B, H, S, D = 1, 2, 20, 8
+    q, k, v, do = _qkvdo(B, H, S, D, 9)
+    ref = attention_bwd_ref(q, k, v, do, 0.35, MASK_DOC_CAUSAL, CU_SMALL)
+    a, b = int(CU_SMALL[1]), int(CU_SMALL[2])
+    cu_e = np.array([0, 0] + [int(x) for x in CU_SMALL[1:2]] * 3 + [int(x) for x in CU_SMALL[2:]] + [S],
+                    dtype=np.int32)
+    assert a < b and cu_e[0] == 0 and cu_e[-1] == S
+    r = attention_bwd_ref(q, k, v, do, 0.35, MASK_DOC_CAUSAL, cu_e)
+    for name in ("o", "lse", "dq", "dk", "dv", "delta"):
+        np.testing.assert_array_equal(r[name], ref[name])
+    from oracle import rope_positions
+    assert (rope_positions(S, MASK_DOC_CAUSAL, cu_e) == rope_positions(S, MASK_DOC_CAUSAL, CU_SMALL)).all()
 
 
 def test_single_document_equals_causal():

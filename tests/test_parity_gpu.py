@@ -136,6 +136,28 @@ def test_single_document_equals_causal_bitwise(dtype):
         assert bool((a[n] == b[n]).all()), n
 
 
+EMPTY_DOC_CU = ([0, 1, 2, 50, 51, 180, 181, 300, 429, 430],
+                [0, 0, 1, 2, 2, 2, 50, 51, 180, 181, 181, 300, 429, 430, 430, 430])
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("f32", 32), ("f32", 128)])
+def test_empty_documents_change_nothing(dtype, D):
+    """Empty documents (repeated boundaries: first, in between, several in a
+    row, last) own no rows: outputs match the oracle and are bitwise those of
+    the same call without them."""
+    cu, cu_e = EMPTY_DOC_CU
+    log(f"[doc] empty documents D={D} {dtype}")
+    x = _doc_inputs(dtype, D, cu_e, seed=5 + D)
+    assert len(cu_e) - 1 > 0 and int(np.min(np.diff(cu_e))) == 0
+    got = run_hip(x)
+    compare(got, oracle(x), dtype, tag=f"empty docs D{D} {dtype}")
+    y = dict(x)
+    y["cu_seqlens"] = np.asarray(cu, dtype=np.int32)
+    ref = run_hip(y)
+    for n in ("o", "lse", "dq", "dk", "dv", "delta"):
+        assert bool((got[n] == ref[n]).all()), n
+
+
 def test_large_logits():
     """Q and K scaled by 4: scores with std ~32 stress the running-max rescaling."""
     c = AttnConfig("big", B=2, H=2, S=512, D=64, dtype="bf16", qkv_scale=1.0)

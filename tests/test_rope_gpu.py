@@ -133,6 +133,23 @@ def test_rotation_positions_restart_per_document():
     check_rotated(q_rot, round_to_dtype(rope_rotate(x["q"], pos), "bf16"), x["q"], "bf16", "q_rot docs")
 
 
+def test_rope_empty_documents_change_nothing():
+    """RoPE positions restart per document; empty documents (first, in between,
+    last) own no rows and must not shift them: parity with the oracle, and
+    bitwise the outputs of the same call without the empty documents."""
+    cu = np.array([0, 1, 97, 98, 260, 300], dtype=np.int32)
+    cu_e = np.array([0, 0, 1, 97, 97, 97, 98, 260, 300, 300], dtype=np.int32)
+    log("[rope] empty documents bf16 D128 G=3")
+    x = _inputs(1, 3, 300, 128, "bf16", 81, H_kv=1, cu=cu_e)
+    out = run_rope(x)
+    compare(out, rope_oracle(x), "bf16", tag="rope empty docs")
+    y = dict(x)
+    y["cu_seqlens"] = cu
+    ref = run_rope(y)
+    for n in ("o", "lse", "dq", "dk", "dv", "delta", "q_rot", "k_rot"):
+        assert bool((out[n] == ref[n]).all()), n
+
+
 @pytest.mark.parametrize("B,H,S,D,dtype", [
     (2, 4, 300, 64, "bf16"), (1, 2, 1000, 128, "bf16"), (3, 2, 257, 32, "bf16"), (1, 1, 1, 64, "bf16"),
     (2, 2, 257, 64, "f16"), (1, 3, 130, 32, "f32"), (1, 2, 333, 128, "f32"), (2, 2, 190, 64, "f32"),
