@@ -847,17 +847,27 @@ static hipError_t launch_dkdv_pair(const Args &a) {
   return hipGetLastError();
 }
 
-// 16-bit inputs: grouped heads with an even group size split the group over
-// two waves per key group; otherwise, at D = 128 (where one wave holding
-// both accumulators leaves room for one wave per SIMD) wave pairs; else one
-// wave per 32 keys.  Measured on MI355X: the pairs take S = 8192, D = 128
-// from 760 to 710 us but are slower at D = 64 (LDS for three workgroups per
-// CU, a barrier per 17 products) and than the group split.
+// 16-bit inputs.  At D = 128, where one wave holding both accumulators
+// leaves room for one wave per SIMD, wave pairs (two per SIMD); at D = 64 the
+// pairs are slower (LDS for three workgroups per CU, a barrier per 17
+// products).  Grouped heads with an even group size can instead split the
+// group over two waves per key group, which halves the longest workgroup's
+// chain of query tiles.  Measured on MI355X (backward, bf16, D = 128, 12
+// shapes with 2 to 8 K/V heads and S from 1024 to 8192): with 64-key units
+// B * H_kv * ceil(S / 64) >= 1024, two rounds of the pair kernel's resident
+// workgroups on 256 CUs, the pairs are 9-13 % faster than the split; at 512
+// units within 3 % either way; at 256 units 27-29 % slower, the step then
+// waiting on the heads chained in the first key tiles.  Else one wave per
+// 32 keys.
 template <typename T, typename OT, int D, bool DOC>
 static hipError_t launch_dkdv_t(const Args &a) {
   if constexpr (sizeof(T) == 2) {
-    if ((a.H / a.H_kv) % 2 == 0) return launch_dkdv_split<T, OT, D, DOC, 2>(a);
-    if constexpr (D == 128) return launch_dkdv_pair<T, OT, D, DOC>(a);
+    const bool even_group = (a.H / a.H_kv) % 2 == 0;
+    if constexpr (D == 128) {
+      const int64_t units = (int64_t)a.B * a.H_kv * ((a.S + 63) / 64);
+      if (!even_group || units >= 1024) return launch_dkdv_pair<T, OT, D, DOC>(a);
+    }
+    if (even_group) return launch_dkdv_split<T, OT, D, DOC, 2>(a);
   }
   return launch_dkdv_split<T, OT, D, DOC, 1>(a);
 }

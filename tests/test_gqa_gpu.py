@@ -53,6 +53,32 @@ def test_gqa_parity(dtype, B, H, H_kv, S, D):
     compare(run_hip(x), oracle(x), dtype, tag=f"gqa {dtype} B{B} H{H}/{H_kv} S{S} D{D}")
 
 
+@pytest.mark.parametrize("B,H,H_kv,S", [(4, 16, 8, 2048), (16, 16, 4, 1024)])
+def test_gqa_even_group_wave_pairs_sampled(B, H, H_kv, S):
+    """Even groups at D = 128 with B * H_kv * ceil(S / 64) >= 1024 64-key units
+    take dK/dV by wave pairs (smaller grids split the group instead, covered
+    above).  The oracle checks sampled (batch, K/V head) slices: batch entries
+    and K/V heads are independent problems with G query heads each."""
+    import torch
+    D, G = 128, H // H_kv
+    assert B * H_kv * ((S + 63) // 64) >= 1024 and G % 2 == 0
+    log(f"[gqa] wave pairs, even group: B{B} H{H} H_kv{H_kv} S{S} D{D}")
+    x = gqa_inputs("bf16", B, H, H_kv, S, D, 900 + B + S)
+    out = run_hip(x)
+    rng = np.random.default_rng(901)
+    for b, j in [(0, 0), (B - 1, H_kv - 1), (int(rng.integers(B)), int(rng.integers(H_kv)))]:
+        hs = slice(j * G, (j + 1) * G)
+        xs = dict(x, B=1, H=G)
+        for n in ("q", "do"):
+            xs[n] = np.ascontiguousarray(x[n][b:b + 1, hs])
+        for n in ("k", "v"):
+            xs[n] = np.ascontiguousarray(x[n][b:b + 1, j:j + 1])
+        got = {n: out[n][b:b + 1, hs] for n in ("o", "lse", "dq", "delta")}
+        got.update({n: out[n][b:b + 1, j:j + 1] for n in ("dk", "dv")})
+        assert all(bool(torch.isfinite(t).all()) for t in out.values())
+        compare(got, oracle(xs), "bf16", tag=f"gqa pairs B{B} H{H}/{H_kv} S{S} slice ({b},{j})")
+
+
 @pytest.mark.parametrize("D,H", [(64, 8), (128, 8), (128, 6)])
 def test_gqa_packed_documents(D, H):
     cu = make_cu_seqlens(700, 1, 260, 41 + D)
