@@ -1,8 +1,8 @@
 """Seeded random combinations of every option of attn_fwd_ex / attn_bwd_ex
 (input dtype, D, causal or packed documents, grouped K/V heads, RoPE, 16-bit
-outputs, [B, S, H, D] views) against the fp64 oracle, at sizes the oracle
-finishes quickly.  The cases are drawn once from a fixed seed, so a failure
-names a reproducible case."""
+outputs, [B, S, H, D] views, empty documents among packed ones) against
+the fp64 oracle, at sizes the oracle finishes quickly.  The cases are drawn
+once from a fixed seed, so a failure names a reproducible case."""
 import numpy as np
 import pytest
 
@@ -12,7 +12,7 @@ from tests.gpu_util import compare, log
 pytestmark = pytest.mark.gpu
 
 
-def _draw_cases(n=28, seed=2026):
+def _draw_cases(n=96, seed=2026):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
@@ -26,6 +26,11 @@ def _draw_cases(n=28, seed=2026):
             lens = rng.integers(1, 160, size=int(rng.integers(1, 5)))
             cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
             S = int(cu[-1])
+            if i % 3 == 0:  # empty documents (repeated boundaries), from a stream of their own
+                er = np.random.default_rng(seed + i)
+                for _ in range(int(er.integers(1, 4))):
+                    j = int(er.integers(0, len(cu)))
+                    cu = np.insert(cu, j, cu[j])
         else:
             cu = None
             S = int(rng.integers(1, 330))
