@@ -158,6 +158,18 @@ def test_empty_documents_change_nothing(dtype, D):
         assert bool((got[n] == ref[n]).all()), n
 
 
+@pytest.mark.parametrize("B", [48, 49])
+def test_dq_tile_choice_boundary(B):
+    """Causal 16-bit D = 64 dQ takes 64-key tiles when B * H * ceil(S / 128)
+    <= 768 workgroups and 32-key tiles above: B = 48 and 49 at H = 2, S = 1024
+    give 768 and 784.  Sampled heads against the oracle."""
+    H, S, D = 2, 1024, 64
+    log(f"[edge] dQ tile choice B{B} H{H} S{S} D{D} ({B * H * S // 128} workgroups)")
+    x = make_inputs(_shape_cfg("bf16", D), 60 + B, shape=(B, H, S, D))
+    heads = [(0, 0), (B - 1, 1), (B // 2, 0)]
+    compare(run_hip(x), oracle(x, heads=heads), "bf16", heads=heads, tag=f"dq tiles B{B}")
+
+
 def test_large_logits():
     """Q and K scaled by 4: scores with std ~32 stress the running-max rescaling."""
     c = AttnConfig("big", B=2, H=2, S=512, D=64, dtype="bf16", qkv_scale=1.0)
