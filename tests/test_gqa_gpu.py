@@ -53,16 +53,19 @@ def test_gqa_parity(dtype, B, H, H_kv, S, D):
     compare(run_hip(x), oracle(x), dtype, tag=f"gqa {dtype} B{B} H{H}/{H_kv} S{S} D{D}")
 
 
-@pytest.mark.parametrize("B,H,H_kv,S", [(4, 16, 8, 2048), (16, 16, 4, 1024)])
+@pytest.mark.parametrize("B,H,H_kv,S", [(4, 16, 8, 2048), (16, 16, 4, 1024), (15, 4, 2, 2048), (16, 4, 2, 2048)])
 def test_gqa_even_group_wave_pairs_sampled(B, H, H_kv, S):
     """Even groups at D = 128 with B * H_kv * ceil(S / 64) >= 1024 64-key units
-    take dK/dV by wave pairs (smaller grids split the group instead, covered
-    above).  The oracle checks sampled (batch, K/V head) slices: batch entries
-    and K/V heads are independent problems with G query heads each."""
+    take dK/dV by wave pairs, smaller grids split the group (the last two
+    cases sit on either side: 960 and 1024 units).  The oracle checks sampled
+    (batch, K/V head) slices: batch entries and K/V heads are independent
+    problems with G query heads each."""
     import torch
     D, G = 128, H // H_kv
-    assert B * H_kv * ((S + 63) // 64) >= 1024 and G % 2 == 0
-    log(f"[gqa] wave pairs, even group: B{B} H{H} H_kv{H_kv} S{S} D{D}")
+    units = B * H_kv * ((S + 63) // 64)
+    assert G % 2 == 0
+    log(f"[gqa] even group: B{B} H{H} H_kv{H_kv} S{S} D{D}, {units} units "
+        f"({'wave pairs' if units >= 1024 else 'group split'})")
     x = gqa_inputs("bf16", B, H, H_kv, S, D, 900 + B + S)
     out = run_hip(x)
     rng = np.random.default_rng(901)
