@@ -4,21 +4,35 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the whole path on resident inputs: attn_fwd (forward
-with LSE) then attn_bwd (Delta preprocess, dK/dV, dQ), called on a stream of
-the workload's own.  (The same step captured as a HIP graph and replayed is
-no faster on this stack: ms_per_step_graph.)  Throughput counts the
-causal FLOPs actually allowed by the mask: 4*D per allowed (query, key) pair
-forward and 10*D backward (the five products of the FlashAttention-2
-accounting), divided by the measured time.  One JSON line is printed.
+with LSE) then attn_bwd (dQ with Delta, then dK/dV), called on a stream of
+the workload's own.  Throughput counts the causal FLOPs actually allowed by
+the mask: 4*D per allowed (query, key) pair forward and 10*D backward (the
+five products of the FlashAttention-2 accounting), divided by the measured
+time.  One JSON line is printed.
+
+Timing.  W untimed steps, then exactly K steps between two device
+synchronisations: `ms_per_step` and `value` come from the host clock around
+those K steps.  Inside the same loop HIP events on the launch stream bracket
+every step's forward and backward, giving per-iteration median, p10 and p90
+(`events_ms`).  A second loop writes a 512 MiB buffer before each step (more
+than the 256 MiB last-level cache holds), so every step starts cold
+(`cold`).  The GPU's graphics clock is sampled while steps run back to back
+(`sclk_mhz`).
 
 Besides the headline workload the line carries:
+  kernels       per-kernel median/p10/p90 from HIP events, each kernel run
+                through its own entry point: the forward, the two stages
+                attn_bwd runs (dQ with Delta fused, then dK/dV) and the
+                standalone Delta preprocess (fp32 inputs and staged callers);
+  rooflines     each of those kernels against its binding roof,
+                min(matrix-core peak, arithmetic intensity x HBM peak), from
+                its counted flops and algorithmic HBM bytes;
+  roofline      the dominant kernel's entry, with the rocprofv3-measured HBM
+                traffic when it was taken on the current sources;
   by_workload   the same measurement at the other full-size workloads
                 (context 512, 8192, packed documents, grouped-query heads,
-                RoPE on q and k, bf16 outputs),
-                fewer steps, and one decode step against a full 8192-token
-                K/V cache (time, GB/s against HBM peak);
-  kernels       per-kernel mean duration from HIP events on the launch stream;
-  roofline      the dominant kernel against its roofline;
+                RoPE on q and k, bf16 outputs), and one decode step against a
+                full 8192-token K/V cache (time, GB/s against HBM peak);
   cpu_baseline  the fp64 oracle timed on this host's cores on a bounded sample.
 """
 from __future__ import annotations
@@ -46,9 +60,6 @@ PEAK_HBM_GBS = 8000.0
 HEADLINE = "lm237m_ctx1024"
 SEEDS = {"tiny_f32": 1, "lm12m_ctx512": 2, "lm237m_ctx1024": 3, "long_ctx8192": 4, "packed_docs8192": 5,
          "lm237m_ctx1024_gqa4": 6, "lm237m_ctx1024_rope": 7, "lm237m_ctx1024_out16": 8}
-# algorithmic flops per allowed pair, per kernel (times D)
-KERNEL_FLOPS_PER_PAIR = {"fwd": 4, "dkdv": 8, "dq": 2}
-KERNEL_SOURCES = ["attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_bwd.hip"]
 
 
 def log(msg):
@@ -65,6 +76,10 @@ def parse():
     p.add_argument("--no-others", action="store_true", help="skip the other full-size workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time for the oracle sample")
+    p.add_argument("--cold-mib", type=int, default=512,
+                   help="MiB written before each step of the cold-cache loop (0: no cold loop)")
+    p.add_argument("--sclk-seconds", type=float, default=1.0,
+                   help="seconds of back-to-back steps while the graphics clock is sampled (0: none)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="also run a plain fp32 elementwise kernel (negation) over MIB MiB, a known number of "
                         "HBM bytes, to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -148,6 +163,10 @@ class Workload:
         self.ca.attn_bwd_dq(self.q, self.k, self.v, self.do, self.lse, self.delta, self.dq,
                             self.x["scale"], **self.sargs)
 
+    def dq_delta(self):
+        self.ca.attn_bwd_dq_delta(self.q, self.k, self.v, self.o, self.do, self.lse, self.dq, self.delta,
+                                  self.x["scale"], **self.sargs)
+
     def step(self):
         self.fwd()
         self.bwd()
@@ -164,39 +183,70 @@ class Workload:
         torch.cuda.synchronize()
         return g
 
-    def timed_steps(self, steps, warmup, graph=False):
-        """Seconds per step over `steps` steps after `warmup`: the entry points
-        called in turn, or (graph=True) one replay of the captured step."""
+    def timed_loop(self, steps, warmup, cold=None):
+        """`warmup` untimed steps, then exactly `steps` steps between two device
+        synchronisations.  Returns the host-clock seconds per step and, from HIP
+        events recorded on the launch stream around each step's forward and
+        backward, the per-iteration times (ms) of fwd, bwd and the whole step.
+        cold: a device buffer written (on the same stream, outside the events)
+        before every step, to evict the last-level cache."""
         import torch
-        if graph:
-            g = self.capture()
-
-            def run():
-                with torch.cuda.stream(self.stream):
-                    g.replay()
-        else:
-            run = self.step
         for _ in range(warmup):
-            run()
+            self.step()
         torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         t0 = time.perf_counter()
-        for _ in range(steps):
-            run()
+        for i in range(steps):
+            if cold is not None:
+                with torch.cuda.stream(self.stream):
+                    cold.fill_(float(i & 1))
+            ev[i][0].record(self.stream)
+            self.fwd()
+            ev[i][1].record(self.stream)
+            self.bwd()
+            ev[i][2].record(self.stream)
         torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / steps
+        per = {"fwd": [e[0].elapsed_time(e[1]) for e in ev], "bwd": [e[1].elapsed_time(e[2]) for e in ev],
+               "step": [e[0].elapsed_time(e[2]) for e in ev]}
+        return sec, per
+
+    def graph_seconds(self, steps, warmup):
+        """Host-clock seconds per step of the step captured once and replayed."""
+        import torch
+        g = self.capture()
+        with torch.cuda.stream(self.stream):
+            for _ in range(warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                g.replay()
+            torch.cuda.synchronize()
         return (time.perf_counter() - t0) / steps
 
-    def kernel_times(self, reps):
-        """Mean duration (ms) from HIP events recorded on the launch stream: the
-        forward, the whole backward call, and the three backward stages run one
-        by one through their own entry points (with bf16 inputs attn_bwd runs
-        dQ with Delta fused, then dK/dV; the staged dQ reads Delta instead)."""
-        import torch
-        stages = [("fwd", self.fwd), ("bwd", self.bwd)]
+    def stages(self):
+        """(name, call) of each kernel this workload's path runs, through the entry
+        point that runs it alone: the forward, the two stages of attn_bwd (16-bit
+        inputs: dQ with Delta fused, then dK/dV) and the standalone Delta
+        preprocess (fp32 inputs run it inside attn_bwd_dq_delta; 16-bit callers
+        of the staged API use it).  Workloads whose options have no staged entry
+        points (grouped heads, RoPE, 16-bit outputs) time the forward and the
+        whole backward only."""
+        out = [("fwd", self.fwd), ("bwd", self.bwd)]
         if self.cfg.rope:  # the rotation pass alone (it is part of the forward above)
-            stages.append(("rope", lambda: self.ca.attn_rope(self.q, self.k, self.q_rot, self.k_rot, self.tab,
-                                                             stream=self.stream)))
-        elif not self.grouped and not self.cfg.out16:  # the staged entry points: fp32 outputs, plain heads
-            stages += [("pre", self.pre), ("dkdv", self.dkdv), ("dq", self.dqk)]
+            out.append(("rope", lambda: self.ca.attn_rope(self.q, self.k, self.q_rot, self.k_rot, self.tab,
+                                                          stream=self.stream)))
+        elif not self.grouped and not self.cfg.out16:
+            out += [("dq_delta", self.dq_delta), ("dkdv", self.dkdv), ("pre", self.pre)]
+        return out
+
+    def kernel_times(self, reps):
+        """Per-kernel times (ms) from HIP events recorded on the launch stream,
+        one pair of events around each stage in each of `reps` repetitions:
+        median, p10, p90 and mean."""
+        import torch
+        stages = self.stages()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(reps)]
         for _ in range(3):
             self.step()
@@ -207,24 +257,39 @@ class Workload:
                 fn()
                 ev[r][i + 1].record(self.stream)
         torch.cuda.synchronize()
-        out = {}
-        for i, (name, _) in enumerate(stages):
-            ts = sorted(ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps))
-            out[name] = {"mean_ms": float(np.mean(ts)), "median_ms": float(np.median(ts))}
-        return out
+        return {name: stats([ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps)])
+                for i, (name, _) in enumerate(stages)}
 
-    def preprocess_bytes(self):
-        B, H, S, D = self.x["B"], self.x["H"], self.x["S"], self.x["D"]
-        in_bytes = 2 if self.cfg.dtype == "bf16" else 4
-        return B * H * S * (D * (in_bytes + 4) + 4)
+    def kernel_work(self):
+        """Counted flops and algorithmic HBM bytes of one launch of each kernel:
+        every input read once, every output written once (tile re-reads served by
+        the caches are not algorithmic).  fwd: q, k, v -> o, lse; dq_delta: q, k,
+        v, dO, o, lse -> dq, delta; dkdv: q, k, v, dO, lse, delta -> dk, dv; pre:
+        o, dO -> delta."""
+        nb = lambda t: t.numel() * t.element_size()  # noqa: E731
+        D = self.x["D"]
+        qkv = nb(self.q) + nb(self.k) + nb(self.v)
+        return {
+            "fwd": (4 * D * self.pairs, qkv + nb(self.o) + nb(self.lse)),
+            "dq_delta": (2 * D * self.pairs,
+                         qkv + nb(self.do) + nb(self.o) + nb(self.lse) + nb(self.delta) + nb(self.dq)),
+            "dkdv": (8 * D * self.pairs,
+                     qkv + nb(self.do) + nb(self.lse) + nb(self.delta) + nb(self.dk) + nb(self.dv)),
+            "pre": (0, nb(self.o) + nb(self.do) + nb(self.delta)),
+        }
+
+
+def stats(ts):
+    """median, p10, p90 and mean of a list of times (ms)."""
+    a = np.asarray(ts, dtype=np.float64)
+    return {"median_ms": float(np.median(a)), "p10_ms": float(np.percentile(a, 10)),
+            "p90_ms": float(np.percentile(a, 90)), "mean_ms": float(a.mean()), "n": int(a.size)}
 
 
 def sources_digest():
-    h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "causal_attention_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    """Digest of the library's sources and build flags (the library's build id)."""
+    from causal_attention_amd.build import source_digest
+    return source_digest()
 
 
 def measured_traffic(kernel, workload):
@@ -319,21 +384,107 @@ def write_traffic(fetch_dir, write_dir, workload, mib):
     return rec
 
 
-def roofline(w, times):
-    """The dominant kernel (most time per step) against its roofline."""
-    peak = PEAK_BF16_TFLOPS if w.cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
-    dom = max((k for k in times if k in KERNEL_FLOPS_PER_PAIR or k == "pre"), key=lambda k: times[k]["mean_ms"])
-    t = times[dom]["mean_ms"] * 1e-3
-    if dom == "pre":
-        achieved = w.preprocess_bytes() / t / 1e9
-        r = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+def kernel_roofline(flops, nbytes, ms, mfma_peak):
+    """One kernel against its binding roof: the matrix-core peak, or the HBM peak
+    times its arithmetic intensity (flops per algorithmic byte), whichever is
+    lower.  `achieved` and `peak` are in the binding roof's unit (TFLOP/s for
+    the matrix cores, GB/s for HBM), so frac is the same either way."""
+    t = ms * 1e-3
+    tflops = flops / t / 1e12
+    gbs = nbytes / t / 1e9
+    ai = flops / nbytes
+    hbm_bound = ai * PEAK_HBM_GBS * 1e9 < mfma_peak * 1e12
+    if hbm_bound:
+        r = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     else:
-        achieved = KERNEL_FLOPS_PER_PAIR[dom] * w.x["D"] * w.pairs / t / 1e12
-        r = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s"}
+        r = {"bound": "mfma", "achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s"}
     r["frac"] = r["achieved"] / r["peak"]
+    r.update({"ms": ms, "flops": flops, "bytes": nbytes, "flop_per_byte": ai, "tflops": tflops, "gbs": gbs,
+              "frac_of_mfma_peak": tflops / mfma_peak})
+    return r
+
+
+def rooflines(w, times):
+    """Every timed kernel of the path against its own binding roof (median times)."""
+    peak = PEAK_BF16_TFLOPS if w.cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    work = w.kernel_work()
+    return {k: kernel_roofline(*work[k], times[k]["median_ms"], peak) for k in work if k in times}
+
+
+def roofline(w, times, per_kernel):
+    """The top-level entry: the kernel of the path (fwd, dq_delta, dkdv) taking
+    the most time per step, with its rocprofv3-measured HBM bytes per launch
+    when those were taken on the current sources."""
+    on_path = [k for k in ("fwd", "dq_delta", "dkdv") if k in per_kernel]
+    if not on_path:
+        return None
+    dom = max(on_path, key=lambda k: times[k]["median_ms"])
+    r = {k: per_kernel[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
     r["traffic"] = measured_traffic(dom, w.name)
     r["kernel"] = dom
+    r["algorithmic_bytes"] = per_kernel[dom]["bytes"]
     return r
+
+
+def sample_sclk(run, seconds):
+    """Graphics clock (MHz) sampled about every 2 ms from the driver's GPU
+    metrics while `run` (one step) is called back to back for `seconds`:
+    mean, min and max of the samples (for every XCD where the metrics give one
+    clock per XCD).  None if the metrics are not readable here."""
+    import threading
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+        amdsmi.amdsmi_get_gpu_metrics_info(handle)
+    except Exception as e:  # no metrics on this host: report why
+        return {"error": f"{type(e).__name__}: {e}"[:200]}
+
+    def clocks(m):
+        out = []
+        for key in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
+            v = m.get(key)
+            vals = v if isinstance(v, list) else [v]
+            vals = [float(x) for x in vals if isinstance(x, (int, float)) and 0 < x < 10000]
+            if vals:
+                return key, vals
+        return None, out
+
+    samples, keys = [], set()
+    stop = threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                key, vals = clocks(amdsmi.amdsmi_get_gpu_metrics_info(handle))
+                if vals:
+                    keys.add(key)
+                    samples.append(float(np.mean(vals)))
+            except Exception:
+                pass
+            time.sleep(0.002)
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    n = 0
+    while time.perf_counter() < t_end:
+        run()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    if not samples:
+        return {"error": "no clock in the GPU metrics"}
+    return {"mean": float(np.mean(samples)), "min": float(np.min(samples)), "max": float(np.max(samples)),
+            "samples": len(samples), "steps": n, "field": sorted(keys)[0]}
 
 
 def cpu_baseline(w, seconds):
@@ -406,28 +557,49 @@ def measure_decode(name, reps):
                                                "D": cfg.D, "dtype": cfg.dtype}}
 
 
-def measure(name, steps, warmup, reps):
+def measure(name, steps, warmup, reps, cold_mib=0, sclk_seconds=0.0):
+    """One workload: the timed loop (host clock + per-iteration events), the
+    graph-replayed step, per-kernel event times and rooflines; optionally the
+    cold-cache loop and the clock samples."""
+    import torch
     w = Workload(name)
-    sec = w.timed_steps(steps, warmup)
-    sec_graph = w.timed_steps(steps, warmup, graph=True)
+    sec, per = w.timed_loop(steps, warmup)
+    sec_graph = w.graph_seconds(steps, warmup)
     total = w.flops_fwd + w.flops_bwd
-    tflops = total / sec / 1e12
-    times = w.kernel_times(reps)
     peak = PEAK_BF16_TFLOPS if w.cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
-    ms_fwd = times["fwd"]["mean_ms"]
-    ms_bwd = times["bwd"]["mean_ms"]
+    ev = {k: stats(v) for k, v in per.items()}
+    times = w.kernel_times(reps)
+    per_kernel = rooflines(w, times)
+    tflops = total / sec / 1e12
     summary = {
         "tflops": tflops, "pct_peak": 100.0 * tflops / peak, "ms_per_step": sec * 1e3,
         "ms_per_step_graph": sec_graph * 1e3,
-        "fwd_tflops": w.flops_fwd / (ms_fwd * 1e-3) / 1e12,
-        "bwd_tflops": w.flops_bwd / (ms_bwd * 1e-3) / 1e12,
-        "kernels_ms": {k: round(v["mean_ms"], 5) for k, v in times.items()},
+        "events_ms": ev,
+        "tflops_events_median": total / (ev["step"]["median_ms"] * 1e-3) / 1e12,
+        "fwd_tflops": w.flops_fwd / (ev["fwd"]["median_ms"] * 1e-3) / 1e12,
+        "bwd_tflops": w.flops_bwd / (ev["bwd"]["median_ms"] * 1e-3) / 1e12,
+        "kernels_ms": {k: round(v["median_ms"], 5) for k, v in times.items()},
         "pairs": w.pairs,
     }
+    if per_kernel:
+        summary["rooflines"] = {k: {f: v[f] for f in ("bound", "frac", "tflops", "gbs", "ms")}
+                                for k, v in per_kernel.items()}
+    if "pre" in per_kernel:
+        summary["preprocess_GBs"] = per_kernel["pre"]["gbs"]
+        summary["preprocess_frac_hbm_peak"] = per_kernel["pre"]["gbs"] / PEAK_HBM_GBS
     if "rope" in times:  # the rotation pass reads q, k and writes q_rot, k_rot once (the table stays in L2)
         nbytes = 2 * (w.q.numel() + w.k.numel()) * w.q.element_size()
-        summary["rope_GBs"] = nbytes / (times["rope"]["mean_ms"] * 1e-3) / 1e9
-    return w, sec, times, summary
+        summary["rope_GBs"] = nbytes / (times["rope"]["median_ms"] * 1e-3) / 1e9
+    if cold_mib:
+        buf = torch.empty(cold_mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+        _, cper = w.timed_loop(max(20, steps // 4), 3, cold=buf)
+        cev = {k: stats(v) for k, v in cper.items()}
+        summary["cold"] = {"evict_mib": cold_mib, "events_ms": cev,
+                           "tflops_events_median": total / (cev["step"]["median_ms"] * 1e-3) / 1e12}
+        del buf
+    if sclk_seconds:
+        summary["sclk_mhz"] = sample_sclk(w.step, sclk_seconds)
+    return w, sec, times, per_kernel, summary
 
 
 def main():
@@ -446,19 +618,21 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     import causal_attention_amd as ca
-    ca.load_library()
+    ca.load_library()  # refuses a library built from other sources than this tree's
 
-    log(f"[bench] workload {a.workload}: warmup {a.warmup}, steps {a.steps}")
-    w, sec, times, summary = measure(a.workload, a.steps, a.warmup, a.kernel_reps)
+    log(f"[bench] library build {ca.build_id()}; workload {a.workload}: warmup {a.warmup}, steps {a.steps}")
+    w, sec, times, per_kernel, summary = measure(a.workload, a.steps, a.warmup, a.kernel_reps,
+                                                 cold_mib=a.cold_mib, sclk_seconds=a.sclk_seconds)
     log(f"[bench] {a.workload}: {summary['tflops']:.1f} TFLOPS ({summary['pct_peak']:.1f}% of peak), "
-        f"{sec * 1e3:.4f} ms/step, kernels {summary['kernels_ms']}")
+        f"{sec * 1e3:.4f} ms/step, step events median {summary['events_ms']['step']['median_ms']:.4f} ms, "
+        f"kernels {summary['kernels_ms']}")
     by_workload = {a.workload: summary}
     if not a.no_others:
         for name in ("lm12m_ctx512", "long_ctx8192", "packed_docs8192", "lm237m_ctx1024_gqa4",
                      "lm237m_ctx1024_rope", "lm237m_ctx1024_out16", "lm237m_ctx1024"):
             if name == a.workload:
                 continue
-            _, _, _, s = measure(name, max(10, a.steps // 4), max(3, a.warmup // 2), max(10, a.kernel_reps // 2))
+            _, _, _, _, s = measure(name, max(50, a.steps // 2), max(10, a.warmup), max(20, a.kernel_reps // 2))
             by_workload[name] = s
             log(f"[bench] {name}: {s['tflops']:.1f} TFLOPS ({s['pct_peak']:.1f}% of peak), "
                 f"kernels {s['kernels_ms']}")
@@ -466,7 +640,7 @@ def main():
         by_workload["decode_ctx8192"] = d
         log(f"[bench] decode_ctx8192: {d['us_per_step']:.1f} us/step, {d['achieved_GBs']:.0f} GB/s "
             f"({100 * d['frac_hbm_peak']:.1f}% of HBM peak)")
-    rl = roofline(w, times)
+    rl = roofline(w, times, per_kernel)
     log(f"[bench] roofline: {rl}")
     cpu = None
     if not a.no_cpu_baseline:
@@ -491,10 +665,17 @@ def main():
                    "mask": "packed_documents" if cfg.mask_mode else "causal",
                    "outputs": cfg.dtype if cfg.out16 else "fp32", "parallelism": "single GPU"},
         "pct_peak": summary["pct_peak"],
+        "build_id": ca.build_id(),
+        "events_ms": summary["events_ms"],
+        "tflops_events_median": summary["tflops_events_median"],
         "ms_per_step_graph": summary["ms_per_step_graph"],
         "fwd_tflops": summary["fwd_tflops"],
         "bwd_tflops": summary["bwd_tflops"],
-        "kernels": {k: v["mean_ms"] for k, v in times.items()},
+        "cold": summary.get("cold"),
+        "sclk_mhz": summary.get("sclk_mhz"),
+        "preprocess_GBs": summary.get("preprocess_GBs"),
+        "kernels": times,
+        "rooflines": per_kernel,
         "roofline": rl,
         "cpu_baseline": cpu,
         "by_workload": by_workload,

@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     attn_bwd_dkdv,
     attn_bwd_ex,
     attn_bwd_dq,
+    attn_bwd_dq_delta,
     attn_bwd_preprocess,
     attn_bwd_rope,
     attn_decode,
@@ -27,6 +28,7 @@ from ._binding import (  # noqa: F401
     attn_rope,
     attn_rope_table,
     backward,
+    build_id,
     decode,
     decode_workspace_bytes,
     forward,

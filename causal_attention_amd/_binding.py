@@ -60,6 +60,7 @@ SIGNATURES = {
     "attn_bwd_preprocess": [_P, _P, _P, _I, _I, _I, _I, _I, _P],
     "attn_bwd_dkdv": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
     "attn_bwd_dq": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
+    "attn_bwd_dq_delta": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
     "attn_fwd_gqa": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
     "attn_bwd_gqa": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
     "attn_decode_workspace_bytes": [_I, _I, _I, _I, _I],
@@ -73,6 +74,7 @@ SIGNATURES = {
     "attn_bwd_ex": [ctypes.POINTER(AttnParams), _P],
     "attn_status_string": [_I],
     "attn_abi_version": [],
+    "attn_build_id": [],
 }
 
 _lib = None
@@ -100,8 +102,11 @@ def _init_device_runtime():
         torch.cuda.init()
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load the HIP library (once).  Raises if it has not been built."""
+def load_library(path: str = LIB_PATH, check_build: bool = True) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built, or if it
+    was built from other sources than the tree it sits in (its attn_build_id
+    differs from the digest of csrc/, the header and the build flags): a stale
+    library is never run in place of the current kernels."""
     global _lib
     if _lib is not None:
         return _lib
@@ -114,10 +119,22 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name, args in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.argtypes = args
-        fn.restype = {"attn_status_string": ctypes.c_char_p,
+        fn.restype = {"attn_status_string": ctypes.c_char_p, "attn_build_id": ctypes.c_char_p,
                       "attn_decode_workspace_bytes": ctypes.c_size_t}.get(name, ctypes.c_int)
+    if check_build:
+        from .build import source_digest
+        built, want = lib.attn_build_id().decode(), source_digest()
+        if built != want:
+            raise RuntimeError(
+                f"{path} was built from other sources (build id {built}, sources {want}): "
+                "rebuild it (python -m causal_attention_amd.build or __graft_entry__.build())")
     _lib = lib
     return lib
+
+
+def build_id() -> str:
+    """The source digest the loaded library was built from."""
+    return load_library().attn_build_id().decode()
 
 
 def status_string(status: int) -> str:
@@ -280,6 +297,24 @@ def attn_bwd_dq(q, k, v, dO, lse, delta, dq, scale, mask_mode=ATTN_MASK_CAUSAL, 
         _ptr(q, "q", device=dev), _ptr(k, "k", device=dev), _ptr(v, "v", device=dev),
         _ptr(dO, "dO", (B, H, S, D), q.dtype, dev), _ptr(lse, "lse", (B, H, S), f32, dev),
         _ptr(delta, "delta", (B, H, S), f32, dev), _ptr(dq, "dq", (B, H, S, D), f32, dev),
+        B, H, S, D, float(scale), int(mask_mode), cu, ns, ms, dt, _stream(stream)))
+
+
+def attn_bwd_dq_delta(q, k, v, o, dO, lse, dq, delta, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None,
+                      n_seqs=None, max_seqlen=None, stream=None):
+    """Enqueue the backward's first stage: delta [B,H,S] and dq [B,H,S,D] fp32 from o
+    (attn_bwd runs this, then attn_bwd_dkdv)."""
+    torch = _torch()
+    lib = load_library()
+    B, H, _, S, D, dt = _qkv_info(q, k, v, grouped=False)
+    dev = q.device
+    cu, ns, ms = _mask_args(mask_mode, cu_seqlens, n_seqs, max_seqlen, dev)
+    f32 = torch.float32
+    _check(lib.attn_bwd_dq_delta(
+        _ptr(q, "q", device=dev), _ptr(k, "k", device=dev), _ptr(v, "v", device=dev),
+        _ptr(o, "o", (B, H, S, D), f32, dev), _ptr(dO, "dO", (B, H, S, D), q.dtype, dev),
+        _ptr(lse, "lse", (B, H, S), f32, dev), _ptr(dq, "dq", (B, H, S, D), f32, dev),
+        _ptr(delta, "delta", (B, H, S), f32, dev),
         B, H, S, D, float(scale), int(mask_mode), cu, ns, ms, dt, _stream(stream)))
 
 

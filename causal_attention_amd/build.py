@@ -7,6 +7,7 @@ tree; nothing is installed anywhere else.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -36,6 +37,23 @@ HIPCC_FLAGS = [
 ]
 
 
+def source_digest() -> str:
+    """Digest of everything the library is built from: every file under csrc/,
+    the public header and the compiler flags.  The build embeds it in the
+    library (attn_build_id), and the binding refuses a library whose digest
+    differs from the tree's, so a stale build never runs in its place."""
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+    for name in files:
+        h.update(name.encode() + b"\0")
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    with open(os.path.join(INCLUDE, "attn_api.h"), "rb") as f:
+        h.update(f.read())
+    h.update(" ".join(HIPCC_FLAGS).encode())
+    return h.hexdigest()[:16]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -59,7 +77,8 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     """Compile each source to an object (in parallel), then link the library."""
     from concurrent.futures import ThreadPoolExecutor
     import tempfile
-    flags = [*HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", f"-I{CSRC}"]
+    flags = [*HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", f"-I{CSRC}",
+             f'-DATTN_SOURCE_DIGEST="{source_digest()}"']
     compile_flags = [f for f in flags if f != "-shared"]
     tmp = LIB_PATH + ".tmp"
     with tempfile.TemporaryDirectory(prefix="attn_build_") as objdir:

@@ -11,7 +11,12 @@
 
 namespace {
 
-constexpr int kAbiVersion = 160;  // 1.60: grouped-query, decode, RoPE, fp16 inputs, attn_params calls (16-bit outputs, strides)
+constexpr int kAbiVersion = 170;  // 1.70: grouped-query, decode, RoPE, fp16 inputs, attn_params calls (16-bit outputs,
+                                  // strides), the fused dQ + Delta stage, the build identifier
+
+#ifndef ATTN_SOURCE_DIGEST
+#error "build with -DATTN_SOURCE_DIGEST=... (causal_attention_amd/build.py computes it from the sources)"
+#endif
 
 int check_common(int B, int H, int S, int D, int dtype) {
   if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_DTYPE;
@@ -152,6 +157,16 @@ int fwd_all(const void *q, const void *k, const void *v, void *o, float *lse, bo
   return to_status(attn::launch_fwd(a));
 }
 
+// Delta and dQ.  16-bit inputs: the dQ kernel computes Delta on the way
+// (bitwise equal to the preprocess kernel's) and writes it for dK/dV, one pass
+// over O and dO fewer; fp32 inputs: the preprocess kernel, then dQ.
+hipError_t dq_delta_stage(const attn::Args &a) {
+  if (a.half()) return attn::launch_bwd_dq_delta(a);
+  hipError_t e = attn::launch_bwd_preprocess(a);
+  if (e == hipSuccess) e = attn::launch_bwd_dq(a);
+  return e;
+}
+
 // Whole backward (optionally with RoPE gradients turned back in the dQ and dK
 // epilogues): argument checks, then the kernels on one stream.
 int bwd_all(const void *q, const void *k, const void *v, const void *o, const void *dO, const float *lse,
@@ -189,17 +204,8 @@ int bwd_all(const void *q, const void *k, const void *v, const void *o, const vo
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  hipError_t e;
-  if (a.half()) {
-    // 16-bit inputs: dQ computes Delta on the way (bitwise equal to the
-    // preprocess kernel's) and writes it for dK/dV: one pass over O and dO fewer.
-    e = attn::launch_bwd_dq_delta(a);
-    if (e == hipSuccess) e = attn::launch_bwd_dkdv(a);
-  } else {
-    e = attn::launch_bwd_preprocess(a);
-    if (e == hipSuccess) e = attn::launch_bwd_dkdv(a);
-    if (e == hipSuccess) e = attn::launch_bwd_dq(a);
-  }
+  hipError_t e = dq_delta_stage(a);
+  if (e == hipSuccess) e = attn::launch_bwd_dkdv(a);
   return to_status(e);
 }
 
@@ -208,6 +214,8 @@ int bwd_all(const void *q, const void *k, const void *v, const void *o, const vo
 extern "C" {
 
 int attn_abi_version(void) { return kAbiVersion; }
+
+const char *attn_build_id(void) { return ATTN_SOURCE_DIGEST; }
 
 const char *attn_status_string(int status) {
   switch (status) {
@@ -292,6 +300,28 @@ int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dO, con
   a.delta_in = delta;
   a.dq = dq;
   return to_status(attn::launch_bwd_dq(a));
+}
+
+int attn_bwd_dq_delta(const void *q, const void *k, const void *v, const float *o, const void *dO,
+                      const float *lse, float *dq, float *delta, int B, int H, int S, int D, float scale,
+                      int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype,
+                      void *stream) {
+  int st = check_common(B, H, S, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !delta) return ATTN_ERR_NULL;
+  if ((st = check_mask(B, H, S, mask_mode, cu_seqlens, n_seqs, max_seqlen)) != ATTN_OK) return st;
+  if ((st = check_scale(scale)) != ATTN_OK) return st;
+  attn::Args a = make_args(B, H, S, D, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen, dtype, stream);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dO = dO;
+  a.o_in = o;
+  a.lse_in = lse;
+  a.delta = delta;
+  a.delta_in = delta;
+  a.dq = dq;
+  return to_status(dq_delta_stage(a));
 }
 
 int attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o, const void *dO, const float *lse,

@@ -877,28 +877,18 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
 // allocation must allow.  Two 64-row slots of Q and dO (or K and V) at D = 128, or in
 // fp32, would leave room for one workgroup per CU: those take 32 rows.
 template <typename T, int D> struct BwdCfg {
-#ifdef ATTN_BWD_BMQ
-  static constexpr int BMQ = (D == 128 || sizeof(T) == 4) ? 32 : D == 32 ? 64 : ATTN_BWD_BMQ;
-  static constexpr int BN = (D == 128 && sizeof(T) == 4) ? 32 : D == 32 ? 64 : ATTN_BWD_BN;
-  static constexpr int MINB_DKDV = ATTN_BWD_MINB_DKDV;
-  static constexpr int MINB_DQ = ATTN_BWD_MINB_DQ;
-#else
   static constexpr int BMQ = (D == 128 || sizeof(T) == 4) ? 32 : 64;
   static constexpr int BN = (D == 128 && sizeof(T) == 4) ? 32 : 64;
   static constexpr int MINB_DKDV = 1;
   static constexpr int MINB_DQ = 1;
-#endif
   // dQ key tile: 32 keys leave the bf16 kernel enough registers for more
   // waves per SIMD (D = 64: 126 VGPRs, four; D = 128: two instead of one),
   // measured 9 % (context 1024) and 26 % (S = 8192, D = 128) faster; packed
-  // documents at D <= 64 ran 12 % faster with 64.
+  // documents at D <= 64 ran 12 % faster with 64, and a 32-row tile at D = 32
+  // is too small to split over four waves.
   template <bool DOC>
   static constexpr int dq_bn() {
-#ifdef ATTN_BWD_BMQ
-    return BN;
-#else
-    return (sizeof(T) == 2 && D > 32 && !(DOC && D <= 64)) ? 32 : BN;  // a 32-row D=32 tile is too small to split over 4 waves
-#endif
+    return (sizeof(T) == 2 && D > 32 && !(DOC && D <= 64)) ? 32 : BN;
   }
 };
 

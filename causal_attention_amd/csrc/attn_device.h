@@ -93,13 +93,42 @@ template <typename T, typename V> struct Elem16 {
     for (int s = 0; s < 8; ++s) f[s] = (T)acc[8 * j + s];
     return f;
   }
-  // pack() and add the eight fp32 values to `sum` (round-to-nearest-even is
-  // unbiased, so normalising the rounded weights by the fp32 sum adds only
-  // random error far below the rounding of the weights themselves).
+  // pack() and add the eight fp32 values to `sum` (for weights whose largest
+  // value is 1, as with an exact per-tile maximum, normalising the rounded
+  // weights by the fp32 sum adds only random error below the rounding of the
+  // weights themselves).
   __device__ __forceinline__ static frag pack_sum(const f32x16 &acc, int j, float &sum) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) sum += acc[8 * j + s];
     return pack(acc, j);
+  }
+  // pack(), add the eight fp32 values to `sum` and the eight ROUNDED values
+  // to `rsum` (one two-element dot product with ones per pair: exact products,
+  // fp32 sums).  Weights shifted by something other than the row maximum can
+  // have their largest value anywhere; dividing the product with the rounded
+  // weights by their own sum cancels the rounding of a dominant weight
+  // (a one-key row gives exactly that key's value), which dividing by the
+  // unrounded sum does not.
+  __device__ __forceinline__ static frag pack_sums(const f32x16 &acc, int j, float &sum, float &rsum) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) sum += acc[8 * j + s];
+    const frag f = pack(acc, j);
+    const u32x4 w = __builtin_bit_cast(u32x4, f);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) rsum = dot2_ones(w[s], rsum);
+    return f;
+  }
+  // x.lo + x.hi + acc for a pair of 16-bit values packed in one word.
+  __device__ __forceinline__ static float dot2_ones(uint32_t x, float acc) {
+    if constexpr (__is_same(T, bf16)) {
+      typedef bf16 v2 __attribute__((ext_vector_type(2)));
+      const v2 one = {(bf16)1.f, (bf16)1.f};
+      return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2, x), one, acc, false);
+    } else {
+      typedef f16 v2 __attribute__((ext_vector_type(2)));
+      const v2 one = {(f16)1.f, (f16)1.f};
+      return __builtin_amdgcn_fdot2(__builtin_bit_cast(v2, x), one, acc, false);
+    }
   }
   // Operands of a rank-1 product mma_rows(acc, rows_a(x, hh), rows_b(hh)) that
   // adds x_c to every element of row c of a 32x32 result, x_c being the value
@@ -156,6 +185,10 @@ template <> struct Elem<float> {
       sum += f[s];
     }
     return f;
+  }
+  // fp32 weights are not rounded: the rounded sum is the sum (callers use `sum`).
+  __device__ __forceinline__ static frag pack_sums(const f32x16 &acc, int j, float &sum, float &) {
+    return pack_sum(acc, j, sum);
   }
   using rows_frag = frag;
   __device__ __forceinline__ static void mma_rows(f32x16 &acc, const frag &a, const frag &b) { mma(acc, a, b); }

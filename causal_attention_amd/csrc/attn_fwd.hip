@@ -8,16 +8,16 @@
 // and LSE = m + ln l.  Scores never leave registers.
 //
 // gfx950 mapping.
-//  * Each wave computes S^T = K Q^T for its 32*QB queries, so a lane owns one
+//  * Each wave computes S^T = K Q^T for its 32 queries, so a lane owns one
 //    query and holds that query's scores in its own registers; P^T is then
 //    already the B operand of O^T += V^T P^T ("accum" slot order,
 //    attn_device.h).  K is read from LDS as (swizzled) row fragments; V is
-//    stored row-major and read through the transposing LDS load.
-//  * Software pipeline per wave: while the softmax of tile j runs on the
-//    vector ALUs, the matrix cores compute the scores of tile j+1 and the
-//    P V product of tile j-1.
-//  * K and V tiles arrive by direct global->LDS copies into 3-slot rings,
-//    requested two iterations before use, with one barrier per tile.
+//    read through the transposing LDS load from a swizzled row-major tile.
+//  * No software pipeline inside a wave: at D = 64 the kernel needs about
+//    120 VGPRs, so four workgroups share a CU and the hardware overlaps one
+//    wave's exponentials with another wave's matrix-core work.
+//  * K and V tiles arrive by direct global->LDS copies into two-slot rings,
+//    requested one iteration before use, with one barrier per tile.
 //  * No per-tile maximum: p = exp2(s * c2 - m) uses the reference maximum m
 //    of earlier tiles (c2 = scale * log2 e).  The first tile, and any tile
 //    whose exponentials could overflow (a row sum above 2^64 or not finite,
@@ -26,7 +26,9 @@
 //    recomputed from its key tile, still in LDS, so the exponentials can
 //    overwrite the scores in place).
 //  * P is rounded to the input type (round to nearest even) for the P V
-//    product; the row sum adds the fp32 values.
+//    product.  O is divided by the sum of the rounded weights (a one-key row
+//    then gives that key's value exactly, whatever the shift), LSE takes the
+//    sum of the fp32 weights.
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -100,7 +102,9 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
 
   f32x16 oacc[DB];
   float m = -INFINITY;  // reference max (scaled, base 2)
-  float l = 0.f;        // this lane-half's partial row sum
+  float l = 0.f;        // this lane-half's partial row sum (for LSE)
+  float lr = 0.f;       // ... of the rounded weights (16-bit inputs; divides O)
+  constexpr bool kRounded = sizeof(T) == 2;
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
 
@@ -147,19 +151,20 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
 
   // Exponentials against the reference max, in place, then rounded and
   // summed.  True when every row of the wave stayed in range.
-  auto softmax_fast = [&](f32x16 (&sacc)[NB], frag (&pf)[PB], float &psum) {
+  auto softmax_fast = [&](f32x16 (&sacc)[NB], frag (&pf)[PB], float &psum, float &rsum) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[nb][r] = fast_exp2(__builtin_fmaf(sacc[nb][r], c2, -m));
     psum = 0.f;
+    rsum = 0.f;
 #pragma unroll
-    for (int j = 0; j < PB; ++j) pf[j] = E::pack_sum(sacc[j / 2], j % 2, psum);
+    for (int j = 0; j < PB; ++j) pf[j] = E::pack_sums(sacc[j / 2], j % 2, psum, rsum);
     return __builtin_amdgcn_ballot_w64(!(psum <= kRescaleLimit)) == 0;
   };
 
   // Exact path: true row maximum, rescale of the running output and sum.
-  auto softmax_exact = [&](f32x16 (&sacc)[NB], frag (&pf)[PB], float &psum) {
+  auto softmax_exact = [&](f32x16 (&sacc)[NB], frag (&pf)[PB], float &psum, float &rsum) {
     float mx = -INFINITY;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -170,6 +175,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
     const float alpha = fast_exp2(m - mnew);
     m = mnew;
     l *= alpha;
+    lr *= alpha;
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
 #pragma unroll
@@ -177,8 +183,9 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[nb][r] = fast_exp2(__builtin_fmaf(sacc[nb][r], c2, -mnew));
     psum = 0.f;
+    rsum = 0.f;
 #pragma unroll
-    for (int j = 0; j < PB; ++j) pf[j] = E::pack_sum(sacc[j / 2], j % 2, psum);
+    for (int j = 0; j < PB; ++j) pf[j] = E::pack_sums(sacc[j / 2], j % 2, psum, rsum);
   };
 
   // One key tile in ring slot P: wait for its copies (issued one iteration
@@ -196,21 +203,22 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
     const lds_t<T> *ks = kslot.template operator()<P>();
     f32x16 sacc[NB];
     frag pf[PB];
-    float psum;
+    float psum, rsum;
     mma_priority_hi();
     scores(ks, sacc);
     mma_priority_lo();
     if (masked) apply_mask(sacc, k0);
     if (m == -INFINITY) {
-      softmax_exact(sacc, pf, psum);
-    } else if (!softmax_fast(sacc, pf, psum)) {
+      softmax_exact(sacc, pf, psum, rsum);
+    } else if (!softmax_fast(sacc, pf, psum, rsum)) {
       // a row sum left the safe range: recompute the scores from the key
       // tile (still in its slot) and take the exact path
       scores(ks, sacc);
       if (masked) apply_mask(sacc, k0);
-      softmax_exact(sacc, pf, psum);
+      softmax_exact(sacc, pf, psum, rsum);
     }
     l += psum;
+    if constexpr (kRounded) lr += rsum;
     mma_priority_hi();
     pv(vslot.template operator()<P>(), pf);
     mma_priority_lo();
@@ -225,7 +233,8 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
   const GBuf go(o + panel_off(lo, bi, hq), panel_bytes(lo, t.r_end, D, sizeof(OT)));
   const int qi = w0 + c;
   const float lt = l + swap_halves(l);
-  const float inv = 1.0f / lt;
+  const float lrt = kRounded ? lr + swap_halves(lr) : lt;
+  const float inv = 1.0f / lrt;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -243,15 +252,9 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
 // per tile (BN) and the minimum number of workgroups per CU the register
 // allocation must allow (MINB).
 template <typename T, int D> struct FwdCfg {
-#ifdef ATTN_FWD_BN
-  static constexpr int NW = ATTN_FWD_NW;
-  static constexpr int BN = (sizeof(T) == 4 && D == 128) ? 32 : D == 32 ? 64 : ATTN_FWD_BN;
-  static constexpr int MINB = ATTN_FWD_MINB;
-#else
   static constexpr int NW = 4;
   static constexpr int BN = (sizeof(T) == 4 && D == 128) ? 32 : 64;
   static constexpr int MINB = 1;
-#endif
 };
 
 template <typename T, typename OT, int D, bool DOC>

@@ -103,9 +103,8 @@ int attn_fwd(const void *q, const void *k, const void *v, float *o, float *lse,
  * Backward.  Reads q, k, v, dO (dtype), o and lse (float32, from attn_fwd
  * with the same arguments) and writes dq, dk, dv [B,H,S,D] float32.
  * delta: caller-owned float32 workspace of B*H*S elements; on return it holds
- * Delta_i = sum_d dO_id O_id.  The results are bit for bit those of the three
- * stages below run in order; with bf16 inputs the dQ stage computes Delta
- * itself and runs first, then dK/dV (one pass over O and dO fewer).
+ * Delta_i = sum_d dO_id O_id.  The call is exactly attn_bwd_dq_delta, then
+ * attn_bwd_dkdv, below (bit for bit).
  */
 int attn_bwd(const void *q, const void *k, const void *v, const float *o,
              const void *dO, const float *lse, float *dq, float *dk, float *dv,
@@ -115,15 +114,21 @@ int attn_bwd(const void *q, const void *k, const void *v, const float *o,
 
 /*
  * The backward's stages, exported separately so that callers (and timing
- * harnesses) can schedule or measure them one by one.  attn_bwd is exactly
- * attn_bwd_preprocess, then attn_bwd_dkdv, then attn_bwd_dq; the last two
- * both need only the first and may run in either order.
+ * harnesses) can schedule or measure them one by one.
  *
  * attn_bwd_preprocess: delta[B*H*S] = rowsum(dO o O).  S, D, dtype as above.
  * attn_bwd_dkdv: dk, dv from q, k, v, dO, lse, delta (loops over query tiles
  *   for each key tile).
  * attn_bwd_dq: dq from q, k, v, dO, lse, delta (loops over key tiles for
  *   each query tile).
+ * attn_bwd_dq_delta: delta and dq in one call, from o instead of delta.
+ *   16-bit inputs: one kernel, the dQ kernel computing each row's Delta from
+ *   O and dO on the way (one pass over O and dO fewer); fp32 inputs:
+ *   attn_bwd_preprocess then attn_bwd_dq.  Either way delta and dq are bit
+ *   for bit those of attn_bwd_preprocess followed by attn_bwd_dq.
+ *
+ * attn_bwd is attn_bwd_dq_delta, then attn_bwd_dkdv; dK/dV needs only the
+ * Delta that the first stage writes.
  */
 int attn_bwd_preprocess(const float *o, const void *dO, float *delta,
                         int B, int H, int S, int D, int dtype, void *stream);
@@ -139,6 +144,12 @@ int attn_bwd_dq(const void *q, const void *k, const void *v, const void *dO,
                 int B, int H, int S, int D, float scale, int mask_mode,
                 const int32_t *cu_seqlens, int n_seqs, int max_seqlen,
                 int dtype, void *stream);
+
+int attn_bwd_dq_delta(const void *q, const void *k, const void *v, const float *o,
+                      const void *dO, const float *lse, float *dq, float *delta,
+                      int B, int H, int S, int D, float scale, int mask_mode,
+                      const int32_t *cu_seqlens, int n_seqs, int max_seqlen,
+                      int dtype, void *stream);
 
 /*
  * Grouped-query attention (Forge, "Architecture": attention with GQA behind
@@ -329,6 +340,14 @@ const char *attn_status_string(int status);
 
 /* Library ABI version (major * 100 + minor). */
 int attn_abi_version(void);
+
+/*
+ * Static, NUL-terminated identifier of the sources this library was built
+ * from: a digest of the kernel sources, this header and the compiler flags,
+ * fixed at build time.  A caller that holds the sources can recompute it and
+ * refuse a library built from other sources.
+ */
+const char *attn_build_id(void);
 
 #ifdef __cplusplus
 }

@@ -75,6 +75,24 @@ def errors(got, ref):
     return max_abs, rel_fro
 
 
+def check_delta(out, x):
+    """Delta against fp64 rowsum(dO o O) of the O the GPU stored: both kernels
+    that compute it add D products of an input-dtype dO and an fp32 O in fp32,
+    so each row's error is at most D * 2^-24 * sum_d |dO_d O_d| (a chain of D
+    rounded fused multiply-adds, or a tree of them: the same bound)."""
+    o = out["o"].detach().float().cpu().numpy().astype(np.float64)
+    do = np.asarray(x["do"], dtype=np.float64)
+    if o.shape != do.shape:
+        raise ValueError("Delta check needs O and dO of the same shape")
+    got = out["delta"].detach().cpu().numpy().astype(np.float64)
+    exact = np.sum(do * o, axis=-1)
+    D = o.shape[-1]
+    bound = D * 2.0 ** -24 * np.sum(np.abs(do * o), axis=-1) + 1e-30
+    worst = float(np.max(np.abs(got - exact) / bound))
+    assert worst <= 1.0, f"Delta off rowsum(dO o O_stored) by {worst:.2f}x its fp32 bound"
+    return worst
+
+
 # significant bits of the 16-bit output formats
 _OUT_BITS = {"bf16": 8, "f16": 11}
 

@@ -31,7 +31,29 @@ def test_header_status_codes_match_binding():
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 160
+    assert lib.attn_abi_version() == 170
+
+
+def test_build_id_is_the_source_digest(lib):
+    """The library carries the digest of the sources it was built from, and it
+    is the digest of the tree it sits in (load_library refuses it otherwise)."""
+    from causal_attention_amd.build import source_digest
+    built = lib.attn_build_id().decode()
+    assert re.fullmatch(r"[0-9a-f]{16}", built)
+    assert built == source_digest() == ca.build_id()
+
+
+def test_stale_library_is_refused(lib, monkeypatch):
+    """A library whose build id differs from the tree's sources does not load."""
+    from causal_attention_amd import build as _build
+    monkeypatch.setattr(_build, "source_digest", lambda: "0123456789abcdef")
+    saved = _binding._lib
+    _binding._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="built from other sources"):
+            _binding.load_library()
+    finally:
+        _binding._lib = saved
 
 
 def test_status_strings(lib):
@@ -99,6 +121,13 @@ def test_stage_entry_points_reject_invalid_arguments(lib):
                            None, 0, 0, 7, None) == -4
     assert lib.attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, -1.0, 0,
                            None, 0, 0, 1, None) == -9
+    dqd = lib.attn_bwd_dq_delta
+    assert dqd(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 0.1, 0, None, 0, 0, 1, None) == -1
+    assert dqd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 64, 0.1, 0, None, 0, 0, 1, None) == -1
+    assert dqd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 48, 0.1, 0, None, 0, 0, 1, None) == -3
+    assert dqd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 0.1, 4, None, 0, 0, 1, None) == -5
+    assert dqd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1, 64, 64, 0.1, 1, FAKE, 1, 64, 1, None) == -6
+    assert dqd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 0.0, 0, None, 0, 0, 1, None) == -9
 
 
 def _fwd_gqa(lib, H_kv, **kw):
@@ -301,6 +330,8 @@ def test_no_device_reports_hip_error(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert _fwd(lib) == -7
+    assert lib.attn_bwd_dq_delta(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 0.1, 0, None, 0, 0,
+                                 1, None) == -7
     assert _decode(lib) == -7
     assert _fwd_gqa(lib, 2) == -7
     assert _bwd_gqa(lib, 1) == -7

@@ -59,3 +59,32 @@ def test_runs_on_caller_stream():
     for n in ("o", "lse", "dq", "dk", "dv"):
         assert bool((out[n] == ref[n]).all()), n
     assert np.isfinite(out["o"].cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("cfg,shape", [("lm12m_ctx512", (2, 3, 333, 64)), ("tiny_f32", (1, 2, 130, 32)),
+                                       ("packed_docs8192", None)])
+def test_dq_delta_stage_is_the_fused_path(cfg, shape):
+    """attn_bwd is attn_bwd_dq_delta then attn_bwd_dkdv, bit for bit, and
+    attn_bwd_dq_delta equals attn_bwd_preprocess then attn_bwd_dq."""
+    import torch
+    import causal_attention_amd as ca
+    log(f"[determinism] dq_delta stage {cfg} {shape}")
+    x = make_inputs(CONFIGS[cfg], 84, shape=shape)
+    dev = to_device(x)
+    ref = run_hip(x, dev=dev)
+    kw = dict(mask_mode=x["mask_mode"], cu_seqlens=dev["cu"], max_seqlen=dev["max_seqlen"])
+    s = x["scale"]
+    delta = torch.full_like(ref["delta"], float("nan"))
+    dq = torch.full_like(ref["dq"], float("nan"))
+    dk = torch.full_like(ref["dk"], float("nan"))
+    dv = torch.full_like(ref["dv"], float("nan"))
+    ca.attn_bwd_dq_delta(dev["q"], dev["k"], dev["v"], ref["o"], dev["do"], ref["lse"], dq, delta, s, **kw)
+    ca.attn_bwd_dkdv(dev["q"], dev["k"], dev["v"], dev["do"], ref["lse"], delta, dk, dv, s, **kw)
+    delta2 = torch.full_like(delta, float("nan"))
+    dq2 = torch.full_like(dq, float("nan"))
+    ca.attn_bwd_preprocess(ref["o"], dev["do"], delta2)
+    ca.attn_bwd_dq(dev["q"], dev["k"], dev["v"], dev["do"], ref["lse"], delta2, dq2, s, **kw)
+    torch.cuda.synchronize()
+    for n, t in (("delta", delta), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool((t == ref[n]).all()), n
+    assert bool((delta2 == delta).all()) and bool((dq2 == dq).all())
