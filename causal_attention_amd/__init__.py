@@ -6,6 +6,7 @@ include/attn_api.h (libcausal_attn.so, built in-tree by
 binding: the same entry points, taking torch device tensors.
 """
 from ._binding import (  # noqa: F401
+    ATTN_DECODE_SCRATCH_BYTES,
     ATTN_DTYPE_BF16,
     ATTN_DTYPE_F16,
     ATTN_DTYPE_F32,
@@ -22,6 +23,7 @@ from ._binding import (  # noqa: F401
     attn_bwd_preprocess,
     attn_bwd_rope,
     attn_decode,
+    attn_decode_noalloc,
     attn_fwd,
     attn_fwd_ex,
     attn_fwd_rope,

@@ -22,12 +22,13 @@ ATTN_MASK_DOC_CAUSAL = 1
 ATTN_DTYPE_F32 = 0
 ATTN_DTYPE_BF16 = 1
 ATTN_DTYPE_F16 = 2
+ATTN_DECODE_SCRATCH_BYTES = 16 << 20  # include/attn_api.h: the static scratch of attn_decode_noalloc
 
 STATUS_NAMES = {
     0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEAD_DIM",
     -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_MASK", -6: "ATTN_ERR_SEQLENS", -7: "ATTN_ERR_HIP",
     -8: "ATTN_ERR_UNIMPLEMENTED", -9: "ATTN_ERR_SCALE", -10: "ATTN_ERR_HEADS", -11: "ATTN_ERR_WORKSPACE",
-    -12: "ATTN_ERR_ROPE", -13: "ATTN_ERR_STRIDE",
+    -12: "ATTN_ERR_ROPE", -13: "ATTN_ERR_STRIDE", -14: "ATTN_ERR_SCRATCH",
 }
 
 
@@ -65,6 +66,7 @@ SIGNATURES = {
     "attn_bwd_gqa": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
     "attn_decode_workspace_bytes": [_I, _I, _I, _I, _I],
     "attn_decode": [_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _I, _F, _I, _I, _P],
+    "attn_decode_noalloc": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P],
     "attn_rope_table": [_P, _I, _I, _F, _P],
     "attn_rope": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _I, _I, _P],
     "attn_fwd_rope": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
@@ -483,6 +485,27 @@ def attn_decode(q, k_cache, v_cache, cache_lens, o, lse, workspace, scale, max_l
         _ptr(q, "q", device=dev), _ptr(k_cache, "k_cache", device=dev), _ptr(v_cache, "v_cache", device=dev),
         _ptr(cache_lens, "cache_lens", (B,), torch.int32, dev), _ptr(o, "o", (B, H, D), torch.float32, dev),
         _ptr(lse, "lse", (B, H), torch.float32, dev), ws_ptr, ws_bytes,
+        B, H, H_kv, S_max, D, float(scale), int(max_len), _dtype_code(q), _stream(stream)))
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, cache_lens, o, lse, scale, max_len, stream=None):
+    """attn_decode without a workspace: the chunk partials go to the library's
+    static per-GPU scratch (ATTN_DECODE_SCRATCH_BYTES); calls that overlap on
+    one GPU race.  Raises AttnError (ATTN_ERR_SCRATCH) when the split needs more."""
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, H, D] and the caches [B, H_kv, S_max, D]")
+    B, H, D = q.shape
+    _, H_kv, S_max, _ = k_cache.shape
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if tuple(t.shape) != (B, H_kv, S_max, D) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be [B, H_kv, S_max, D] with q's dtype")
+    dev = q.device
+    _check(lib.attn_decode_noalloc(
+        _ptr(q, "q", device=dev), _ptr(k_cache, "k_cache", device=dev), _ptr(v_cache, "v_cache", device=dev),
+        _ptr(cache_lens, "cache_lens", (B,), torch.int32, dev), _ptr(o, "o", (B, H, D), torch.float32, dev),
+        _ptr(lse, "lse", (B, H), torch.float32, dev),
         B, H, H_kv, S_max, D, float(scale), int(max_len), _dtype_code(q), _stream(stream)))
 
 

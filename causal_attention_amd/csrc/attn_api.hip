@@ -11,8 +11,8 @@
 
 namespace {
 
-constexpr int kAbiVersion = 170;  // 1.70: grouped-query, decode, RoPE, fp16 inputs, attn_params calls (16-bit outputs,
-                                  // strides), the fused dQ + Delta stage, the build identifier
+constexpr int kAbiVersion = 180;  // 1.80: grouped-query, decode, RoPE, fp16 inputs, attn_params calls (16-bit outputs,
+                                  // strides), the fused dQ + Delta stage, the build identifier, decode without allocation
 
 #ifndef ATTN_SOURCE_DIGEST
 #error "build with -DATTN_SOURCE_DIGEST=... (causal_attention_amd/build.py computes it from the sources)"
@@ -233,6 +233,7 @@ const char *attn_status_string(int status) {
     case ATTN_ERR_WORKSPACE: return "workspace NULL or smaller than attn_decode_workspace_bytes()";
     case ATTN_ERR_ROPE: return "RoPE table NULL or shorter than the positions (S, or max_seqlen for documents), or base not finite and > 0";
     case ATTN_ERR_STRIDE: return "strides: batch and head >= 0, sequence >= D, panel extent < 2^31 bytes";
+    case ATTN_ERR_SCRATCH: return "attn_decode_noalloc: the key split needs more than ATTN_DECODE_SCRATCH_BYTES (16 MiB) of partials; use attn_decode with a workspace";
     default: return "unknown status";
   }
 }
@@ -403,9 +404,14 @@ size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int D, int max_len) {
   return attn::decode_workspace_bytes(B, H, H_kv, D, max_len);
 }
 
-int attn_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *cache_lens, float *o,
-                float *lse, void *workspace, size_t workspace_bytes, int B, int H, int H_kv, int S_max, int D,
-                float scale, int max_len, int dtype, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the decode entry points; fills `a` on success.
+int decode_args(const void *q, const void *k_cache, const void *v_cache, const int32_t *cache_lens, float *o,
+                float *lse, int B, int H, int H_kv, int S_max, int D, float scale, int max_len, int dtype,
+                void *stream, attn::DecodeArgs &a) {
   int st = check_common(B, H, S_max, D, dtype);
   if (st != ATTN_OK) return st;
   if ((st = check_heads(H, H_kv)) != ATTN_OK) return st;
@@ -414,17 +420,13 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, const i
   if (max_len < 1 || max_len > S_max) return ATTN_ERR_SHAPE;
   if (!q || !k_cache || !v_cache || !cache_lens || !o) return ATTN_ERR_NULL;
   if ((st = check_scale(scale)) != ATTN_OK) return st;
-  const size_t need = attn::decode_workspace_bytes(B, H, H_kv, D, max_len);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
-  attn::DecodeArgs a{};
+  a = attn::DecodeArgs{};
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.cache_lens = cache_lens;
   a.o = o;
   a.lse = lse;
-  a.o_part = static_cast<float *>(workspace);
-  a.lse_part = need > 0 ? static_cast<float *>(workspace) + (need / sizeof(float)) / (D + 1) * D : nullptr;
   a.B = B;
   a.H = H;
   a.H_kv = H_kv;
@@ -434,7 +436,36 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, const i
   a.scale = scale;
   a.dtype = dtype;
   a.stream = static_cast<hipStream_t>(stream);
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *cache_lens, float *o,
+                float *lse, void *workspace, size_t workspace_bytes, int B, int H, int H_kv, int S_max, int D,
+                float scale, int max_len, int dtype, void *stream) {
+  attn::DecodeArgs a;
+  const int st = decode_args(q, k_cache, v_cache, cache_lens, o, lse, B, H, H_kv, S_max, D, scale, max_len, dtype,
+                             stream, a);
+  if (st != ATTN_OK) return st;
+  const size_t need = attn::decode_workspace_bytes(B, H, H_kv, D, max_len);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  a.o_part = static_cast<float *>(workspace);
+  a.lse_part = need > 0 ? static_cast<float *>(workspace) + (need / sizeof(float)) / (D + 1) * D : nullptr;
   return to_status(attn::launch_decode(a));
+}
+
+int attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache, const int32_t *cache_lens,
+                        float *o, float *lse, int B, int H, int H_kv, int S_max, int D, float scale, int max_len,
+                        int dtype, void *stream) {
+  attn::DecodeArgs a;
+  const int st = decode_args(q, k_cache, v_cache, cache_lens, o, lse, B, H, H_kv, S_max, D, scale, max_len, dtype,
+                             stream, a);
+  if (st != ATTN_OK) return st;
+  if (attn::decode_workspace_bytes(B, H, H_kv, D, max_len) > attn::decode_scratch_bytes()) return ATTN_ERR_SCRATCH;
+  return to_status(attn::launch_decode_noalloc(a));
 }
 
 }  // extern "C"

@@ -21,8 +21,17 @@
 //    M = max_c LSE_c, O = sum_c e^(LSE_c - M) O_c / sum_c e^(LSE_c - M),
 //    LSE = M + ln sum_c e^(LSE_c - M).  With one chunk the first kernel writes
 //    the result directly.
+#include <mutex>
+
+#include "attn_api.h"
 #include "attn_device.h"
 #include "attn_launch.h"
+
+// Chunk partials of attn_decode_noalloc: a static buffer on every GPU the
+// library runs on (callers that cannot allocate).  In host code `scratch`
+// names a host-side stand-in; its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_SCRATCH_BYTES];
 
 namespace attn {
 
@@ -225,6 +234,49 @@ hipError_t launch_decode(const DecodeArgs &a) {
     case 2: return launch_decode_dt<f16>(a);
     default: return launch_decode_dt<float>(a);
   }
+}
+
+size_t decode_scratch_bytes() { return sizeof(scratch); }
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_addr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// Device address of this device's `scratch` (the current device), looked up
+// on the first call on that device with the device current.
+hipError_t scratch_for_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_addr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    scratch_addr[dev] = p;
+  }
+  *out = scratch_addr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_decode_noalloc(DecodeArgs a) {
+  const size_t need = decode_workspace_bytes(a.B, a.H, a.H_kv, a.D, a.max_len);
+  if (need > sizeof(scratch)) return hipErrorInvalidValue;  // the caller checks first
+  a.o_part = nullptr;
+  a.lse_part = nullptr;
+  if (need > 0) {
+    void *base = nullptr;
+    const hipError_t e = scratch_for_current_device(&base);
+    if (e != hipSuccess) return e;
+    // the same partition of the partials as attn_decode's workspace
+    a.o_part = static_cast<float *>(base);
+    a.lse_part = static_cast<float *>(base) + (need / sizeof(float)) / (a.D + 1) * a.D;
+  }
+  return launch_decode(a);
 }
 
 size_t decode_workspace_bytes(int B, int H, int H_kv, int D, int max_len) {

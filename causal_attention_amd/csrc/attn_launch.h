@@ -59,6 +59,11 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs &a);
 size_t decode_workspace_bytes(int B, int H, int H_kv, int D, int max_len);
+// The same with the partials in the library's static per-device scratch
+// (a.o_part, a.lse_part ignored); the caller has checked the size against
+// decode_scratch_bytes().
+hipError_t launch_decode_noalloc(DecodeArgs a);
+size_t decode_scratch_bytes();
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const Args &a);

@@ -80,7 +80,9 @@ typedef enum attn_status {
   ATTN_ERR_WORKSPACE = -11,    /* decode workspace missing or too small            */
   ATTN_ERR_ROPE = -12,         /* RoPE table NULL or shorter than the positions,
                                   or base not finite and > 0                       */
-  ATTN_ERR_STRIDE = -13        /* attn_params strides out of range                 */
+  ATTN_ERR_STRIDE = -13,       /* attn_params strides out of range                 */
+  ATTN_ERR_SCRATCH = -14       /* attn_decode_noalloc: the split needs more than
+                                  ATTN_DECODE_SCRATCH_BYTES of scratch             */
 } attn_status;
 
 enum { ATTN_MASK_CAUSAL = 0, ATTN_MASK_DOC_CAUSAL = 1 };
@@ -201,6 +203,28 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
                 void *workspace, size_t workspace_bytes,
                 int B, int H, int H_kv, int S_max, int D, float scale, int max_len,
                 int dtype, void *stream);
+
+/*
+ * The same decode step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): no workspace argument, and no allocation by the library.  The
+ * chunk partials go to a static device buffer of ATTN_DECODE_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on until the process ends (its
+ * address is looked up once per device, on the first call there).  The
+ * kernels, the split and the results are those of attn_decode.  Calls whose
+ * split needs more than ATTN_DECODE_SCRATCH_BYTES (attn_decode_workspace_bytes
+ * larger) return ATTN_ERR_SCRATCH and touch no memory.  Every call on one GPU
+ * shares that GPU's buffer: calls that overlap on one GPU (different streams,
+ * or threads) race and must be ordered by the caller; calls on one stream are
+ * ordered by it.  Nothing in the buffer needs clearing: each call writes every
+ * partial it reads.  Other arguments and errors as attn_decode.
+ */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+
+int attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *cache_lens, float *o, float *lse,
+                        int B, int H, int H_kv, int S_max, int D, float scale, int max_len,
+                        int dtype, void *stream);
 
 /*
  * Rotary position embedding (RoPE) of queries and keys: RoFormer (Su et al.

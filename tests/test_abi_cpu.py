@@ -31,7 +31,7 @@ def test_header_status_codes_match_binding():
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 170
+    assert lib.attn_abi_version() == 180
 
 
 def test_build_id_is_the_source_digest(lib):
@@ -178,6 +178,36 @@ def _decode(lib, **kw):
 ])
 def test_decode_rejects_invalid_arguments(lib, kw, code):
     assert _decode(lib, **kw) == code
+
+
+def _decode_noalloc(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, o=FAKE, lse=FAKE, B=2, H=8, H_kv=2, S_max=4096, D=64, scale=0.125,
+             max_len=4096, dtype=1, stream=None)
+    a.update(kw)
+    return lib.attn_decode_noalloc(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["B"], a["H"], a["H_kv"],
+                                   a["S_max"], a["D"], a["scale"], a["max_len"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(lens=None), -1), (dict(o=None), -1), (dict(D=48), -3), (dict(dtype=3), -4),
+    (dict(H_kv=3), -10), (dict(H=64, H_kv=1), -8), (dict(max_len=0), -2), (dict(max_len=4097), -2),
+    (dict(scale=float("nan")), -9),
+    # 1024 chunks x 32 query heads x 129 floats: more than the 16 MiB scratch
+    (dict(B=1, H=32, H_kv=1, S_max=65536, max_len=65536, D=128), -14),
+])
+def test_decode_noalloc_rejects_invalid_arguments(lib, kw, code):
+    assert _decode_noalloc(lib, **kw) == code
+
+
+def test_decode_noalloc_scratch_limit(lib):
+    """The refusal follows the workspace attn_decode would need: the largest
+    split that fits passes validation (and fails later only for lack of a GPU)."""
+    assert lib.attn_decode_workspace_bytes(1, 32, 1, 128, 65536) > ca.ATTN_DECODE_SCRATCH_BYTES
+    assert lib.attn_decode_workspace_bytes(1, 16, 1, 128, 65536) <= ca.ATTN_DECODE_SCRATCH_BYTES
+    assert _decode_noalloc(lib, B=1, H=16, H_kv=1, S_max=65536, max_len=65536, D=128) in (0, -7)
+    with open(_binding.HEADER_PATH) as f:
+        assert "#define ATTN_DECODE_SCRATCH_BYTES ((size_t)16 << 20)" in f.read()
+    assert ca.ATTN_DECODE_SCRATCH_BYTES == 16 << 20
 
 
 def test_decode_workspace_size(lib):
@@ -333,6 +363,7 @@ def test_no_device_reports_hip_error(lib):
     assert lib.attn_bwd_dq_delta(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 0.1, 0, None, 0, 0,
                                  1, None) == -7
     assert _decode(lib) == -7
+    assert _decode_noalloc(lib) == -7
     assert _fwd_gqa(lib, 2) == -7
     assert _bwd_gqa(lib, 1) == -7
     assert _rope(lib) == -7 and _fwd_rope(lib) == -7 and _bwd_rope(lib) == -7
