@@ -113,15 +113,19 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   static_assert(SPLIT == 1 || SPLIT == 2, "one or two halves");
   static_assert(SPLIT == 1 || DB * 16 * kWaveSize * 4 <= SPLIT * BMQ * D * (int)sizeof(T),
                 "a wave's partial dK (or dV) fits one ring slot");
+  constexpr int VROWS = BMQ < 64 ? 64 : BMQ;  // rows of LSE / Delta per slot
+  constexpr int NVEC = 2 * (VROWS / 64);      // 64-row copies of LSE and Delta per tile
+  static_assert(BMQ <= 64 || BMQ % 64 == 0, "LSE / Delta copies move 64 rows at a time");
+  static_assert(NVEC <= NWH, "one LSE or Delta copy per wave");
 
   __shared__ __attribute__((aligned(1024))) T sQ0[SPLIT * BMQ * D];  // [half][row][col]
   __shared__ __attribute__((aligned(1024))) T sQ1[SPLIT * BMQ * D];
   __shared__ __attribute__((aligned(1024))) T sO0[SPLIT * BMQ * D];  // dO
   __shared__ __attribute__((aligned(1024))) T sO1[SPLIT * BMQ * D];
-  __shared__ __attribute__((aligned(256))) float sL0[SPLIT * 64];    // LSE (natural log)
-  __shared__ __attribute__((aligned(256))) float sL1[SPLIT * 64];
-  __shared__ __attribute__((aligned(256))) float sD0[SPLIT * 64];    // Delta
-  __shared__ __attribute__((aligned(256))) float sD1[SPLIT * 64];
+  __shared__ __attribute__((aligned(256))) float sL0[SPLIT * VROWS];  // LSE (natural log)
+  __shared__ __attribute__((aligned(256))) float sL1[SPLIT * VROWS];
+  __shared__ __attribute__((aligned(256))) float sD0[SPLIT * VROWS];  // Delta
+  __shared__ __attribute__((aligned(256))) float sD1[SPLIT * VROWS];
 
   const RowTile t = DOC ? doc_tile(cu, blockIdx.x, gridDim.x, ntiles, n_seqs, BN, false)
                         : causal_tile(blockIdx.x, gridDim.x, ntiles, BN, S, false);
@@ -155,8 +159,8 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
 
   auto qslot = [&]<int P>() { return lds_cast(P == 0 ? sQ0 : sQ1) + half * BMQ * D; };
   auto oslot = [&]<int P>() { return lds_cast(P == 0 ? sO0 : sO1) + half * BMQ * D; };
-  auto lslot = [&]<int P>() { return lds_cast(P == 0 ? sL0 : sL1) + half * 64; };
-  auto dslot = [&]<int P>() { return lds_cast(P == 0 ? sD0 : sD1) + half * 64; };
+  auto lslot = [&]<int P>() { return lds_cast(P == 0 ? sL0 : sL1) + half * VROWS; };
+  auto dslot = [&]<int P>() { return lds_cast(P == 0 ? sD0 : sD1) + half * VROWS; };
   uint32_t qoff[QTile::kPerWave], dooff[QTile::kPerWave];
   QTile::lane_offsets(qoff, kg, lane, lq.ss);
   QTile::lane_offsets(dooff, kg, lane, ldo.ss);
@@ -172,8 +176,13 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     const GBuf gdel(delta + rbase, (uint32_t)(t.seg_end * sizeof(float)));
     QTile::issue_at(gq, qslot.template operator()<P>(), QTile::row0_bytes(q0, lq.ss), qoff, kg);
     QTile::issue_at(gdo, oslot.template operator()<P>(), QTile::row0_bytes(q0, ldo.ss), dooff, kg);
-    if (kg == 0) dma_vec64(glse, lslot.template operator()<P>(), q0, lane);
-    if (kg == 1) dma_vec64(gdel, dslot.template operator()<P>(), q0, lane);
+    // 64-row copies of LSE, then of Delta, one per wave
+    if (kg < NVEC / 2) {
+      dma_vec64(glse, lslot.template operator()<P>() + 64 * kg, q0 + 64 * kg, lane);
+    } else if (kg < NVEC) {
+      const int r = 64 * (kg - NVEC / 2);
+      dma_vec64(gdel, dslot.template operator()<P>() + r, q0 + r, lane);
+    }
   };
   issue.template operator()<0>(0);
 
@@ -217,7 +226,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   // MI355X, backward: ctx 1024 97.8 -> 94.9 us, S = 8192 499 -> 490 us; at
   // D = 32 the second set of score accumulators costs the fourth wave per
   // SIMD (165 VGPRs) and it is 3-6 % slower.
-  constexpr bool kPipe = QB == 2 && sizeof(T) == 2 && D == 64;
+  constexpr bool kPipe = QB % 2 == 0 && sizeof(T) == 2 && D == 64;
   auto tile = [&]<int P>(int q0, bool masked) {
     const lds_t<T> *sq = qslot.template operator()<P>();
     const lds_t<T> *so = oslot.template operator()<P>();
@@ -225,15 +234,11 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     const lds_t<float> *sd = dslot.template operator()<P>();
     const TrSwz<T, D> tr = tr0.pinned();
     const RowFrag<T, D> rf = rf0.pinned();
-    ATTN_SCHED_HINT();
+    sched_hint<D != 64>();
     if constexpr (kPipe) {
-      // Two 32-query blocks, software-pipelined inside the wave: block 1's
-      // score products issue among block 0's softmax, and block 0's dV / dK
-      // products among block 1's softmax.  The mask branches sit between
-      // these groups, so each group is one basic block the compiler can
-      // interleave.  A block whose queries all precede this wave's keys is
+      // The tile's 32-query blocks in a software pipeline inside the wave
+      // (below).  A block whose queries all precede this wave's keys is
       // computed with every score masked: P = dS = 0 adds exact zeros.
-      f32x16 sa0 = f32x16{}, pa0 = f32x16{}, sa1 = f32x16{}, pa1 = f32x16{};
       auto scores = [&](int qb, f32x16 &sacc, f32x16 &pacc) {
         E::mma_rows(sacc, E::rows_a(-sl[qb * 32 + c] * rscale, hh), ones);
         E::mma_rows(pacc, E::rows_a(-sd[qb * 32 + c], hh), ones);
@@ -269,19 +274,34 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
           E::mma(dkacc[db], tr(sq, 32 * qb + 16, db), ps[3]);
         }
       };
-      frag ps0[4], ps1[4];
-      scores(0, sa0, pa0);
-      if (masked) mask(0, sa0);
-      scores(1, sa1, pa1);
-      soft(sa0, pa0, ps0);
-      // keep block 0's softmax in this group: without a use here the
-      // compiler sinks it past the next branch, next to its products
+      // Each step issues block b + 1's score products, block b's softmax and
+      // block b - 1's dV / dK products: independent work in one basic block
+      // that the compiler interleaves; the mask branch sits between steps.
+      // (Measured with two blocks per tile and with four (128-query tiles):
+      // within 1 % of each other.)
+      f32x16 sa[2], pa[2];
+      frag ps[2][4];
+      sa[0] = f32x16{};
+      pa[0] = f32x16{};
+      scores(0, sa[0], pa[0]);
+      if (masked) mask(0, sa[0]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(ps0[i]));
-      if (masked) mask(1, sa1);
-      accum(0, ps0);
-      soft(sa1, pa1, ps1);
-      accum(1, ps1);
+      for (int b = 0; b <= QB; ++b) {
+        if (b >= 1) accum(b - 1, ps[(b - 1) % 2]);
+        if (b + 1 < QB) {
+          sa[(b + 1) % 2] = f32x16{};
+          pa[(b + 1) % 2] = f32x16{};
+          scores(b + 1, sa[(b + 1) % 2], pa[(b + 1) % 2]);
+        }
+        if (b < QB) {
+          soft(sa[b % 2], pa[b % 2], ps[b % 2]);
+          // keep block b's softmax in this step: without a use here the
+          // compiler sinks it past the next branch, next to its products
+#pragma unroll
+          for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(ps[b % 2][i]));
+        }
+        if (b + 1 < QB && masked) mask(b + 1, sa[(b + 1) % 2]);
+      }
       return;
     }
 #pragma unroll
@@ -381,27 +401,38 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     }
   }
 
+  // Each wave stores its keys' rows through ring-slot memory of its own
+  // (store_block_rows): with one half, slot kg once every wave is past its
+  // last tile; with two, the slot its partner's partial sums came through.
+  if constexpr (SPLIT == 1) wg_barrier();
   if (!wave_active) return;
   const GBuf gdk(dk + panel_off(ldk, bi, hk), panel_bytes(ldk, t.r_end, D, sizeof(OT)));
   const GBuf gdv(dv + panel_off(ldv, bi, hk), panel_bytes(ldv, t.r_end, D, sizeof(OT)));
   // RoPE: this key's table row (keys past the tile end are not stored)
   const float *rrow =
       rope == nullptr ? nullptr : rope + (size_t)min(min(key, t.r_end - 1) - t.seg_start, rope_npos - 1) * D;
+  static_assert(SPLIT * BMQ * D * sizeof(T) >= 4096, "a 4 KB slot per wave");
+  lds_t<f32x4> *scr;
+  if constexpr (SPLIT == 1)
+    scr = (lds_t<f32x4> *)(kg == 0 ? lds_cast(sQ0) : kg == 1 ? lds_cast(sQ1) : kg == 2 ? lds_cast(sO0) : lds_cast(sO1));
+  else
+    scr = (lds_t<f32x4> *)lds_cast(kg == 0 ? sQ0 : sO0);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
+    f32x16 a = dkacc[db] * scale;
+    if (rope != nullptr) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4 a4, b4;
+      for (int g = 0; g < 4; ++g) {
+        f32x4 a4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a4[i] = dkacc[db][4 * g + i] * scale;
-        b4[i] = dvacc[db][4 * g + i];
+        for (int i = 0; i < 4; ++i) a4[i] = a[4 * g + i];
+        rope_back(a4, *reinterpret_cast<const f32x4 *>(rrow + db * 32 + 8 * g + 4 * hh));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[4 * g + i] = a4[i];
       }
-      if (rope != nullptr) rope_back(a4, *reinterpret_cast<const f32x4 *>(rrow + db * 32 + 8 * g + 4 * hh));
-      const uint32_t col = (uint32_t)(db * 32 + 8 * g + 4 * hh);
-      store_out4<OT>(gdk, a4, (uint32_t)key * ldk.ss + col);
-      store_out4<OT>(gdv, b4, (uint32_t)key * ldv.ss + col);
     }
+    store_block_rows<OT>(a, scr, gdk, w0, ldk.ss, db * 32, lane);
+    store_block_rows<OT>(dvacc[db], scr, gdv, w0, ldv.ss, db * 32, lane);
   }
 }
 
@@ -610,6 +641,10 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_pair_kernel(
     if (j + 2 <= ntile) step.template operator()<2>(j + 2);
   }
 
+  // Every wave is past its last tile: each stores its keys' rows through a
+  // ring slot of its own (store_block_rows).
+  static_assert(NW == 4 && BMQ * D * sizeof(T) >= 4096, "one 4 KB slot per wave");
+  wg_barrier();
   if (!wave_active) return;
   OT *out = vwave ? dv : dk;
   const Layout &lout = vwave ? ldv : ldk;
@@ -619,16 +654,23 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_pair_kernel(
   const float *rrow = (rope == nullptr || vwave)
                           ? nullptr
                           : rope + (size_t)min(min(key, t.r_end - 1) - t.seg_start, rope_npos - 1) * D;
+  lds_t<f32x4> *scr = (lds_t<f32x4> *)(wave == 0 ? lds_cast(sQ0) : wave == 1 ? lds_cast(sQ1)
+                                       : wave == 2 ? lds_cast(sO0) : lds_cast(sO1));
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
+    f32x16 a = acc[db] * osc;
+    if (rrow != nullptr) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4 a4;
+      for (int g = 0; g < 4; ++g) {
+        f32x4 a4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a4[i] = acc[db][4 * g + i] * osc;
-      if (rrow != nullptr) rope_back(a4, *reinterpret_cast<const f32x4 *>(rrow + db * 32 + 8 * g + 4 * hh));
-      store_out4<OT>(gout, a4, (uint32_t)key * lout.ss + (uint32_t)(db * 32 + 8 * g + 4 * hh));
+        for (int i = 0; i < 4; ++i) a4[i] = a[4 * g + i];
+        rope_back(a4, *reinterpret_cast<const f32x4 *>(rrow + db * 32 + 8 * g + 4 * hh));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[4 * g + i] = a4[i];
+      }
     }
+    store_block_rows<OT>(a, scr, gout, w0, lout.ss, db * 32, lane);
   }
 }
 
@@ -759,7 +801,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
     const TrSwz<T, D> tr = tr0.pinned();
     const RowFrag<T, D> rf = rf0.pinned();
     const int lim = qi - k0 - 4 * hh;  // the mask's per-lane limit
-    ATTN_SCHED_HINT();
+    sched_hint<D != 64>();
     if constexpr (kPipe) {
       // Two 32-key blocks, software-pipelined inside the wave as in dK/dV:
       // block 1's score products issue among block 0's softmax, block 0's
@@ -851,21 +893,34 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dq_kernel(
     if (j + 1 < ntile) step.template operator()<1>(j + 1);
   }
 
+  // Every wave is past its last read of the ring slots: each wave stores its
+  // rows through one slot (store_block_rows).
+  static_assert(BN * D * sizeof(T) >= 4096, "one 4 KB slot per wave");
+  wg_barrier();
   if (!wave_active) return;
   const GBuf gdq(dq + panel_off(ldq, bi, hq), panel_bytes(ldq, t.r_end, D, sizeof(OT)));
   // RoPE: this query's table row (queries past the tile end are not stored)
   const float *rrow =
       rope == nullptr ? nullptr : rope + (size_t)min(min(qi, t.r_end - 1) - t.seg_start, rope_npos - 1) * D;
+  lds_t<f32x4> *scr = (lds_t<f32x4> *)(wave == 0 ? kslot.template operator()<0>()
+                                       : wave == 1 ? kslot.template operator()<1>()
+                                       : wave == 2 ? vslot.template operator()<0>()
+                                                   : vslot.template operator()<1>());
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
+    f32x16 a = dqacc[db] * scale;
+    if (rope != nullptr) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4 a4;
+      for (int g = 0; g < 4; ++g) {
+        f32x4 a4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a4[i] = dqacc[db][4 * g + i] * scale;
-      if (rope != nullptr) rope_back(a4, *reinterpret_cast<const f32x4 *>(rrow + db * 32 + 8 * g + 4 * hh));
-      store_out4<OT>(gdq, a4, (uint32_t)(qi * ldq.ss + db * 32 + 8 * g + 4 * hh));
+        for (int i = 0; i < 4; ++i) a4[i] = a[4 * g + i];
+        rope_back(a4, *reinterpret_cast<const f32x4 *>(rrow + db * 32 + 8 * g + 4 * hh));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[4 * g + i] = a4[i];
+      }
     }
+    store_block_rows<OT>(a, scr, gdq, w0, ldq.ss, db * 32, lane);
   }
 }
 

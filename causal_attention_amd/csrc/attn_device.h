@@ -44,18 +44,16 @@ typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaveSize = 64;
 
-// Instruction-scheduling strategy requested for the tile loops: the
-// compiler's instruction-group strategy 3 interleaves exponentials with
-// matrix-core instructions (a hint only; no effect on results).  Measured a
-// few percent faster than the default schedule; -DATTN_IGLP=-1 turns it off.
-#ifndef ATTN_IGLP
-#define ATTN_IGLP 3
-#endif
-#if ATTN_IGLP >= 0
-#define ATTN_SCHED_HINT() __builtin_amdgcn_iglp_opt(ATTN_IGLP)
-#else
-#define ATTN_SCHED_HINT() ((void)0)
-#endif
+// Instruction-scheduling strategy requested for a tile loop: the compiler's
+// instruction-group strategy 3, which interleaves exponentials with
+// matrix-core instructions (a hint only; no effect on results).  Measured on
+// MI355X it helps the forward and the D = 128 backward by a few percent; for
+// the D = 64 backward kernels, whose tile bodies are pipelined by hand, it
+// serialises each LDS read with its product and the backward runs 2-3 %
+// faster without it.
+template <bool ON> __device__ __forceinline__ void sched_hint() {
+  if constexpr (ON) __builtin_amdgcn_iglp_opt(3);
+}
 
 // Pointers into LDS carry their address space explicitly: the compiler then
 // keeps track of which LDS object an access touches, and waits for an
@@ -344,6 +342,65 @@ __device__ __forceinline__ void store_out4(const GBuf &g, const f32x4 &v, uint32
     for (int i = 0; i < 4; ++i) h[i] = (OT)v[i];
     g.store8(__builtin_bit_cast(u32x2, h), e * 2u);
   }
+}
+
+// Store of one 32 x 32 output block that a wave holds in accumulator layout
+// (lane (c, hh) holds row c, columns 8g + 4hh .. 8g + 4hh + 3 in registers
+// 4g .. 4g + 3; e.g. O = (O^T)^T with a lane per query), through 4 KB of the
+// wave's own LDS, so that every store instruction writes whole rows of the
+// block: written straight from the accumulator, each instruction covers 32
+// rows with 32 bytes apiece (32 partial cache lines), rearranged it covers 8
+// rows with 128 bytes apiece (fp32) or 16 rows with 64 (16-bit outputs), four
+// to eight times fewer memory requests for the same bytes.
+//   v        the block, already scaled as stored
+//   scratch  256 f32x4 of LDS that no other wave touches meanwhile
+//   g        output buffer; rows past its range are dropped
+//   row0     row of the block's row 0; ss the row stride in elements
+//   col0     element column of the block's column 0
+// Chunk x (16 bytes) of scratch row r sits at x ^ ((r >> 1) & 7): the 16
+// lanes of each write (16 rows, one chunk) and each read (2 rows, 8 chunks)
+// then fall on distinct banks.  LDS accesses of one wave complete in order,
+// so the reads see the writes; the empty asm keeps the compiler from
+// reordering them.
+template <typename OT>
+__device__ __forceinline__ void store_block_rows(const f32x16 &v, lds_t<f32x4> *scratch, const GBuf &g, int row0,
+                                                 int ss, int col0, int lane) {
+  // the lane index is re-derived here so that none of this address arithmetic
+  // is shared with (and kept live through) the caller's main loop
+  asm volatile("" : "+v"(lane));
+  const int c = lane % 32, hh = lane / 32;
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq) {
+    f32x4 x4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x4[i] = v[4 * gq + i];
+    scratch[c * 8 + ((2 * gq + hh) ^ ((c >> 1) & 7))] = x4;
+  }
+  asm volatile("" ::: "memory");
+  if constexpr (sizeof(OT) == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = 8 * k + lane / 8, x = lane % 8;
+      const f32x4 x4 = scratch[r * 8 + (x ^ ((r >> 1) & 7))];
+      g.store16(x4, (uint32_t)((row0 + r) * ss + col0 + 4 * x) * 4u);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int r = 16 * k + lane / 4, x = 2 * (lane % 4);
+      const f32x4 a = scratch[r * 8 + (x ^ ((r >> 1) & 7))];
+      const f32x4 b = scratch[r * 8 + ((x + 1) ^ ((r >> 1) & 7))];
+      typename Vec8Of<OT>::type h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[i] = (OT)a[i];
+        h[4 + i] = (OT)b[i];
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, h), g.r,
+                                             (uint32_t)((row0 + r) * ss + col0 + 4 * x) * 2u, 0, 0);
+    }
+  }
+  asm volatile("" ::: "memory");
 }
 
 // An 8-slot fragment of row `row`, columns [col, col + 8), of rows `ss`

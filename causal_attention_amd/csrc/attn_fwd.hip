@@ -197,7 +197,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
     wg_barrier();
     if (j + 1 < ntile) issue.template operator()<1 - P>(j + 1);
     if (j >= jw) return;
-    ATTN_SCHED_HINT();
+    sched_hint<true>();
     const int k0 = kv_lo + j * BN;
     const bool masked = (k0 + BN - 1 > w0) || (k0 + BN > t.seg_end);
     const lds_t<T> *ks = kslot.template operator()<P>();
@@ -229,22 +229,22 @@ __global__ __launch_bounds__(NW * 64, MINB) void attn_fwd_kernel(const T *__rest
     if (j + 1 < ntile) step.template operator()<1>(j + 1);
   }
 
+  // Every wave is past its last read of the ring slots: each wave stores its
+  // rows through one slot (store_block_rows).
+  static_assert(NW == 4 && BN * D * sizeof(T) >= 4096, "one 4 KB slot per wave");
+  wg_barrier();
   if (!wave_active) return;
   const GBuf go(o + panel_off(lo, bi, hq), panel_bytes(lo, t.r_end, D, sizeof(OT)));
   const int qi = w0 + c;
   const float lt = l + swap_halves(l);
   const float lrt = kRounded ? lr + swap_halves(lr) : lt;
   const float inv = 1.0f / lrt;
+  lds_t<f32x4> *scr = (lds_t<f32x4> *)(wave == 0 ? kslot.template operator()<0>()
+                                       : wave == 1 ? kslot.template operator()<1>()
+                                       : wave == 2 ? vslot.template operator()<0>()
+                                                   : vslot.template operator()<1>());
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4 val;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) val[i] = oacc[db][4 * g + i] * inv;
-      store_out4<OT>(go, val, (uint32_t)(qi * lo.ss + db * 32 + 8 * g + 4 * hh));
-    }
-  }
+  for (int db = 0; db < DB; ++db) store_block_rows<OT>(oacc[db] * inv, scr, go, w0, lo.ss, db * 32, lane);
   if (lse != nullptr && hh == 0 && qi < t.r_end) lse[(size_t)t.head * S + qi] = (m + __log2f(lt)) * kLn2;
 }
 
