@@ -16,8 +16,8 @@ those K steps.  Inside the same loop HIP events on the launch stream bracket
 every step's forward and backward, giving per-iteration median, p10 and p90
 (`events_ms`).  A second loop writes a 512 MiB buffer before each step (more
 than the 256 MiB last-level cache holds), so every step starts cold
-(`cold`).  The GPU's graphics clock is sampled while steps run back to back
-(`sclk_mhz`).
+(`cold`).  The graphics clock is measured while steps run back to back
+(`sclk_mhz`: the library's clock probe on a side stream).
 
 Besides the headline workload the line carries:
   kernels       per-kernel median/p10/p90 from HIP events, each kernel run
@@ -426,65 +426,36 @@ def roofline(w, times, per_kernel):
     return r
 
 
-def sample_sclk(run, seconds):
-    """Graphics clock (MHz) sampled about every 2 ms from the driver's GPU
-    metrics while `run` (one step) is called back to back for `seconds`:
-    mean, min and max of the samples (for every XCD where the metrics give one
-    clock per XCD).  None if the metrics are not readable here."""
-    import threading
+def sample_sclk(w, seconds):
+    """Graphics clock (MHz) while the workload's steps run back to back for
+    `seconds`: the library's clock probe (one wave on a stream of its own,
+    reading the shader-clock and 100 MHz counters) spans the middle 80 % of
+    that window; cycles / ticks x 100 MHz is the clock of the chiplet the
+    probe ran on."""
     import torch
-    try:
-        import amdsmi
-        amdsmi.amdsmi_init()
-        handle = amdsmi.amdsmi_get_processor_handles()[0]
-        amdsmi.amdsmi_get_gpu_metrics_info(handle)
-    except Exception as e:  # no metrics on this host: report why
-        return {"error": f"{type(e).__name__}: {e}"[:200]}
-
-    def clocks(m):
-        out = []
-        for key in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
-            v = m.get(key)
-            vals = v if isinstance(v, list) else [v]
-            vals = [float(x) for x in vals if isinstance(x, (int, float)) and 0 < x < 10000]
-            if vals:
-                return key, vals
-        return None, out
-
-    samples, keys = [], set()
-    stop = threading.Event()
-
-    def poll():
-        while not stop.is_set():
-            try:
-                key, vals = clocks(amdsmi.amdsmi_get_gpu_metrics_info(handle))
-                if vals:
-                    keys.add(key)
-                    samples.append(float(np.mean(vals)))
-            except Exception:
-                pass
-            time.sleep(0.002)
-
-    th = threading.Thread(target=poll, daemon=True)
-    th.start()
+    import causal_attention_amd as ca
+    out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        w.step()
     t_end = time.perf_counter() + seconds
     n = 0
+    launched = False
     while time.perf_counter() < t_end:
-        run()
+        w.step()
         n += 1
-        if n % 16 == 0:
-            torch.cuda.synchronize()
+        if not launched and n == 8:  # the queue is full of work: start the probe
+            ca.clock_probe(out, int(0.8 * seconds * 1e8), stream=side)
+            launched = True
+        if n % 64 == 0:  # keep the host at most 64 steps ahead
+            w.stream.synchronize()
     torch.cuda.synchronize()
-    stop.set()
-    th.join()
-    try:
-        amdsmi.amdsmi_shut_down()
-    except Exception:
-        pass
-    if not samples:
-        return {"error": "no clock in the GPU metrics"}
-    return {"mean": float(np.mean(samples)), "min": float(np.min(samples)), "max": float(np.max(samples)),
-            "samples": len(samples), "steps": n, "field": sorted(keys)[0]}
+    cycles, ticks = (int(x) for x in out.cpu().tolist())
+    if ticks <= 0:
+        return {"error": "clock probe did not run"}
+    return {"mhz": cycles / ticks * 100.0, "steps": n, "probe_ms": ticks / 1e5,
+            "method": "s_memtime / s_memrealtime on a side stream during back-to-back steps"}
 
 
 def cpu_baseline(w, seconds):
@@ -598,7 +569,7 @@ def measure(name, steps, warmup, reps, cold_mib=0, sclk_seconds=0.0):
                            "tflops_events_median": total / (cev["step"]["median_ms"] * 1e-3) / 1e12}
         del buf
     if sclk_seconds:
-        summary["sclk_mhz"] = sample_sclk(w.step, sclk_seconds)
+        summary["sclk_mhz"] = sample_sclk(w, sclk_seconds)
     return w, sec, times, per_kernel, summary
 
 
@@ -673,6 +644,9 @@ def main():
         "bwd_tflops": summary["bwd_tflops"],
         "cold": summary.get("cold"),
         "sclk_mhz": summary.get("sclk_mhz"),
+        "pct_peak_at_sclk": (100.0 * summary["tflops"] / (PEAK_BF16_TFLOPS * summary["sclk_mhz"]["mhz"] / 2400.0)
+                             if isinstance(summary.get("sclk_mhz"), dict) and "mhz" in summary["sclk_mhz"]
+                             else None),
         "preprocess_GBs": summary.get("preprocess_GBs"),
         "kernels": times,
         "rooflines": per_kernel,

@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     attn_rope_table,
     backward,
     build_id,
+    clock_probe,
     decode,
     decode_workspace_bytes,
     forward,

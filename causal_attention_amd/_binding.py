@@ -77,6 +77,7 @@ SIGNATURES = {
     "attn_status_string": [_I],
     "attn_abi_version": [],
     "attn_build_id": [],
+    "attn_clock_probe": [_P, ctypes.c_ulonglong, _P],
 }
 
 _lib = None
@@ -132,6 +133,12 @@ def load_library(path: str = LIB_PATH, check_build: bool = True) -> ctypes.CDLL:
                 "rebuild it (python -m causal_attention_amd.build or __graft_entry__.build())")
     _lib = lib
     return lib
+
+
+def clock_probe(out, ticks, stream=None):
+    """Enqueue the clock probe: out (device uint64/int64 tensor of 2) receives
+    shader-clock cycles and 100 MHz ticks over about `ticks` ticks."""
+    _check(load_library().attn_clock_probe(_ptr(out, "out"), int(ticks), _stream(stream)))
 
 
 def build_id() -> str:

@@ -9,9 +9,36 @@
 #include "attn_api.h"
 #include "attn_launch.h"
 
+namespace attn {
+
+// One wave: shader-clock cycles (s_memtime) and 100 MHz real-time ticks
+// (s_memrealtime) over at least `ticks` real-time ticks, sleeping between
+// reads; at most 2^24 reads, so it always ends.
+__global__ __launch_bounds__(64) void clock_probe_kernel(unsigned long long *out, unsigned long long ticks) {
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+  unsigned long long r = r0;
+  for (int it = 0; it < (1 << 24) && r - r0 < ticks; ++it) {
+    __builtin_amdgcn_s_sleep(8);
+    r = __builtin_amdgcn_s_memrealtime();
+  }
+  const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+  if (threadIdx.x == 0) {
+    out[0] = c1 - c0;
+    out[1] = r - r0;
+  }
+}
+
+hipError_t launch_clock_probe(unsigned long long *out, unsigned long long ticks, hipStream_t stream) {
+  hipLaunchKernelGGL(clock_probe_kernel, dim3(1), dim3(64), 0, stream, out, ticks);
+  return hipGetLastError();
+}
+
+}  // namespace attn
+
 namespace {
 
-constexpr int kAbiVersion = 180;  // 1.80: grouped-query, decode, RoPE, fp16 inputs, attn_params calls (16-bit outputs,
+constexpr int kAbiVersion = 190;  // 1.90: clock probe; grouped-query, decode, RoPE, fp16 inputs, attn_params calls (16-bit outputs,
                                   // strides), the fused dQ + Delta stage, the build identifier, decode without allocation
 
 #ifndef ATTN_SOURCE_DIGEST
@@ -216,6 +243,12 @@ extern "C" {
 int attn_abi_version(void) { return kAbiVersion; }
 
 const char *attn_build_id(void) { return ATTN_SOURCE_DIGEST; }
+
+int attn_clock_probe(unsigned long long *out, unsigned long long ticks, void *stream) {
+  if (out == nullptr) return ATTN_ERR_NULL;
+  if (ticks == 0) return ATTN_ERR_SHAPE;
+  return to_status(attn::launch_clock_probe(out, ticks, static_cast<hipStream_t>(stream)));
+}
 
 const char *attn_status_string(int status) {
   switch (status) {

@@ -75,5 +75,7 @@ hipError_t launch_bwd_dq_delta(const Args &a);
 // RoPE: the cos/sin table, and the rotation of a.q, a.k into q_rot, k_rot (table a.rope)
 hipError_t launch_rope_table(float *tab, int n_pos, int D, double base, hipStream_t stream);
 hipError_t launch_rope(const Args &a, void *q_rot, void *k_rot);
+// Clock probe (attn_clock_probe): shader cycles and real-time ticks over `ticks`.
+hipError_t launch_clock_probe(unsigned long long *out, unsigned long long ticks, hipStream_t stream);
 
 }  // namespace attn

@@ -359,6 +359,18 @@ int attn_fwd_ex(const attn_params *p, void *stream);
 
 int attn_bwd_ex(const attn_params *p, void *stream);
 
+/*
+ * Measurement helper, not part of the attention path: one wave that reads the
+ * shader-clock counter and the constant 100 MHz real-time counter, sleeps
+ * between reads until `ticks` real-time ticks have passed (or 2^24 reads),
+ * then writes out[0] = shader-clock cycles elapsed and out[1] = real-time
+ * ticks elapsed (out: DEVICE memory, 2 x uint64, caller-owned).  Launched on
+ * a stream of its own while a workload runs, out[0] / out[1] x 100 MHz is
+ * the graphics clock of the chiplet it ran on during the workload.  Errors:
+ * ATTN_ERR_NULL, ATTN_ERR_SHAPE (ticks 0), ATTN_ERR_HIP.
+ */
+int attn_clock_probe(unsigned long long *out, unsigned long long ticks, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *attn_status_string(int status);
 

@@ -31,7 +31,7 @@ def test_header_status_codes_match_binding():
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 180
+    assert lib.attn_abi_version() == 190
 
 
 def test_build_id_is_the_source_digest(lib):
@@ -41,6 +41,11 @@ def test_build_id_is_the_source_digest(lib):
     built = lib.attn_build_id().decode()
     assert re.fullmatch(r"[0-9a-f]{16}", built)
     assert built == source_digest() == ca.build_id()
+
+
+def test_clock_probe_rejects_invalid_arguments(lib):
+    assert lib.attn_clock_probe(None, 100, None) == -1
+    assert lib.attn_clock_probe(FAKE, 0, None) == -2
 
 
 def test_stale_library_is_refused(lib, monkeypatch):
