@@ -156,6 +156,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   const int ntq = (t.seg_end - q_lo + BMQ - 1) / BMQ;  // query tiles per query head
   const int GH = G / SPLIT;                             // query heads per half
   const int ntile = GH * ntq;                           // over the half's heads
+  float staged = 0.f;                                   // this wave's LSE or Delta rows in flight
 
   auto qslot = [&]<int P>() { return lds_cast(P == 0 ? sQ0 : sQ1) + half * BMQ * D; };
   auto oslot = [&]<int P>() { return lds_cast(P == 0 ? sO0 : sO1) + half * BMQ * D; };
@@ -176,13 +177,22 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     const GBuf gdel(delta + rbase, (uint32_t)(t.seg_end * sizeof(float)));
     QTile::issue_at(gq, qslot.template operator()<P>(), QTile::row0_bytes(q0, lq.ss), qoff, kg);
     QTile::issue_at(gdo, oslot.template operator()<P>(), QTile::row0_bytes(q0, ldo.ss), dooff, kg);
-    // 64-row copies of LSE, then of Delta, one per wave
-    if (kg < NVEC / 2) {
-      dma_vec64(glse, lslot.template operator()<P>() + 64 * kg, q0 + 64 * kg, lane);
-    } else if (kg < NVEC) {
-      const int r = 64 * (kg - NVEC / 2);
-      dma_vec64(gdel, dslot.template operator()<P>() + r, q0 + r, lane);
-    }
+    // 64 rows of LSE, then of Delta, one load per wave into a register; the
+    // wave writes them to the slot (as row shifts) before the tile's barrier
+    if (kg < NVEC / 2)
+      staged = glse.load4((uint32_t)(q0 + 64 * kg + lane) * 4u);
+    else if (kg < NVEC)
+      staged = gdel.load4((uint32_t)(q0 + 64 * (kg - NVEC / 2) + lane) * 4u);
+  };
+  // The staged rows enter the tile's slot as the shifts the scores need:
+  // -LSE / scale and -Delta, so that each 32-query block starts its S and dP
+  // accumulators from them (shift_rows) instead of adding them afterwards.
+  const float rscale = 1.0f / scale;
+  auto publish = [&]<int P>() {
+    if (kg < NVEC / 2)
+      lslot.template operator()<P>()[64 * kg + lane] = -staged * rscale;
+    else if (kg < NVEC)
+      dslot.template operator()<P>()[64 * (kg - NVEC / 2) + lane] = -staged;
   };
   issue.template operator()<0>(0);
 
@@ -216,12 +226,21 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   const RowFrag<T, D> rf0(lane);  // row fragments of the same tiles
 
   // One query tile: per 32-query block, S' = Q K^T - LSE/scale and
-  // dP' = dO V^T - Delta as [query][key] blocks (lane c owns key w0 + c; the
-  // per-query shifts enter as a rank-1 product, so no lane needs the shift of
-  // every row it holds), P = exp2(S' c2), dS = P dP', then dV^T += dO^T P and
-  // dK^T += Q^T dS.
-  const typename E::rows_frag ones = E::rows_b(hh);
-  const float rscale = 1.0f / scale;
+  // dP' = dO V^T - Delta as [query][key] blocks (lane c owns key w0 + c), the
+  // accumulators starting from the per-query shifts: element r of a lane's
+  // block is query row 8 (r / 4) + 4 hh + r % 4, so four 16-byte LDS reads of
+  // the shift rows fill it.  Then P = exp2(S' c2), dS = P dP', dV^T += dO^T P
+  // and dK^T += Q^T dS.
+  auto shift_rows = [&](const lds_t<float> *sh, int qb) {
+    f32x16 a;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 v4 = *(const lds_t<f32x4> *)(sh + qb * 32 + 8 * j + 4 * hh);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[4 * j + i] = v4[i];
+    }
+    return a;
+  };
   // Pipelined pair of query blocks (16-bit inputs, D = 64).  Measured on
   // MI355X, backward: ctx 1024 97.8 -> 94.9 us, S = 8192 499 -> 490 us; at
   // D = 32 the second set of score accumulators costs the fourth wave per
@@ -240,8 +259,8 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
       // (below).  A block whose queries all precede this wave's keys is
       // computed with every score masked: P = dS = 0 adds exact zeros.
       auto scores = [&](int qb, f32x16 &sacc, f32x16 &pacc) {
-        E::mma_rows(sacc, E::rows_a(-sl[qb * 32 + c] * rscale, hh), ones);
-        E::mma_rows(pacc, E::rows_a(-sd[qb * 32 + c], hh), ones);
+        sacc = shift_rows(sl, qb);
+        pacc = shift_rows(sd, qb);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           E::mma(sacc, rf(sq, qb, kb), kfrag(kb));
@@ -281,18 +300,12 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
       // within 1 % of each other.)
       f32x16 sa[2], pa[2];
       frag ps[2][4];
-      sa[0] = f32x16{};
-      pa[0] = f32x16{};
       scores(0, sa[0], pa[0]);
       if (masked) mask(0, sa[0]);
 #pragma unroll
       for (int b = 0; b <= QB; ++b) {
         if (b >= 1) accum(b - 1, ps[(b - 1) % 2]);
-        if (b + 1 < QB) {
-          sa[(b + 1) % 2] = f32x16{};
-          pa[(b + 1) % 2] = f32x16{};
-          scores(b + 1, sa[(b + 1) % 2], pa[(b + 1) % 2]);
-        }
+        if (b + 1 < QB) scores(b + 1, sa[(b + 1) % 2], pa[(b + 1) % 2]);
         if (b < QB) {
           soft(sa[b % 2], pa[b % 2], ps[b % 2]);
           // keep block b's softmax in this step: without a use here the
@@ -308,10 +321,8 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     for (int qb = 0; qb < QB; ++qb) {
       // a block whose queries all precede this wave's first key adds nothing
       if (masked && q0 + qb * 32 + 31 < w0) continue;
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
+      f32x16 sacc = shift_rows(sl, qb), pacc = shift_rows(sd, qb);
       mma_priority_hi();
-      E::mma_rows(sacc, E::rows_a(-sl[qb * 32 + c] * rscale, hh), ones);
-      E::mma_rows(pacc, E::rows_a(-sd[qb * 32 + c], hh), ones);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         E::mma(sacc, rf(sq, qb, kb), kfrag(kb));
@@ -343,10 +354,14 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     }
   };
 
-  // Query tile `it` in ring slot P: wait for its copies (this wave's, then
-  // everyone's), request the next tile into the other slot, compute.
+  // Query tile `it` in ring slot P: wait for this wave's copies and staged
+  // rows, write the rows to the slot, cross the barrier (everyone's copies
+  // and rows are then visible), request the next tile into the other slot,
+  // compute.
   auto step = [&]<int P>(int it) {
     wait_vmcnt<0>();
+    publish.template operator()<P>();
+    wait_vmcnt_lgkm0<0>();
     wg_barrier();
     if (it + 1 < ntile) issue.template operator()<1 - P>(it + 1);
     const int q0 = q_lo + (it % ntq) * BMQ;
