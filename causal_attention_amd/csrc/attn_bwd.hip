@@ -87,12 +87,14 @@ __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const OT *__re
 // by two) one iteration ahead; Q and dO are read both as row fragments and,
 // through the transposing load, as Q^T and dO^T.
 //
-// SPLIT = 2 (grouped heads, G even): the workgroup owns 64 keys, and each key
-// group of 32 has two waves, each running the query-tile loop over half of
-// the G query heads with a ring of its own; at the end the second wave hands
-// its partial dK, dV to the first through LDS, which adds them (first half +
-// second half, a fixed order) and stores.  Twice the workgroups of SPLIT = 1
-// for the same keys, so grouped heads fill twice the wave slots.
+// SPLIT = 2 or 4 (grouped heads, G a multiple of SPLIT): the workgroup owns
+// 128 / SPLIT keys, and each key group of 32 has SPLIT waves, each running
+// the query-tile loop over G / SPLIT of the query heads with a ring of its
+// own; at the end the other waves hand their partial dK, dV to the first
+// through LDS, which adds them (in the order of their parts, a fixed order)
+// and stores.  SPLIT times the workgroups of SPLIT = 1 for the same keys, so
+// grouped heads fill more wave slots and each wave's chain of query tiles is
+// SPLIT times shorter.
 template <typename T, typename OT, int D, int BMQ, int MINB, bool DOC, int SPLIT>
 __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dO,
@@ -102,21 +104,23 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     Layout ldk, Layout ldv) {
   constexpr int NW = 4;
   constexpr int NT = NW * kWaveSize;
-  constexpr int NWH = NW / SPLIT;  // waves per half: one per 32-key group
+  constexpr int NWH = NW / SPLIT;  // waves per part: one per 32-key group
   constexpr int BN = NWH * 32;     // keys per workgroup
   constexpr int KB = D / 16;
   constexpr int DB = D / 32;
   constexpr int QB = BMQ / 32;  // 32-query blocks per tile
   using E = Elem<T>;
   using frag = typename E::frag;
-  using QTile = DmaTile<T, BMQ, D, NT / SPLIT, true>;  // copied by the half's waves
-  static_assert(SPLIT == 1 || SPLIT == 2, "one or two halves");
+  using QTile = DmaTile<T, BMQ, D, NT / SPLIT, true>;  // copied by the part's waves
+  static_assert(SPLIT == 1 || SPLIT == 2 || SPLIT == 4, "one, two or four parts");
   static_assert(SPLIT == 1 || DB * 16 * kWaveSize * 4 <= SPLIT * BMQ * D * (int)sizeof(T),
                 "a wave's partial dK (or dV) fits one ring slot");
+  static_assert(SPLIT != 4 || 2 * DB * 16 * kWaveSize * 4 <= SPLIT * BMQ * D * (int)sizeof(T),
+                "a wave's partial dK and dV fit one ring slot");
   constexpr int VROWS = BMQ < 64 ? 64 : BMQ;  // rows of LSE / Delta per slot
-  constexpr int NVEC = 2 * (VROWS / 64);      // 64-row copies of LSE and Delta per tile
-  static_assert(BMQ <= 64 || BMQ % 64 == 0, "LSE / Delta copies move 64 rows at a time");
-  static_assert(NVEC <= NWH, "one LSE or Delta copy per wave");
+  constexpr int NVEC = 2 * (VROWS / 64);      // 64-row loads of LSE and Delta per tile
+  static_assert(BMQ <= 64 || BMQ % 64 == 0, "LSE / Delta loads move 64 rows at a time");
+  constexpr int NPW = (NVEC + NWH - 1) / NWH;  // of them per wave
 
   __shared__ __attribute__((aligned(1024))) T sQ0[SPLIT * BMQ * D];  // [half][row][col]
   __shared__ __attribute__((aligned(1024))) T sQ1[SPLIT * BMQ * D];
@@ -133,8 +137,8 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
 
   const int tid = threadIdx.x;
   const int wave = wave_id();
-  const int half = wave % SPLIT;  // which half of the query heads
-  const int kg = wave / SPLIT;    // which 32 keys; also the wave's index in its half
+  const int half = wave % SPLIT;  // which part of the query heads
+  const int kg = wave / SPLIT;    // which 32 keys; also the wave's index in its part
   const int lane = tid % kWaveSize;
   const int hh = lane / 32;
   const int c = lane % 32;
@@ -154,9 +158,11 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   const int key = w0 + c;
   const int q_lo = t.r_start;  // the first query that sees any of these keys
   const int ntq = (t.seg_end - q_lo + BMQ - 1) / BMQ;  // query tiles per query head
-  const int GH = G / SPLIT;                             // query heads per half
-  const int ntile = GH * ntq;                           // over the half's heads
-  float staged = 0.f;                                   // this wave's LSE or Delta rows in flight
+  const int GH = G / SPLIT;                             // query heads per part
+  const int ntile = GH * ntq;                           // over the part's heads
+  float staged[NPW];                                    // this wave's LSE or Delta rows in flight
+#pragma unroll
+  for (int i = 0; i < NPW; ++i) staged[i] = 0.f;
 
   auto qslot = [&]<int P>() { return lds_cast(P == 0 ? sQ0 : sQ1) + half * BMQ * D; };
   auto oslot = [&]<int P>() { return lds_cast(P == 0 ? sO0 : sO1) + half * BMQ * D; };
@@ -177,22 +183,31 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     const GBuf gdel(delta + rbase, (uint32_t)(t.seg_end * sizeof(float)));
     QTile::issue_at(gq, qslot.template operator()<P>(), QTile::row0_bytes(q0, lq.ss), qoff, kg);
     QTile::issue_at(gdo, oslot.template operator()<P>(), QTile::row0_bytes(q0, ldo.ss), dooff, kg);
-    // 64 rows of LSE, then of Delta, one load per wave into a register; the
-    // wave writes them to the slot (as row shifts) before the tile's barrier
-    if (kg < NVEC / 2)
-      staged = glse.load4((uint32_t)(q0 + 64 * kg + lane) * 4u);
-    else if (kg < NVEC)
-      staged = gdel.load4((uint32_t)(q0 + 64 * (kg - NVEC / 2) + lane) * 4u);
+    // 64-row loads of LSE, then of Delta, dealt over the part's waves into
+    // registers; each wave writes its rows to the slot (as row shifts) before
+    // the tile's barrier
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+      const int v = kg + i * NWH;
+      if (v < NVEC / 2)
+        staged[i] = glse.load4((uint32_t)(q0 + 64 * v + lane) * 4u);
+      else if (v < NVEC)
+        staged[i] = gdel.load4((uint32_t)(q0 + 64 * (v - NVEC / 2) + lane) * 4u);
+    }
   };
   // The staged rows enter the tile's slot as the shifts the scores need:
   // -LSE / scale and -Delta, so that each 32-query block starts its S and dP
   // accumulators from them (shift_rows) instead of adding them afterwards.
   const float rscale = 1.0f / scale;
   auto publish = [&]<int P>() {
-    if (kg < NVEC / 2)
-      lslot.template operator()<P>()[64 * kg + lane] = -staged * rscale;
-    else if (kg < NVEC)
-      dslot.template operator()<P>()[64 * (kg - NVEC / 2) + lane] = -staged;
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+      const int v = kg + i * NWH;
+      if (v < NVEC / 2)
+        lslot.template operator()<P>()[64 * v + lane] = -staged[i] * rscale;
+      else if (v < NVEC)
+        dslot.template operator()<P>()[64 * (v - NVEC / 2) + lane] = -staged[i];
+    }
   };
   issue.template operator()<0>(0);
 
@@ -415,10 +430,57 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
         }
     }
   }
+  if constexpr (SPLIT == 4) {
+    // One key group; parts 1-3 write their partial dK, dV (lane-major) to a
+    // ring slot each, part 0 adds them in part order and stores.
+    static_assert(NWH == 1, "four parts of one key group");
+    wg_barrier();
+    auto part_buf = [&](int h) {
+      return (lds_t<f32x4> *)lds_cast(h == 1 ? sQ0 : h == 2 ? sQ1 : sO0);
+    };
+    constexpr int kV = DB * 4 * kWaveSize;  // f32x4 offset of dV behind dK
+    if (half != 0 && wave_active) {
+      lds_t<f32x4> *pb = part_buf(half);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 a4, b4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            a4[i] = dkacc[db][4 * g + i];
+            b4[i] = dvacc[db][4 * g + i];
+          }
+          pb[(db * 4 + g) * kWaveSize + lane] = a4;
+          pb[kV + (db * 4 + g) * kWaveSize + lane] = b4;
+        }
+    }
+    wg_barrier();
+    if (half != 0) return;
+    if (wave_active) {
+#pragma unroll
+      for (int h = 1; h < 4; ++h) {
+        const lds_t<f32x4> *pb = part_buf(h);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 a4 = pb[(db * 4 + g) * kWaveSize + lane];
+            const f32x4 b4 = pb[kV + (db * 4 + g) * kWaveSize + lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              dkacc[db][4 * g + i] += a4[i];
+              dvacc[db][4 * g + i] += b4[i];
+            }
+          }
+      }
+    }
+  }
 
   // Each wave stores its keys' rows through ring-slot memory of its own
-  // (store_block_rows): with one half, slot kg once every wave is past its
-  // last tile; with two, the slot its partner's partial sums came through.
+  // (store_block_rows): with one part, slot kg once every wave is past its
+  // last tile; with two, the slot its partner's partial sums came through;
+  // with four, the slot part 1's sums came through (read back already).
   if constexpr (SPLIT == 1) wg_barrier();
   if (!wave_active) return;
   const GBuf gdk(dk + panel_off(ldk, bi, hk), panel_bytes(ldk, t.r_end, D, sizeof(OT)));
@@ -976,7 +1038,9 @@ static hipError_t launch_pre_t(const Args &a) {
 
 template <typename T, typename OT, int D, bool DOC, int SPLIT>
 static hipError_t launch_dkdv_split(const Args &a) {
-  constexpr int BMQ = BwdCfg<T, D>::BMQ;
+  // four parts at D = 64 take 32-query tiles: four 64-row rings would leave
+  // room for one workgroup per CU
+  constexpr int BMQ = (SPLIT == 4 && D == 64) ? 32 : BwdCfg<T, D>::BMQ;
   constexpr int MINB = BwdCfg<T, D>::MINB_DKDV;
   constexpr int BN = 4 * 32 / SPLIT;  // keys per workgroup
   const float c2 = a.scale * kLog2e;
@@ -1022,22 +1086,28 @@ static hipError_t launch_dkdv_pair(const Args &a) {
 // leaves room for one wave per SIMD, wave pairs (two per SIMD); at D = 64 the
 // pairs are slower (LDS for three workgroups per CU, a barrier per 17
 // products).  Grouped heads with an even group size can instead split the
-// group over two waves per key group, which halves the longest workgroup's
-// chain of query tiles.  Measured on MI355X (backward, bf16, D = 128, 12
-// shapes with 2 to 8 K/V heads and S from 1024 to 8192): with 64-key units
-// B * H_kv * ceil(S / 64) >= 1024, two rounds of the pair kernel's resident
-// workgroups on 256 CUs, the pairs are 9-13 % faster than the split; at 512
-// units within 3 % either way; at 256 units 27-29 % slower, the step then
-// waiting on the heads chained in the first key tiles.  Else one wave per
+// group over two (or, G a multiple of four, four) waves per key group, which
+// halves (quarters) the longest workgroup's chain of query tiles.  Measured
+// on MI355X (backward, bf16, D = 128, 12 shapes with 2 to 8 K/V heads and S
+// from 1024 to 8192): with 64-key units B * H_kv * ceil(S / 64) >= 1024, two
+// rounds of the pair kernel's resident workgroups on 256 CUs, the pairs are
+// 9-13 % faster than the two-way split; at 512 units within 3 % either way;
+// at 256 units 27-29 % slower, the step then waiting on the heads chained in
+// the first key tiles.  Four ways against two, B1 H16 S8192 D128: 4 K/V heads
+// 1.68 -> 1.47 ms, 2 heads 1.89 -> 1.56, 1 head 3.40 -> 2.33; B8 H16 S1024
+// D64: 1 K/V head 209 -> 178 us, 2 heads 132 -> 120, but 4 heads (G = 4)
+// 99 -> 109 us, so at D <= 64 four ways only from G = 8.  Else one wave per
 // 32 keys.
 template <typename T, typename OT, int D, bool DOC>
 static hipError_t launch_dkdv_t(const Args &a) {
   if constexpr (sizeof(T) == 2) {
-    const bool even_group = (a.H / a.H_kv) % 2 == 0;
+    const int G = a.H / a.H_kv;
+    const bool even_group = G % 2 == 0;
     if constexpr (D == 128) {
       const int64_t units = (int64_t)a.B * a.H_kv * ((a.S + 63) / 64);
       if (!even_group || units >= 1024) return launch_dkdv_pair<T, OT, D, DOC>(a);
     }
+    if (G % 4 == 0 && (D == 128 || G >= 8)) return launch_dkdv_split<T, OT, D, DOC, 4>(a);
     if (even_group) return launch_dkdv_split<T, OT, D, DOC, 2>(a);
   }
   return launch_dkdv_split<T, OT, D, DOC, 1>(a);

@@ -43,6 +43,12 @@ CASES = [
     ("bf16", 1, 6, 2, 300, 128),   # odd group (G = 3): dK/dV by wave pairs, three heads per key
     ("f16", 1, 9, 3, 257, 128),
     ("bf16", 2, 6, 2, 190, 64),    # odd group at D = 64: one wave per 32 keys
+    # dK/dV split four ways per key group: G a multiple of four at D = 128,
+    # of eight at D <= 64
+    ("bf16", 1, 8, 2, 300, 128),
+    ("bf16", 1, 16, 1, 200, 128),  # multi-query, 16 query heads
+    ("f16", 1, 8, 1, 257, 32),
+    ("bf16", 2, 16, 2, 130, 64),
 ]
 
 
@@ -53,10 +59,12 @@ def test_gqa_parity(dtype, B, H, H_kv, S, D):
     compare(run_hip(x), oracle(x), dtype, tag=f"gqa {dtype} B{B} H{H}/{H_kv} S{S} D{D}")
 
 
-@pytest.mark.parametrize("B,H,H_kv,S", [(4, 16, 8, 2048), (16, 16, 4, 1024), (15, 4, 2, 2048), (16, 4, 2, 2048)])
+@pytest.mark.parametrize("B,H,H_kv,S", [(4, 16, 8, 2048), (16, 16, 4, 1024), (15, 4, 2, 2048), (16, 4, 2, 2048),
+                                         (1, 16, 4, 2048), (1, 16, 1, 1024)])
 def test_gqa_even_group_wave_pairs_sampled(B, H, H_kv, S):
     """Even groups at D = 128 with B * H_kv * ceil(S / 64) >= 1024 64-key units
-    take dK/dV by wave pairs, smaller grids split the group (the last two
+    take dK/dV by wave pairs, smaller grids split the group, two ways or (G a
+    multiple of four, the last two cases) four ways (the third and fourth
     cases sit on either side: 960 and 1024 units).  The oracle checks sampled
     (batch, K/V head) slices: batch entries and K/V heads are independent
     problems with G query heads each."""
@@ -82,7 +90,7 @@ def test_gqa_even_group_wave_pairs_sampled(B, H, H_kv, S):
         compare(got, oracle(xs), "bf16", tag=f"gqa pairs B{B} H{H}/{H_kv} S{S} slice ({b},{j})")
 
 
-@pytest.mark.parametrize("D,H", [(64, 8), (128, 8), (128, 6)])
+@pytest.mark.parametrize("D,H", [(64, 8), (64, 16), (128, 8), (128, 6)])
 def test_gqa_packed_documents(D, H):
     cu = make_cu_seqlens(700, 1, 260, 41 + D)
     log(f"[gqa] packed ({len(cu) - 1} docs) D{D} H{H}/2")
