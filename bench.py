@@ -11,12 +11,14 @@ five products of the FlashAttention-2 accounting), divided by the measured
 time.  One JSON line is printed.
 
 Timing.  W untimed steps, then exactly K steps between two device
-synchronisations: `ms_per_step` and `value` come from the host clock around
-those K steps.  Inside the same loop HIP events on the launch stream bracket
-every step's forward and backward, giving per-iteration median, p10 and p90
-(`events_ms`).  A second loop writes a 512 MiB buffer before each step (more
-than the 256 MiB last-level cache holds), so every step starts cold
-(`cold`).  The graphics clock is measured while steps run back to back
+synchronisations with nothing else on the stream: `ms_per_step` and `value`
+come from the host clock around those K steps.  A second loop of K steps
+records HIP events on the launch stream around every step's forward and
+backward, giving per-iteration median, p10 and p90 (`events_ms`; its own
+host-clock time per step, which includes the event records, is
+`ms_per_step_with_events`).  A third loop writes a 512 MiB buffer before
+each step (more than the 256 MiB last-level cache holds), so every step
+starts cold (`cold`).  The graphics clock is measured while steps run back to back
 (`sclk_mhz`: the library's clock probe on a side stream).
 
 Besides the headline workload the line carries:
@@ -182,6 +184,20 @@ class Workload:
             self.step()
         torch.cuda.synchronize()
         return g
+
+    def host_loop(self, steps, warmup):
+        """`warmup` untimed steps, then exactly `steps` steps between two device
+        synchronisations with nothing else on the stream: host-clock seconds
+        per step (the bench line's value)."""
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
 
     def timed_loop(self, steps, warmup, cold=None):
         """`warmup` untimed steps, then exactly `steps` steps between two device
@@ -534,7 +550,8 @@ def measure(name, steps, warmup, reps, cold_mib=0, sclk_seconds=0.0):
     cold-cache loop and the clock samples."""
     import torch
     w = Workload(name)
-    sec, per = w.timed_loop(steps, warmup)
+    sec = w.host_loop(steps, warmup)
+    sec_events, per = w.timed_loop(steps, 3)
     sec_graph = w.graph_seconds(steps, warmup)
     total = w.flops_fwd + w.flops_bwd
     peak = PEAK_BF16_TFLOPS if w.cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -544,7 +561,7 @@ def measure(name, steps, warmup, reps, cold_mib=0, sclk_seconds=0.0):
     tflops = total / sec / 1e12
     summary = {
         "tflops": tflops, "pct_peak": 100.0 * tflops / peak, "ms_per_step": sec * 1e3,
-        "ms_per_step_graph": sec_graph * 1e3,
+        "ms_per_step_graph": sec_graph * 1e3, "ms_per_step_with_events": sec_events * 1e3,
         "events_ms": ev,
         "tflops_events_median": total / (ev["step"]["median_ms"] * 1e-3) / 1e12,
         "fwd_tflops": w.flops_fwd / (ev["fwd"]["median_ms"] * 1e-3) / 1e12,
@@ -640,6 +657,7 @@ def main():
         "events_ms": summary["events_ms"],
         "tflops_events_median": summary["tflops_events_median"],
         "ms_per_step_graph": summary["ms_per_step_graph"],
+        "ms_per_step_with_events": summary["ms_per_step_with_events"],
         "fwd_tflops": summary["fwd_tflops"],
         "bwd_tflops": summary["bwd_tflops"],
         "cold": summary.get("cold"),
