@@ -598,7 +598,7 @@ def main():
         return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
-              "(attention shards by batch and head with no communication; see the design notes)",
+              "(attention shards by batch and head with no communication: run one process per GPU on its share)",
               file=sys.stderr)
         sys.exit(2)
     import torch
