@@ -53,23 +53,30 @@ def _f32(x):
 def attention_model(q, k, v, do, scale, mask_mode=0, cu_seqlens=None, heads=None, fmt="bf16", out16=False):
     """Forward and backward with the 16-bit path's rounding points.
 
-    q, k, v, do: [B, H, S, D] arrays holding input-format values (plain
-    multi-head attention).  fmt: "bf16" or "f16" (the input format), or None
-    for no rounding at all (then the result is the oracle's up to fp32
-    storage of the outputs).  out16: O, dQ, dK, dV stored in fmt instead of
-    fp32 (and Delta taken from that stored O).  heads: list of (b, h), default
-    all.  Returns a dict like the oracle's: o, lse, dq, dk, dv, delta
+    q, do: [B, H, S, D] and k, v: [B, H_kv, S, D] arrays holding input-format
+    values (H_kv dividing H; query head h uses K/V head h // (H / H_kv), and
+    dK, dV sum the group's query heads in fp64 before their one store).
+    fmt: "bf16" or "f16" (the input format), or None for no rounding at all
+    (then the result is the oracle's up to fp32 storage of the outputs).
+    out16: O, dQ, dK, dV stored in fmt instead of fp32 (and Delta taken from
+    that stored O).  heads: list of (b, h), default all (grouped heads need
+    all).  Returns a dict like the oracle's: o, lse, dq, dk, dv, delta
     (float64 arrays; heads not computed are NaN).
     """
     q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
     B, H, S, D = q.shape
+    H_kv = k.shape[1]
+    if H % H_kv or v.shape[1] != H_kv or (heads is not None and H_kv != H):
+        raise ValueError("H_kv must divide H; grouped heads are modelled for all heads at once")
+    G = H // H_kv
     allowed = allowed_mask(S, mask_mode, cu_seqlens)
     store = (lambda x: _rnd(x, fmt)) if out16 and fmt is not None else _f32
-    out = {n: np.full((B, H, S, D), np.nan) for n in ("o", "dq", "dk", "dv")}
+    out = {n: np.full((B, H, S, D), np.nan) for n in ("o", "dq")}
+    out.update({n: np.full((B, H_kv, S, D), np.nan if G == 1 else 0.0) for n in ("dk", "dv")})
     out["lse"] = np.full((B, H, S), np.nan)
     out["delta"] = np.full((B, H, S), np.nan)
     for b, h in (heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]):
-        qh, kh, vh, doh = q[b, h], k[b, h], v[b, h], do[b, h]
+        qh, kh, vh, doh = q[b, h], k[b, h // G], v[b, h // G], do[b, h]
         s = np.where(allowed, scale * (qh @ kh.T), -np.inf)
         m = s.max(axis=1)
         e = np.exp(s - m[:, None])
@@ -84,9 +91,16 @@ def attention_model(q, k, v, do, scale, mask_mode=0, cu_seqlens=None, heads=None
         out["o"][b, h] = o
         out["lse"][b, h] = lse
         out["delta"][b, h] = delta
-        out["dv"][b, h] = store(_rnd(p, fmt).T @ doh)
-        out["dk"][b, h] = store(scale * (ds.T @ qh))
         out["dq"][b, h] = store(scale * (ds @ kh))
+        if G == 1:
+            out["dv"][b, h] = store(_rnd(p, fmt).T @ doh)
+            out["dk"][b, h] = store(scale * (ds.T @ qh))
+        else:
+            out["dv"][b, h // G] += _rnd(p, fmt).T @ doh
+            out["dk"][b, h // G] += scale * (ds.T @ qh)
+    if G > 1:
+        out["dv"] = store(out["dv"])
+        out["dk"] = store(out["dk"])
     return out
 
 

@@ -43,6 +43,23 @@ def test_model_without_rounding_is_the_oracle(mask):
         assert np.max(np.abs(got[n] - r)) <= 2e-6 * max(1.0, float(np.max(np.abs(r)))), n
 
 
+@pytest.mark.parametrize("H,H_kv", [(4, 1), (6, 2)])
+def test_grouped_model_without_rounding_is_the_oracle(H, H_kv):
+    """Grouped heads (K, V with H_kv heads): with the roundings off the model is
+    the oracle's grouped definition, dK and dV summed over each group (a
+    wrong group index or a sum over the wrong heads fails)."""
+    c = AttnConfig("m", B=2, H=H, S=50, D=32, dtype="bf16")
+    x = make_inputs(c, 8, shape=(2, H, 50, 32))
+    x["k"] = np.ascontiguousarray(x["k"][:, :H_kv])
+    x["v"] = np.ascontiguousarray(x["v"][:, :H_kv])
+    ref = _oracle(x)
+    got = _model(x, fmt=None)
+    for n in NAMES + ("delta",):
+        r = ref[n]
+        assert got[n].shape == r.shape, n
+        assert np.max(np.abs(got[n] - r)) <= 2e-6 * max(1.0, float(np.max(np.abs(r)))), n
+
+
 def test_model_rounds_where_the_kernels_do():
     """Turning the rounding on changes O, dQ, dK, dV by bf16-sized amounts and
     leaves LSE at fp32 resolution (it is taken from unrounded weights)."""
