@@ -36,10 +36,19 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
+# Per-source flags.  The backward kernels are scheduled with the compiler's
+# iterative ILP strategy: measured on MI355X (backward, bitwise equal
+# results) ctx 1024 96.3 -> 93.4 us, ctx 512 37.6 -> 36.0, 4 K/V heads at
+# S = 8192 1.47 -> 1.40 ms, packed documents 84.4 -> 85.8; on the forward it
+# made no difference.
+FILE_FLAGS = {
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
 
 def source_digest() -> str:
     """Digest of everything the library is built from: every file under csrc/,
-    the public header and the compiler flags.  The build embeds it in the
+    the public header and the compiler flags (global and per source).  The build embeds it in the
     library (attn_build_id), and the binding refuses a library whose digest
     differs from the tree's, so a stale build never runs in its place."""
     h = hashlib.sha256()
@@ -51,6 +60,8 @@ def source_digest() -> str:
     with open(os.path.join(INCLUDE, "attn_api.h"), "rb") as f:
         h.update(f.read())
     h.update(" ".join(HIPCC_FLAGS).encode())
+    for name in sorted(FILE_FLAGS):
+        h.update((name + ":" + " ".join(FILE_FLAGS[name])).encode())
     return h.hexdigest()[:16]
 
 
@@ -83,7 +94,8 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     tmp = LIB_PATH + ".tmp"
     with tempfile.TemporaryDirectory(prefix="attn_build_") as objdir:
         objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-        cmds = [[hipcc(), *compile_flags, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+        cmds = [[hipcc(), *compile_flags, *FILE_FLAGS.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
         with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
             for f in [ex.submit(_run, c, verbose) for c in cmds]:
                 f.result()
