@@ -4,7 +4,12 @@ outputs, [B, S, H, D] views, empty documents among packed ones) against
 the fp64 oracle, at sizes the oracle finishes quickly.  The cases are drawn
 once from a fixed seed, so a failure names a reproducible case.  16-bit
 cases are bounded by the fixed bounds or by twice the 16-bit rounding
-model's error on the same input, whichever is larger."""
+model's error on the same input, whichever is larger.  With RoPE the
+rotated q, k are checked against the oracle's rotation (one rounding apart
+at most, rarely) and attention against the oracle on those rotated values:
+a last-bit difference in a rotated element moves the scores by up to
+|k| scale ulp, which at unit-scale inputs can pass the fixed LSE bound on
+its own."""
 import numpy as np
 import pytest
 
@@ -12,6 +17,7 @@ from oracle import MASK_CAUSAL, MASK_DOC_CAUSAL, attention_bwd_ref, attention_ro
 from oracle.rope import rope_positions, rope_rotate
 from tests.bf16_model import attention_model
 from tests.gpu_util import TOL, compare, half_ulp, log
+from tests.test_rope_gpu import check_rotated
 
 pytestmark = pytest.mark.gpu
 
@@ -117,22 +123,32 @@ def test_random_option_mix(case):
     ca.attn_bwd_ex(q, k, v, out["o"], do, out["lse"], out["dq"], out["dk"], out["dv"], out["delta"], scale, **kw)
     torch.cuda.synchronize()
     if c["rope"]:
-        ref = attention_rope_ref(x["q"], x["k"], x["v"], x["do"], scale, mode, c["cu"], dtype=c["dtype"])
+        # the rotation against the oracle's (one rounding apart at most,
+        # rarely), then attention against the oracle on the rotated values the
+        # kernels consumed, with dQ, dK turned back to the unrotated inputs
+        rot = attention_rope_ref(x["q"], x["k"], x["v"], x["do"], scale, mode, c["cu"], dtype=c["dtype"])
+        check_rotated(kw["q_rot"], rot["q_rot"], x["q"], c["dtype"], f"random c{c['id']} q_rot")
+        check_rotated(kw["k_rot"], rot["k_rot"], x["k"], c["dtype"], f"random c{c['id']} k_rot")
+        q_in, k_in = (kw[n].float().cpu().numpy().astype(np.float64) for n in ("q_rot", "k_rot"))
+        ref = attention_bwd_ref(q_in, k_in, x["v"], x["do"], scale, mode, c["cu"])
+        pos = rope_positions(S, mode, c["cu"])
+        ref["dq"] = rope_rotate(ref["dq"], pos, inverse=True)
+        ref["dk"] = rope_rotate(ref["dk"], pos, inverse=True)
     else:
+        q_in, k_in = x["q"], x["k"]
         ref = attention_bwd_ref(x["q"], x["k"], x["v"], x["do"], scale, mode, c["cu"])
     out16 = c["dtype"] if c["out16"] else None
     compare(out, ref, c["dtype"], out16=out16, tag=f"random c{c['id']}",
-            bounds=None if c["dtype"] == "f32" else model_bounds(x, ref, c, scale, mode, out16))
+            bounds=None if c["dtype"] == "f32" else model_bounds(x, q_in, k_in, ref, c, scale, mode, out16))
 
 
-def model_bounds(x, ref, c, scale, mode, out16):
+def model_bounds(x, q, k, ref, c, scale, mode, out16):
     """Max-abs bounds of O, dQ, dK, dV for a 16-bit case: the fixed bound, or
     twice the 16-bit rounding model's own error on this input where that is
     larger (unit-scale inputs with groups of 8-16 query heads sum enough
     rounded weights into dK, dV to pass the fixed bound; the model computes
-    the same rounding points on the same values, RoPE inputs rotated as the
-    oracle does)."""
-    q, k = (ref["q_rot"], ref["k_rot"]) if c["rope"] else (x["q"], x["k"])
+    the same rounding points on the same values, q and k the rotated values
+    with RoPE)."""
     m = attention_model(q, k, x["v"], x["do"], scale, mode, c["cu"], fmt=c["dtype"], out16=out16 is not None)
     if c["rope"]:
         pos = rope_positions(q.shape[2], mode, c["cu"])
