@@ -114,7 +114,8 @@ def compare(out, ref, dtype, heads=None, names=("o", "lse", "dq", "dk", "dv", "d
     out16: "bf16" or "f16" when O, dQ, dK, dV are stored in that format; each
     element's bound then grows by its own rounding, half_ulp(ref).
     bounds: optional max-abs bound per output name (O, dQ, dK, dV), replacing
-    the fixed one (derived by the caller from the 16-bit rounding model)."""
+    the fixed one, and optional relative-Frobenius bound under the name plus
+    "_fro" (both derived by the caller from the 16-bit rounding model)."""
     tol = TOL[dtype]
     report = {}
     for name in names:
@@ -141,7 +142,10 @@ def compare(out, ref, dtype, heads=None, names=("o", "lse", "dq", "dk", "dv", "d
                     if g.size else 0.0
                 report[name] = (ma, rf)
             assert ma <= lim, f"{tag} {name}: max-abs {ma:.3e} > {lim}"
-            if tol["rel_fro"] is not None:
-                assert rf <= tol["rel_fro"], f"{tag} {name}: rel-Frobenius {rf:.3e} > {tol['rel_fro']}"
+            fro_lim = tol["rel_fro"]
+            if bounds is not None and name + "_fro" in bounds:
+                fro_lim = bounds[name + "_fro"]
+            if fro_lim is not None:
+                assert rf <= fro_lim, f"{tag} {name}: rel-Frobenius {rf:.3e} > {fro_lim}"
     log(f"{tag} " + " ".join(f"{n}:{m:.2e}/{f:.1e}" for n, (m, f) in report.items()))
     return report

@@ -143,12 +143,14 @@ def test_random_option_mix(case):
 
 
 def model_bounds(x, q, k, ref, c, scale, mode, out16):
-    """Max-abs bounds of O, dQ, dK, dV for a 16-bit case: the fixed bound, or
-    twice the 16-bit rounding model's own error on this input where that is
-    larger (unit-scale inputs with groups of 8-16 query heads sum enough
-    rounded weights into dK, dV to pass the fixed bound; the model computes
-    the same rounding points on the same values, q and k the rotated values
-    with RoPE)."""
+    """Max-abs and relative-Frobenius bounds of O, dQ, dK, dV for a 16-bit
+    case: the fixed bound, or twice the 16-bit rounding model's own error on
+    this input where that is larger.  Unit-scale inputs with groups of 8-16
+    query heads sum enough rounded weights into dK, dV to pass the fixed
+    max-abs bound, and with two or three rows one row whose dP - Delta
+    cancels sets the whole relative-Frobenius error.  The model computes the
+    same rounding points on the same values (q and k the rotated values with
+    RoPE)."""
     m = attention_model(q, k, x["v"], x["do"], scale, mode, c["cu"], fmt=c["dtype"], out16=out16 is not None)
     if c["rope"]:
         pos = rope_positions(q.shape[2], mode, c["cu"])
@@ -161,4 +163,7 @@ def model_bounds(x, q, k, ref, c, scale, mode, out16):
             d = d - half_ulp(np.maximum(np.abs(m[n]), np.abs(ref[n])), out16)
         err = float(np.max(d)) if d.size else 0.0
         bounds[n] = max(TOL[c["dtype"]]["max_abs"], 2.0 * err)
+        r_norm = float(np.linalg.norm(ref[n]))
+        fro = float(np.linalg.norm(m[n] - ref[n])) / r_norm if r_norm > 0 else 0.0
+        bounds[n + "_fro"] = max(TOL[c["dtype"]]["rel_fro"], 2.0 * fro)
     return bounds

@@ -74,7 +74,8 @@ def check_rotated(got, ref, x, dtype, tag):
     pair's magnitude |(x_2i, x_2i+1)| (not of the result, which can cancel to
     near zero), so a 16-bit result may land one unit in the last place away
     where the exact value sits that close to a rounding boundary; such
-    elements must be rare."""
+    elements must be rare: at most one in a thousand, plus two (a tiny input
+    of a few hundred elements can hold one by chance)."""
     g = got.float().cpu().numpy().astype(np.float64)
     d = np.abs(g - ref)
     x = np.asarray(x, dtype=np.float64)
@@ -84,8 +85,9 @@ def check_rotated(got, ref, x, dtype, tag):
         assert np.all(d <= fp32_err), f"{tag}: max excess {float(np.max(d - fp32_err)):.2e}"
         return
     assert np.all(d <= _REL_ULP[dtype] * np.abs(ref) + 2 * fp32_err), f"{tag}: more than one unit in the last place"
-    frac = float(np.mean(d > 0))
-    assert frac <= 1e-3, f"{tag}: {frac:.2e} of the elements differ"
+    n_diff = int(np.count_nonzero(d > 0))
+    frac = n_diff / max(d.size, 1)
+    assert n_diff <= 1e-3 * d.size + 2, f"{tag}: {n_diff} of {d.size} elements differ"
     log(f"{tag}: {frac:.1e} of elements one ulp apart")
 
 
