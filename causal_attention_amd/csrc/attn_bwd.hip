@@ -1014,7 +1014,7 @@ template <typename T, int D> struct BwdCfg {
   static constexpr int MINB_DKDV = 1;
   static constexpr int MINB_DQ = 1;
   // dQ key tile: 32 keys leave the bf16 kernel enough registers for more
-  // waves per SIMD (D = 64: 126 VGPRs, four; D = 128: two instead of one),
+  // waves per SIMD (D = 64: 124 VGPRs, four; D = 128: two instead of one),
   // measured 9 % (context 1024) and 26 % (S = 8192, D = 128) faster; packed
   // documents at D <= 64 ran 12 % faster with 64, and a 32-row tile at D = 32
   // is too small to split over four waves.
@@ -1116,13 +1116,15 @@ static hipError_t launch_dkdv_t(const Args &a) {
 template <typename T, typename OT, int D, bool DOC, bool FUSE_DELTA, int BN = BwdCfg<T, D>::template dq_bn<DOC>()>
 static hipError_t launch_dq_t(const Args &a) {
   // 16-bit causal D = 64: the 32-key tile's registers allow four waves per
-  // SIMD, which only pays when the grid brings them.  A grid that fits three
-  // workgroups per CU (768 on 256 CUs) takes 64-key tiles, whose two blocks
-  // are software-pipelined (160 VGPRs, three waves).  Measured on MI355X,
-  // backward, bitwise equal: 384 workgroups (ctx 512) 35.2 -> 34.0 us, 128
-  // (B2 H8 S1000) 46.6 -> 44.6; at 1024 the 32-key tiles stay 1-4 % ahead.
+  // SIMD, which only pays when the grid brings them.  A grid of fewer than
+  // three workgroups per CU (under 768 on 256 CUs) takes 64-key tiles, whose
+  // two blocks are software-pipelined (170 VGPRs, two waves per SIMD).
+  // Measured on MI355X, backward, 64-key against 32-key tiles (the choice
+  // does not change the results): 256 workgroups (B2 H16 S1024) 48.2 against
+  // 53.2 us, 384 (ctx 512) 36.8 / 39.0, 512 (B1 H16 S4096) 157.7 / 174.6; at
+  // 768 (B32 H6 S512) 57.8 / 54.6 and at 1024 the 32-key tiles lead.
   if constexpr (sizeof(T) == 2 && D == 64 && !DOC && BN == 32) {
-    if ((int64_t)a.B * a.H * ((a.S + 127) / 128) <= 768)
+    if ((int64_t)a.B * a.H * ((a.S + 127) / 128) < 768)
       return launch_dq_t<T, OT, D, DOC, FUSE_DELTA, 64>(a);
   }
   constexpr int MINB = BwdCfg<T, D>::MINB_DQ;

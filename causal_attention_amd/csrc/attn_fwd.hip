@@ -14,7 +14,7 @@
 //    attn_device.h).  K is read from LDS as (swizzled) row fragments; V is
 //    read through the transposing LDS load from a swizzled row-major tile.
 //  * No software pipeline inside a wave: at D = 64 the kernel needs about
-//    120 VGPRs, so four workgroups share a CU and the hardware overlaps one
+//    122 VGPRs, so four workgroups share a CU and the hardware overlaps one
 //    wave's exponentials with another wave's matrix-core work.
 //  * K and V tiles arrive by direct global->LDS copies into two-slot rings,
 //    requested one iteration before use, with one barrier per tile.

@@ -37,8 +37,10 @@
  *
  * Ownership.  Every pointer except where noted is a DEVICE pointer on the
  * current HIP device, allocated and owned by the caller.  The library never
- * allocates, frees, copies between host and device or synchronises; it keeps
- * no state between calls and is safe to call from several threads.
+ * allocates, frees, copies between host and device or synchronises, and it is
+ * safe to call from several threads.  It keeps no state between calls, with
+ * one exception: attn_decode_noalloc's static device buffer and that buffer's
+ * per-device address, looked up once under a lock.
  * Outputs are fully overwritten (no accumulation, no need to clear them first).
  *
  * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls
