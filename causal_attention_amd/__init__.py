@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     attn_rope_table,
     backward,
     build_id,
+    bwd_workspace_bytes,
     clock_probe,
     decode,
     decode_workspace_bytes,

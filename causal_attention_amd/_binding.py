@@ -64,6 +64,9 @@ SIGNATURES = {
     "attn_bwd_dq_delta": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
     "attn_fwd_gqa": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
     "attn_bwd_gqa": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P],
+    "attn_bwd_gqa_workspace_bytes": [_I, _I, _I, _I, _I, _I, _I, _I, _I],
+    "attn_bwd_gqa_ws": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _P,
+                        ctypes.c_size_t, _P],
     "attn_decode_workspace_bytes": [_I, _I, _I, _I, _I],
     "attn_decode": [_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _I, _F, _I, _I, _P],
     "attn_decode_noalloc": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P],
@@ -123,7 +126,8 @@ def load_library(path: str = LIB_PATH, check_build: bool = True) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = {"attn_status_string": ctypes.c_char_p, "attn_build_id": ctypes.c_char_p,
-                      "attn_decode_workspace_bytes": ctypes.c_size_t}.get(name, ctypes.c_int)
+                      "attn_decode_workspace_bytes": ctypes.c_size_t,
+                      "attn_bwd_gqa_workspace_bytes": ctypes.c_size_t}.get(name, ctypes.c_int)
     if check_build:
         from .build import source_digest
         built, want = lib.attn_build_id().decode(), source_digest()
@@ -246,10 +250,22 @@ def attn_fwd(q, k, v, o, lse, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None
         _check(lib.attn_fwd_gqa(*ptrs, B, H, H_kv, *tail))
 
 
+def bwd_workspace_bytes(B, H, H_kv, S, D, dtype, mask_mode=ATTN_MASK_CAUSAL, n_seqs=0, max_seqlen=0):
+    """Bytes of workspace with which attn_bwd (attn_bwd_gqa_ws) splits grouped
+    heads' dK/dV step (0: the split does not apply).  dtype: a torch dtype."""
+    torch = _torch()
+    code = {torch.float32: ATTN_DTYPE_F32, torch.bfloat16: ATTN_DTYPE_BF16, torch.float16: ATTN_DTYPE_F16}[dtype]
+    return int(load_library().attn_bwd_gqa_workspace_bytes(int(B), int(H), int(H_kv), int(S), int(D),
+                                                           int(mask_mode), int(n_seqs), int(max_seqlen), code))
+
+
 def attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None,
-             n_seqs=None, max_seqlen=None, stream=None):
+             n_seqs=None, max_seqlen=None, stream=None, workspace=None):
     """Enqueue the backward: dq [B,H,S,D], dk, dv [B,H_kv,S,D] fp32; delta [B,H,S] fp32
-    workspace.  k and v may have fewer heads than q (attn_bwd_gqa)."""
+    workspace.  k and v may have fewer heads than q (attn_bwd_gqa).  workspace:
+    a device tensor of at least bwd_workspace_bytes(...) bytes, or None; when
+    given, the call is attn_bwd_gqa_ws (grouped heads' dK/dV split into parts
+    where that applies)."""
     torch = _torch()
     lib = load_library()
     B, H, H_kv, S, D, dt = _qkv_info(q, k, v)
@@ -262,7 +278,11 @@ def attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode=ATTN_MASK_
             _ptr(dk, "dk", (B, H_kv, S, D), f32, dev), _ptr(dv, "dv", (B, H_kv, S, D), f32, dev),
             _ptr(delta, "delta", (B, H, S), f32, dev))
     tail = (S, D, float(scale), int(mask_mode), cu, ns, ms, dt, _stream(stream))
-    if H_kv == H:
+    if workspace is not None:
+        ws = _ptr(workspace, "workspace", device=dev)
+        nbytes = workspace.numel() * workspace.element_size()
+        _check(lib.attn_bwd_gqa_ws(*ptrs, B, H, H_kv, *tail[:-1], ws, nbytes, tail[-1]))
+    elif H_kv == H:
         _check(lib.attn_bwd(*ptrs, B, H, *tail))
     else:
         _check(lib.attn_bwd_gqa(*ptrs, B, H, H_kv, *tail))
@@ -557,7 +577,16 @@ def backward(q, k, v, o, dO, lse, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=
     dv = torch.empty_like(dk)
     delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     if o.dtype == torch.float32:
-        attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode, cu_seqlens, None, max_seqlen, stream)
+        ws = None
+        if k.shape[1] != H and q.is_contiguous() and k.is_contiguous() and v.is_contiguous():
+            doc = mask_mode == ATTN_MASK_DOC_CAUSAL and cu_seqlens is not None and max_seqlen is not None
+            n_seqs = cu_seqlens.numel() - 1 if doc else 0
+            ms = int(max_seqlen) if doc else 0
+            nbytes = bwd_workspace_bytes(B, H, k.shape[1], S, D, q.dtype, mask_mode, n_seqs, ms)
+            if nbytes > 0:
+                ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode, cu_seqlens, None, max_seqlen, stream,
+                 workspace=ws)
     else:
         attn_bwd_ex(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode, cu_seqlens, None, max_seqlen,
                     stream=stream)

@@ -38,7 +38,7 @@ hipError_t launch_clock_probe(unsigned long long *out, unsigned long long ticks,
 
 namespace {
 
-constexpr int kAbiVersion = 190;  // 1.90: clock probe; grouped-query, decode, RoPE, fp16 inputs, attn_params calls (16-bit outputs,
+constexpr int kAbiVersion = 191;  // 1.91: grouped-head backward with a workspace; 1.90: clock probe; grouped-query, decode, RoPE, fp16 inputs, attn_params calls (16-bit outputs,
                                   // strides), the fused dQ + Delta stage, the build identifier, decode without allocation
 
 #ifndef ATTN_SOURCE_DIGEST
@@ -196,11 +196,13 @@ hipError_t dq_delta_stage(const attn::Args &a) {
 
 // Whole backward (optionally with RoPE gradients turned back in the dQ and dK
 // epilogues): argument checks, then the kernels on one stream.
+// with_ws: the caller passed a workspace (attn_bwd_gqa_ws), which the
+// grouped-head parts path uses where it applies (attn::dkdv_parts).
 int bwd_all(const void *q, const void *k, const void *v, const void *o, const void *dO, const float *lse,
                    void *dq, void *dk, void *dv, float *delta, bool with_rope, const float *rope, int rope_npos,
                    int B, int H, int H_kv, int S, int D, float scale, int mask_mode, const int32_t *cu_seqlens,
                    int n_seqs, int max_seqlen, int dtype, int out_dtype, const int64_t (*strides)[3],
-                   void *stream) {
+                   void *stream, bool with_ws = false, void *ws = nullptr, size_t ws_bytes = 0) {
   int st = check_common(B, H, S, D, dtype);
   if (st != ATTN_OK) return st;
   if ((st = check_out(dtype, out_dtype)) != ATTN_OK) return st;
@@ -231,8 +233,11 @@ int bwd_all(const void *q, const void *k, const void *v, const void *o, const vo
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
+  const size_t need = with_ws ? attn::dkdv_workspace_bytes(a) : 0;
+  if (need > 0 && (ws == nullptr || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 16 != 0))
+    return ATTN_ERR_WORKSPACE;
   hipError_t e = dq_delta_stage(a);
-  if (e == hipSuccess) e = attn::launch_bwd_dkdv(a);
+  if (e == hipSuccess) e = need > 0 ? attn::launch_bwd_dkdv_parts(a, static_cast<float *>(ws)) : attn::launch_bwd_dkdv(a);
   return to_status(e);
 }
 
@@ -263,7 +268,7 @@ const char *attn_status_string(int status) {
     case ATTN_ERR_UNIMPLEMENTED: return "valid request that this library does not implement";
     case ATTN_ERR_SCALE: return "scale must be finite and > 0";
     case ATTN_ERR_HEADS: return "H_kv must divide H (1 <= H_kv <= H)";
-    case ATTN_ERR_WORKSPACE: return "workspace NULL or smaller than attn_decode_workspace_bytes()";
+    case ATTN_ERR_WORKSPACE: return "workspace NULL, not 16-byte aligned, or smaller than its *_workspace_bytes() size";
     case ATTN_ERR_ROPE: return "RoPE table NULL or shorter than the positions (S, or max_seqlen for documents), or base not finite and > 0";
     case ATTN_ERR_STRIDE: return "strides: batch and head >= 0, sequence >= D, panel extent < 2^31 bytes";
     case ATTN_ERR_SCRATCH: return "attn_decode_noalloc: the key split needs more than ATTN_DECODE_SCRATCH_BYTES (16 MiB) of partials; use attn_decode with a workspace";
@@ -363,6 +368,26 @@ int attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o, co
                  int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype, void *stream) {
   return bwd_all(q, k, v, o, dO, lse, dq, dk, dv, delta, false, nullptr, 0, B, H, H_kv, S, D, scale, mask_mode,
                  cu_seqlens, n_seqs, max_seqlen, dtype, ATTN_DTYPE_F32, nullptr, stream);
+}
+
+size_t attn_bwd_gqa_workspace_bytes(int B, int H, int H_kv, int S, int D, int mask_mode, int n_seqs,
+                                     int max_seqlen, int dtype) {
+  // invalid arguments need nothing here: attn_bwd_gqa_ws reports them
+  static const int32_t any_cu = 0;  // check_mask only tests the pointer
+  if (check_common(B, H, S, D, dtype) != ATTN_OK || check_heads(H, H_kv) != ATTN_OK) return 0;
+  if (check_mask(B, H, S, mask_mode, &any_cu, n_seqs, max_seqlen) != ATTN_OK) return 0;
+  attn::Args a = make_args(B, H, S, D, 1.f, mask_mode, nullptr, n_seqs, max_seqlen, dtype, nullptr);
+  a.H_kv = H_kv;
+  return attn::dkdv_workspace_bytes(a);
+}
+
+int attn_bwd_gqa_ws(const void *q, const void *k, const void *v, const float *o, const void *dO, const float *lse,
+                    float *dq, float *dk, float *dv, float *delta, int B, int H, int H_kv, int S, int D, float scale,
+                    int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen, int dtype,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+  return bwd_all(q, k, v, o, dO, lse, dq, dk, dv, delta, false, nullptr, 0, B, H, H_kv, S, D, scale, mask_mode,
+                 cu_seqlens, n_seqs, max_seqlen, dtype, ATTN_DTYPE_F32, nullptr, stream, true, workspace,
+                 workspace_bytes);
 }
 
 int attn_bwd(const void *q, const void *k, const void *v, const float *o, const void *dO, const float *lse,

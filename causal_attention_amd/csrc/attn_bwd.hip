@@ -525,13 +525,18 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
 // V in registers, so twice as many waves fit.  Query tiles pass through a
 // three-slot ring: at step j the copy into slot (j+1) % 3 starts while the
 // V-wave reads slot j % 3 and the K-wave slot (j-1) % 3.
+//
+// P > 1 parts (grouped heads, with a workspace): the workgroups of one key
+// block and K/V head are P, part p running the loop over query heads
+// p * G/P .. (p+1) * G/P - 1 only and writing its (scaled) dK and dV to
+// dk, dv + p * part_stride; attn_bwd_sum_parts_kernel then adds the parts.
 template <typename T, typename OT, int D, int MINB, bool DOC>
 __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_pair_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, OT *__restrict__ dk,
     OT *__restrict__ dv, int S, float c2, float scale, const int32_t *__restrict__ cu, int ntiles, int n_seqs,
-    int H, int G, const float *__restrict__ rope, int rope_npos, Layout lq, Layout lk, Layout lv, Layout ldo,
-    Layout ldk, Layout ldv) {
+    int H, int G, int P, int64_t part_stride, const float *__restrict__ rope, int rope_npos, Layout lq, Layout lk,
+    Layout lv, Layout ldo, Layout ldk, Layout ldv) {
   static_assert(sizeof(T) == 2, "wave pairs: 16-bit inputs");
   constexpr int NW = 4;
   constexpr int NT = NW * kWaveSize;
@@ -569,12 +574,16 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_pair_kernel(
   const int lane = tid % kWaveSize;
   const int hh = lane / 32;
   const int c = lane % 32;
-  // t.head is a key/value head; its G query heads are qh0 .. qh0 + G - 1, and
-  // dK, dV sum over all of them (the query-tile loop runs over the group).
+  // t.head / P is a key/value head; its G query heads are hk * G .. hk * G +
+  // G - 1 of batch entry bi, and dK, dV sum over all of them (the
+  // query-tile loop runs over the group, or over part t.head % P of it).
   const int Hkv = H / G;
-  const int bi = t.head / Hkv;
-  const int hk = t.head % Hkv;
-  const int qh0 = bi * H + hk * G;
+  const int part = t.head % P;
+  const int GP = G / P;
+  const int bi = t.head / P / Hkv;
+  const int hk = t.head / P % Hkv;
+  const int hq0 = hk * G + part * GP;
+  const int qh0 = bi * H + hq0;
 
   const int w0 = t.r_start + kg * 32;  // first key of this wave
   const bool wave_active = w0 < t.r_end;
@@ -582,7 +591,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_pair_kernel(
   const int key = w0 + c;
   const int q_lo = t.r_start;  // the first query that sees any of these keys
   const int ntq = (t.seg_end - q_lo + BMQ - 1) / BMQ;  // query tiles per query head
-  const int ntile = G * ntq;                            // over the whole group
+  const int ntile = GP * ntq;                           // over the group (or this part of it)
 
   auto qslot = [&]<int P>() { return lds_cast(P == 0 ? sQ0 : P == 1 ? sQ1 : sQ2); };
   auto oslot = [&]<int P>() { return lds_cast(P == 0 ? sO0 : P == 1 ? sO1 : sO2); };
@@ -597,8 +606,8 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_pair_kernel(
     const size_t rbase = (size_t)(qh0 + g) * S;
     // Queries past the segment read as zeros (Q, dO, LSE, Delta all 0): their
     // P is 1 but dO and Q are 0, so they add nothing to dV or dK.
-    const GBuf gq(q + panel_off(lq, bi, hk * G + g), panel_bytes(lq, t.seg_end, D, sizeof(T)));
-    const GBuf gdo(dO + panel_off(ldo, bi, hk * G + g), panel_bytes(ldo, t.seg_end, D, sizeof(T)));
+    const GBuf gq(q + panel_off(lq, bi, hq0 + g), panel_bytes(lq, t.seg_end, D, sizeof(T)));
+    const GBuf gdo(dO + panel_off(ldo, bi, hq0 + g), panel_bytes(ldo, t.seg_end, D, sizeof(T)));
     const GBuf glse(lse + rbase, (uint32_t)(t.seg_end * sizeof(float)));
     const GBuf gdel(delta + rbase, (uint32_t)(t.seg_end * sizeof(float)));
     QTile::issue_at(gq, qslot.template operator()<P>(), QTile::row0_bytes(q0, lq.ss), qoff, wave);
@@ -723,7 +732,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_pair_kernel(
   static_assert(NW == 4 && BMQ * D * sizeof(T) >= 4096, "one 4 KB slot per wave");
   wg_barrier();
   if (!wave_active) return;
-  OT *out = vwave ? dv : dk;
+  OT *out = (vwave ? dv : dk) + part * part_stride;
   const Layout &lout = vwave ? ldv : ldk;
   const GBuf gout(out + panel_off(lout, bi, hk), panel_bytes(lout, t.r_end, D, sizeof(OT)));
   const float osc = vwave ? 1.0f : scale;
@@ -1061,24 +1070,30 @@ static hipError_t launch_dkdv_split(const Args &a) {
   return hipGetLastError();
 }
 
+// P parts: the outputs are dk_out, dv_out (P fp32 partial sets part_stride
+// elements apart, contiguous [B, H_kv, S, D] each) instead of a.dk, a.dv.
 template <typename T, typename OT, int D, bool DOC>
-static hipError_t launch_dkdv_pair(const Args &a) {
+static hipError_t launch_dkdv_pair(const Args &a, int P = 1, OT *dk_out = nullptr, OT *dv_out = nullptr,
+                                   int64_t part_stride = 0) {
   constexpr int BN = 64;  // keys per workgroup
   const float c2 = a.scale * kLog2e;
   dim3 grid;
   int ntiles;
   if (DOC) {
     ntiles = (a.max_seqlen + BN - 1) / BN;
-    grid = dim3(ntiles * a.n_seqs * a.H_kv);
+    grid = dim3(ntiles * a.n_seqs * a.H_kv * P);
   } else {
     ntiles = (a.S + BN - 1) / BN;
-    grid = dim3(ntiles * a.B * a.H_kv);
+    grid = dim3(ntiles * a.B * a.H_kv * P);
   }
+  Layout ldk = a.ldk, ldv = a.ldv;
+  if (P > 1) ldk = ldv = Layout{(int64_t)a.H_kv * a.S * a.D, (int64_t)a.S * a.D, a.D};
   hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<T, OT, D, 1, DOC>), grid, dim3(256), 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
-                     static_cast<const T *>(a.dO), a.lse_in, a.delta_in, static_cast<OT *>(a.dk),
-                     static_cast<OT *>(a.dv), a.S, c2, a.scale, a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv,
-                     a.rope, a.rope_npos, a.lq, a.lk, a.lv, a.ldo, a.ldk, a.ldv);
+                     static_cast<const T *>(a.dO), a.lse_in, a.delta_in,
+                     P > 1 ? dk_out : static_cast<OT *>(a.dk), P > 1 ? dv_out : static_cast<OT *>(a.dv), a.S, c2,
+                     a.scale, a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv, P, part_stride, a.rope,
+                     a.rope_npos, a.lq, a.lk, a.lv, a.ldo, ldk, ldv);
   return hipGetLastError();
 }
 
@@ -1199,6 +1214,67 @@ hipError_t launch_bwd_dkdv(const Args &a) {
     case 2: return a.out16 ? launch_dkdv_dt<f16, f16>(a) : launch_dkdv_dt<f16, float>(a);
     default: return launch_dkdv_dt<float, float>(a);
   }
+}
+
+// Grouped heads with a workspace (attn_bwd_gqa_ws).  At D = 128 the wave
+// pairs chain a K/V head's whole group of query heads through each key
+// block, and with few K/V heads their grid is small: fewer than 1024 64-key
+// units leave the step waiting on the first key blocks' chains.  The parts
+// path gives each (key block, K/V head) P workgroups, part p running G/P of
+// the group's heads and writing its dK, dV to the workspace; then
+// attn_bwd_sum_parts_kernel adds the P sets in part order (deterministic).
+// P is the smallest divisor of G that brings the grid to 1024 units, else G.
+// 16-bit inputs, fp32 contiguous outputs, no RoPE; 0 where it does not apply.
+int dkdv_parts(const Args &a) {
+  if (!a.half() || a.out16 || a.D != 128 || a.rope != nullptr) return 0;
+  const int G = a.H / a.H_kv;
+  if (G % 2 != 0) return 0;
+  const int64_t units = a.doc ? (int64_t)a.n_seqs * a.H_kv * ((a.max_seqlen + 63) / 64)
+                              : (int64_t)a.B * a.H_kv * ((a.S + 63) / 64);
+  if (units >= 1024) return 0;
+  for (int p = 2; p < G; ++p)
+    if (G % p == 0 && units * p >= 1024) return p;
+  return G;
+}
+
+size_t dkdv_workspace_bytes(const Args &a) {
+  const int P = dkdv_parts(a);
+  return P == 0 ? 0 : (size_t)P * 2 * a.B * a.H_kv * a.S * a.D * sizeof(float);
+}
+
+// out[i] = ws[0][i] + ws[1][i] + ... + ws[P-1][i], in that order, over the
+// n4 float4s of dK (parts 0 .. P-1 of the workspace) and then of dV (parts
+// P .. 2P-1).
+__global__ __launch_bounds__(256) void attn_bwd_sum_parts_kernel(const f32x4 *__restrict__ ws, f32x4 *__restrict__ dk,
+                                                                  f32x4 *__restrict__ dv, int P, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 * n4) return;
+  const bool second = i >= n4;
+  const int64_t j = second ? i - n4 : i;
+  const f32x4 *src = ws + (second ? (int64_t)P * n4 : 0) + j;
+  f32x4 acc = src[0];
+  for (int p = 1; p < P; ++p) acc += src[(int64_t)p * n4];
+  (second ? dv : dk)[j] = acc;
+}
+
+hipError_t launch_bwd_dkdv_parts(const Args &a, float *ws) {
+  const int P = dkdv_parts(a);
+  if (P == 0) return launch_bwd_dkdv(a);
+  const int64_t n = (int64_t)a.B * a.H_kv * a.S * a.D;  // elements of dK (and of dV)
+  float *wk = ws, *wv = ws + P * n;
+  hipError_t e;
+  if (a.dtype == 1)
+    e = a.doc ? launch_dkdv_pair<bf16, float, 128, true>(a, P, wk, wv, n)
+              : launch_dkdv_pair<bf16, float, 128, false>(a, P, wk, wv, n);
+  else
+    e = a.doc ? launch_dkdv_pair<f16, float, 128, true>(a, P, wk, wv, n)
+              : launch_dkdv_pair<f16, float, 128, false>(a, P, wk, wv, n);
+  if (e != hipSuccess) return e;
+  const int64_t n4 = n / 4;
+  hipLaunchKernelGGL(attn_bwd_sum_parts_kernel, dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256), 0, a.stream,
+                     reinterpret_cast<const f32x4 *>(ws), static_cast<f32x4 *>(a.dk), static_cast<f32x4 *>(a.dv), P,
+                     n4);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq(const Args &a) {

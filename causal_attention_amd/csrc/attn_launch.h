@@ -69,6 +69,12 @@ size_t decode_scratch_bytes();
 hipError_t launch_fwd(const Args &a);
 hipError_t launch_bwd_preprocess(const Args &a);
 hipError_t launch_bwd_dkdv(const Args &a);
+// Grouped heads with a workspace: the number of parts the dK/dV step splits
+// each group into (0: the parts path does not apply), the workspace it needs,
+// and the step itself (launch_bwd_dkdv where no parts apply).
+int dkdv_parts(const Args &a);
+size_t dkdv_workspace_bytes(const Args &a);
+hipError_t launch_bwd_dkdv_parts(const Args &a, float *ws);
 hipError_t launch_bwd_dq(const Args &a);
 // 16-bit inputs only: dQ that also computes Delta from O and dO (written to a.delta)
 hipError_t launch_bwd_dq_delta(const Args &a);

@@ -79,7 +79,7 @@ typedef enum attn_status {
   ATTN_ERR_UNIMPLEMENTED = -8, /* valid request the library does not implement     */
   ATTN_ERR_SCALE = -9,         /* scale not finite or not > 0                      */
   ATTN_ERR_HEADS = -10,        /* H_kv not a divisor of H (grouped-query calls)    */
-  ATTN_ERR_WORKSPACE = -11,    /* decode workspace missing or too small            */
+  ATTN_ERR_WORKSPACE = -11,    /* workspace missing, misaligned or too small       */
   ATTN_ERR_ROPE = -12,         /* RoPE table NULL or shorter than the positions,
                                   or base not finite and > 0                       */
   ATTN_ERR_STRIDE = -13,       /* attn_params strides out of range                 */
@@ -176,6 +176,37 @@ int attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o,
                  float *delta, int B, int H, int H_kv, int S, int D, float scale,
                  int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen,
                  int dtype, void *stream);
+
+/*
+ * attn_bwd_gqa with a workspace, for few key/value heads at long context.
+ * dK and dV of a key/value head sum over its G = H / H_kv query heads; the
+ * plain call runs the G heads one after the other through each key block,
+ * so with few key/value heads few, long chains of work set the time.  Given
+ * a workspace, the call splits each group into P parts of G / P heads run
+ * side by side; each part writes its dK and dV into the workspace, then
+ * the parts are added in part order (deterministic, bitwise reproducible;
+ * rounded differently from attn_bwd_gqa, which sums the heads in one chain).
+ * The split applies to 16-bit inputs at D = 128 with an even group size and
+ * fewer than 1024 blocks of 64 keys (B * H_kv * ceil(S / 64), or n_seqs *
+ * H_kv * ceil(max_seqlen / 64) for packed documents).
+ * attn_bwd_gqa_workspace_bytes returns the bytes the split needs for these
+ * arguments: 2 * P * B * H_kv * S * D * 4, or 0 where the split does not
+ * apply (and for invalid arguments). With 0 bytes, workspace may be NULL
+ * and the call is exactly attn_bwd_gqa.
+ * workspace: caller-owned DEVICE memory, 16-byte aligned, of at least that
+ * many bytes. Its contents on return are unspecified. It must not overlap
+ * the other arguments. Arguments and errors as attn_bwd_gqa, plus
+ * ATTN_ERR_WORKSPACE if the workspace is needed and is NULL, misaligned or
+ * too small.
+ */
+size_t attn_bwd_gqa_workspace_bytes(int B, int H, int H_kv, int S, int D, int mask_mode,
+                                    int n_seqs, int max_seqlen, int dtype);
+
+int attn_bwd_gqa_ws(const void *q, const void *k, const void *v, const float *o,
+                    const void *dO, const float *lse, float *dq, float *dk, float *dv,
+                    float *delta, int B, int H, int H_kv, int S, int D, float scale,
+                    int mask_mode, const int32_t *cu_seqlens, int n_seqs, int max_seqlen,
+                    int dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Decode step against a key/value cache (Forge, "Roadmap": KV cache for

@@ -38,9 +38,10 @@ def to_device(x):
     return dev
 
 
-def run_hip(x, dev=None, poison=True, stream=None):
+def run_hip(x, dev=None, poison=True, stream=None, workspace=None):
     """Forward + backward on the GPU.  Outputs are NaN-poisoned first, so an
-    element the kernels fail to write shows up as NaN.  Returns torch tensors."""
+    element the kernels fail to write shows up as NaN.  Returns torch tensors.
+    workspace: passed to the backward (attn_bwd_gqa_ws), or None."""
     import torch
     if dev is None:
         dev = to_device(x)
@@ -56,7 +57,7 @@ def run_hip(x, dev=None, poison=True, stream=None):
     ca.attn_fwd(dev["q"], dev["k"], dev["v"], out["o"], out["lse"], x["scale"], mode, dev["cu"], None,
                 dev["max_seqlen"], stream)
     ca.attn_bwd(dev["q"], dev["k"], dev["v"], out["o"], dev["do"], out["lse"], out["dq"], out["dk"], out["dv"],
-                out["delta"], x["scale"], mode, dev["cu"], None, dev["max_seqlen"], stream)
+                out["delta"], x["scale"], mode, dev["cu"], None, dev["max_seqlen"], stream, workspace=workspace)
     torch.cuda.synchronize()
     return out
 

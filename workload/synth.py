@@ -87,6 +87,9 @@ CONFIGS = {
     # context-1024 shape with 4 key/value heads for the 16 query heads.
     "lm237m_ctx1024_gqa4": AttnConfig("lm237m_ctx1024_gqa4", B=8, H=16, S=1024, D=64, dtype="bf16", H_kv=4,
                                       note="237M-class layer with grouped-query attention"),
+    # ... and the long-context window with 4 key/value heads for its 16 query heads.
+    "long_ctx8192_gqa4": AttnConfig("long_ctx8192_gqa4", B=1, H=16, S=8192, D=128, dtype="bf16", H_kv=4,
+                                    note="long-context window with grouped-query attention"),
     # The same layer with rotary position embedding of q and k (ARK, model
     # table: RoPE; Forge, "Architecture": attention with RoPE), base 10000.
     "lm237m_ctx1024_rope": AttnConfig("lm237m_ctx1024_rope", B=8, H=16, S=1024, D=64, dtype="bf16", rope=True,
