@@ -233,7 +233,10 @@ int bwd_all(const void *q, const void *k, const void *v, const void *o, const vo
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  const size_t need = with_ws ? attn::dkdv_workspace_bytes(a) : 0;
+  // the parts' sum stores dK, dV as 16-byte vectors: with outputs not so
+  // aligned (never the case for whole allocations) the call runs unsplit
+  const bool aligned = reinterpret_cast<uintptr_t>(dk) % 16 == 0 && reinterpret_cast<uintptr_t>(dv) % 16 == 0;
+  const size_t need = with_ws && aligned ? attn::dkdv_workspace_bytes(a) : 0;
   if (need > 0 && (ws == nullptr || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 16 != 0))
     return ATTN_ERR_WORKSPACE;
   hipError_t e = dq_delta_stage(a);

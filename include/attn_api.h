@@ -195,7 +195,9 @@ int attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o,
  * and the call is exactly attn_bwd_gqa.
  * workspace: caller-owned DEVICE memory, 16-byte aligned, of at least that
  * many bytes. Its contents on return are unspecified. It must not overlap
- * the other arguments. Arguments and errors as attn_bwd_gqa, plus
+ * the other arguments. The split also needs dk and dv 16-byte aligned (as
+ * whole allocations are); otherwise the call runs as attn_bwd_gqa and does
+ * not touch the workspace. Arguments and errors as attn_bwd_gqa, plus
  * ATTN_ERR_WORKSPACE if the workspace is needed and is NULL, misaligned or
  * too small.
  */
