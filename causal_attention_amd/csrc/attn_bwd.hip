@@ -100,8 +100,8 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, OT *__restrict__ dk,
     OT *__restrict__ dv, int S, float c2, float scale, const int32_t *__restrict__ cu, int ntiles, int n_seqs,
-    int H, int G, const float *__restrict__ rope, int rope_npos, Layout lq, Layout lk, Layout lv, Layout ldo,
-    Layout ldk, Layout ldv) {
+    int H, int G, int P, int64_t part_stride, const float *__restrict__ rope, int rope_npos, Layout lq, Layout lk,
+    Layout lv, Layout ldo, Layout ldk, Layout ldv) {
   constexpr int NW = 4;
   constexpr int NT = NW * kWaveSize;
   constexpr int NWH = NW / SPLIT;  // waves per part: one per 32-key group
@@ -142,13 +142,19 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   const int lane = tid % kWaveSize;
   const int hh = lane / 32;
   const int c = lane % 32;
-  // t.head is a key/value head; its G query heads are qh0 .. qh0 + G - 1, and
-  // dK, dV sum over all of them (the query-tile loop runs over the group, or
-  // over half of it in each half).
+  // t.head / P is a key/value head; its G query heads are hk*G .. hk*G + G - 1,
+  // and dK, dV sum over all of them (the query-tile loop runs over the
+  // group, or over half of it in each half).  With P > 1 workspace parts
+  // (grouped heads, attn_bwd_gqa_ws) this workgroup takes part t.head % P of
+  // the group, G / P heads from hq0 on, and writes its sums to part p of the
+  // workspace (dk, dv + p * part_stride); attn_bwd_sum_parts_kernel adds them.
   const int Hkv = H / G;
-  const int bi = t.head / Hkv;   // batch entry
-  const int hk = t.head % Hkv;   // key/value head; its query heads are hk*G .. hk*G + G - 1
-  const int qh0 = bi * H + hk * G;  // the first one's (batch, head) index into LSE and Delta
+  const int part = t.head % P;
+  const int GP = G / P;
+  const int bi = t.head / P / Hkv;  // batch entry
+  const int hk = t.head / P % Hkv;  // key/value head
+  const int hq0 = hk * G + part * GP;  // this workgroup's first query head
+  const int qh0 = bi * H + hq0;     // its (batch, head) index into LSE and Delta
   const GBuf gk(k + panel_off(lk, bi, hk), panel_bytes(lk, t.r_end, D, sizeof(T)));
   const GBuf gv(v + panel_off(lv, bi, hk), panel_bytes(lv, t.r_end, D, sizeof(T)));
 
@@ -158,7 +164,7 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   const int key = w0 + c;
   const int q_lo = t.r_start;  // the first query that sees any of these keys
   const int ntq = (t.seg_end - q_lo + BMQ - 1) / BMQ;  // query tiles per query head
-  const int GH = G / SPLIT;                             // query heads per part
+  const int GH = GP / SPLIT;                            // query heads per part
   const int ntile = GH * ntq;                           // over the part's heads
   float staged[NPW];                                    // this wave's LSE or Delta rows in flight
 #pragma unroll
@@ -177,8 +183,8 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
     const size_t rbase = (size_t)(qh0 + g) * S;
     // Queries past the segment read as zeros (Q, dO, LSE, Delta all 0): their
     // P is 1 but dO and Q are 0, so they add nothing to dV or dK.
-    const GBuf gq(q + panel_off(lq, bi, hk * G + g), panel_bytes(lq, t.seg_end, D, sizeof(T)));
-    const GBuf gdo(dO + panel_off(ldo, bi, hk * G + g), panel_bytes(ldo, t.seg_end, D, sizeof(T)));
+    const GBuf gq(q + panel_off(lq, bi, hq0 + g), panel_bytes(lq, t.seg_end, D, sizeof(T)));
+    const GBuf gdo(dO + panel_off(ldo, bi, hq0 + g), panel_bytes(ldo, t.seg_end, D, sizeof(T)));
     const GBuf glse(lse + rbase, (uint32_t)(t.seg_end * sizeof(float)));
     const GBuf gdel(delta + rbase, (uint32_t)(t.seg_end * sizeof(float)));
     QTile::issue_at(gq, qslot.template operator()<P>(), QTile::row0_bytes(q0, lq.ss), qoff, kg);
@@ -483,8 +489,8 @@ __global__ __launch_bounds__(256, MINB) void attn_bwd_dkdv_kernel(
   // with four, the slot part 1's sums came through (read back already).
   if constexpr (SPLIT == 1) wg_barrier();
   if (!wave_active) return;
-  const GBuf gdk(dk + panel_off(ldk, bi, hk), panel_bytes(ldk, t.r_end, D, sizeof(OT)));
-  const GBuf gdv(dv + panel_off(ldv, bi, hk), panel_bytes(ldv, t.r_end, D, sizeof(OT)));
+  const GBuf gdk(dk + part * part_stride + panel_off(ldk, bi, hk), panel_bytes(ldk, t.r_end, D, sizeof(OT)));
+  const GBuf gdv(dv + part * part_stride + panel_off(ldv, bi, hk), panel_bytes(ldv, t.r_end, D, sizeof(OT)));
   // RoPE: this key's table row (keys past the tile end are not stored)
   const float *rrow =
       rope == nullptr ? nullptr : rope + (size_t)min(min(key, t.r_end - 1) - t.seg_start, rope_npos - 1) * D;
@@ -1045,8 +1051,10 @@ static hipError_t launch_pre_t(const Args &a) {
   return hipGetLastError();
 }
 
+// P parts: outputs dk_out, dv_out as in launch_dkdv_pair.
 template <typename T, typename OT, int D, bool DOC, int SPLIT>
-static hipError_t launch_dkdv_split(const Args &a) {
+static hipError_t launch_dkdv_split(const Args &a, int P = 1, OT *dk_out = nullptr, OT *dv_out = nullptr,
+                                    int64_t part_stride = 0) {
   // four parts at D = 64 take 32-query tiles: four 64-row rings would leave
   // room for one workgroup per CU
   constexpr int BMQ = (SPLIT == 4 && D == 64) ? 32 : BwdCfg<T, D>::BMQ;
@@ -1057,16 +1065,19 @@ static hipError_t launch_dkdv_split(const Args &a) {
   int ntiles;
   if (DOC) {
     ntiles = (a.max_seqlen + BN - 1) / BN;
-    grid = dim3(ntiles * a.n_seqs * a.H_kv);
+    grid = dim3(ntiles * a.n_seqs * a.H_kv * P);
   } else {
     ntiles = (a.S + BN - 1) / BN;
-    grid = dim3(ntiles * a.B * a.H_kv);
+    grid = dim3(ntiles * a.B * a.H_kv * P);
   }
+  Layout ldk = a.ldk, ldv = a.ldv;
+  if (P > 1) ldk = ldv = Layout{(int64_t)a.H_kv * a.S * a.D, (int64_t)a.S * a.D, a.D};
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, OT, D, BMQ, MINB, DOC, SPLIT>), grid, dim3(256), 0, a.stream,
                      static_cast<const T *>(a.q), static_cast<const T *>(a.k), static_cast<const T *>(a.v),
-                     static_cast<const T *>(a.dO), a.lse_in, a.delta_in, static_cast<OT *>(a.dk),
-                     static_cast<OT *>(a.dv), a.S, c2, a.scale, a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv,
-                     a.rope, a.rope_npos, a.lq, a.lk, a.lv, a.ldo, a.ldk, a.ldv);
+                     static_cast<const T *>(a.dO), a.lse_in, a.delta_in,
+                     P > 1 ? dk_out : static_cast<OT *>(a.dk), P > 1 ? dv_out : static_cast<OT *>(a.dv), a.S, c2,
+                     a.scale, a.cu_seqlens, ntiles, a.n_seqs, a.H, a.H / a.H_kv, P, part_stride, a.rope,
+                     a.rope_npos, a.lq, a.lk, a.lv, a.ldo, ldk, ldv);
   return hipGetLastError();
 }
 
@@ -1223,14 +1234,18 @@ hipError_t launch_bwd_dkdv(const Args &a) {
 // path gives each (key block, K/V head) P workgroups, part p running G/P of
 // the group's heads and writing its dK, dV to the workspace; then
 // attn_bwd_sum_parts_kernel adds the P sets in part order (deterministic).
+// At D <= 64 the one-wave kernel (128 keys per workgroup) takes the parts
+// where G >= 8: the in-workgroup splits serve smaller groups better (the
+// parts' partial sums cost as much HBM traffic as G / P more K/V heads).
 // P is the smallest divisor of G that brings the grid to 1024 units, else G.
 // 16-bit inputs, fp32 contiguous outputs, no RoPE; 0 where it does not apply.
 int dkdv_parts(const Args &a) {
-  if (!a.half() || a.out16 || a.D != 128 || a.rope != nullptr) return 0;
+  if (!a.half() || a.out16 || a.rope != nullptr) return 0;
   const int G = a.H / a.H_kv;
-  if (G % 2 != 0) return 0;
-  const int64_t units = a.doc ? (int64_t)a.n_seqs * a.H_kv * ((a.max_seqlen + 63) / 64)
-                              : (int64_t)a.B * a.H_kv * ((a.S + 63) / 64);
+  if (a.D == 128 ? G % 2 != 0 : G < 8) return 0;
+  const int bn = a.D == 128 ? 64 : 128;  // keys per workgroup
+  const int64_t units = a.doc ? (int64_t)a.n_seqs * a.H_kv * ((a.max_seqlen + bn - 1) / bn)
+                              : (int64_t)a.B * a.H_kv * ((a.S + bn - 1) / bn);
   if (units >= 1024) return 0;
   for (int p = 2; p < G; ++p)
     if (G % p == 0 && units * p >= 1024) return p;
@@ -1263,12 +1278,22 @@ hipError_t launch_bwd_dkdv_parts(const Args &a, float *ws) {
   const int64_t n = (int64_t)a.B * a.H_kv * a.S * a.D;  // elements of dK (and of dV)
   float *wk = ws, *wv = ws + P * n;
   hipError_t e;
-  if (a.dtype == 1)
-    e = a.doc ? launch_dkdv_pair<bf16, float, 128, true>(a, P, wk, wv, n)
-              : launch_dkdv_pair<bf16, float, 128, false>(a, P, wk, wv, n);
+  const bool bf = a.dtype == 1;
+  if (a.D == 128)
+    e = bf ? (a.doc ? launch_dkdv_pair<bf16, float, 128, true>(a, P, wk, wv, n)
+                    : launch_dkdv_pair<bf16, float, 128, false>(a, P, wk, wv, n))
+           : (a.doc ? launch_dkdv_pair<f16, float, 128, true>(a, P, wk, wv, n)
+                    : launch_dkdv_pair<f16, float, 128, false>(a, P, wk, wv, n));
+  else if (a.D == 64)
+    e = bf ? (a.doc ? launch_dkdv_split<bf16, float, 64, true, 1>(a, P, wk, wv, n)
+                    : launch_dkdv_split<bf16, float, 64, false, 1>(a, P, wk, wv, n))
+           : (a.doc ? launch_dkdv_split<f16, float, 64, true, 1>(a, P, wk, wv, n)
+                    : launch_dkdv_split<f16, float, 64, false, 1>(a, P, wk, wv, n));
   else
-    e = a.doc ? launch_dkdv_pair<f16, float, 128, true>(a, P, wk, wv, n)
-              : launch_dkdv_pair<f16, float, 128, false>(a, P, wk, wv, n);
+    e = bf ? (a.doc ? launch_dkdv_split<bf16, float, 32, true, 1>(a, P, wk, wv, n)
+                    : launch_dkdv_split<bf16, float, 32, false, 1>(a, P, wk, wv, n))
+           : (a.doc ? launch_dkdv_split<f16, float, 32, true, 1>(a, P, wk, wv, n)
+                    : launch_dkdv_split<f16, float, 32, false, 1>(a, P, wk, wv, n));
   if (e != hipSuccess) return e;
   const int64_t n4 = n / 4;
   hipLaunchKernelGGL(attn_bwd_sum_parts_kernel, dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256), 0, a.stream,

@@ -186,9 +186,11 @@ int attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o,
  * side by side; each part writes its dK and dV into the workspace, then
  * the parts are added in part order (deterministic, bitwise reproducible;
  * rounded differently from attn_bwd_gqa, which sums the heads in one chain).
- * The split applies to 16-bit inputs at D = 128 with an even group size and
- * fewer than 1024 blocks of 64 keys (B * H_kv * ceil(S / 64), or n_seqs *
- * H_kv * ceil(max_seqlen / 64) for packed documents).
+ * The split applies to 16-bit inputs with fewer than 1024 dK/dV workgroups
+ * (B * H_kv * ceil(S / bn), or n_seqs * H_kv * ceil(max_seqlen / bn) for
+ * packed documents): at D = 128 with an even group size (bn = 64 keys per
+ * workgroup), at D <= 64 with G >= 8 (bn = 128). P is the smallest divisor
+ * of G that brings the workgroups to 1024, else G.
  * attn_bwd_gqa_workspace_bytes returns the bytes the split needs for these
  * arguments: 2 * P * B * H_kv * S * D * 4, or 0 where the split does not
  * apply (and for invalid arguments). With 0 bytes, workspace may be NULL

@@ -194,9 +194,15 @@ def test_gqa_workspace_size(lib):
     assert f(1, 8, 2, 2048, 128, 0, 0, 0, 1) == 4 * 2 * 1 * 2 * 2048 * 128 * 4
     # packed documents: 4 documents, longest 1000 -> 4 * 4 * 16 = 256 units, P = 4
     assert f(1, 16, 4, 3000, 128, 1, 4, 1000, 1) == 4 * 2 * 1 * 4 * 3000 * 128 * 4
-    # no split: fp32 inputs, D = 64, odd group, plain heads, 1024 units and more
+    # D <= 64: groups of 8 and more, 128-key units: B8 H16/1 S1024 -> 64 units, P = 16
+    assert f(8, 16, 1, 1024, 64, 0, 0, 0, 1) == 16 * 2 * 8 * 1 * 1024 * 64 * 4
+    # B1 H16/2 S8192 D32: 128 units, P = 8
+    assert f(1, 16, 2, 8192, 32, 0, 0, 0, 2) == 8 * 2 * 1 * 2 * 8192 * 32 * 4
+    # no split: fp32 inputs, D = 64 with a group under 8, odd group at D = 128, plain heads,
+    # 1024 units and more
     assert f(1, 16, 4, 8192, 128, 0, 0, 0, 0) == 0
     assert f(1, 16, 4, 8192, 64, 0, 0, 0, 1) == 0
+    assert f(16, 16, 1, 8192, 64, 0, 0, 0, 1) == 0
     assert f(1, 12, 4, 8192, 128, 0, 0, 0, 1) == 0
     assert f(1, 16, 16, 8192, 128, 0, 0, 0, 1) == 0
     assert f(1, 16, 8, 8192, 128, 0, 0, 0, 1) == 0

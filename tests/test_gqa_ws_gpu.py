@@ -1,8 +1,9 @@
 """GPU parity of the grouped-head backward with a workspace (attn_bwd_gqa_ws,
-called through the binding): at D = 128 with 16-bit inputs, an even group of
-G query heads per K/V head and fewer than 1024 blocks of 64 keys, the dK/dV
-step splits each group into P parts run side by side, writes each part's dK,
-dV into the workspace and adds the parts in part order.  Checked against the
+called through the binding): with 16-bit inputs, G query heads per K/V head
+(even at D = 128, at least 8 at D <= 64) and fewer than 1024 dK/dV
+workgroups (64 keys each at D = 128, 128 at D <= 64), the dK/dV step splits
+each group into P parts run side by side, writes each part's dK, dV into
+the workspace and adds the parts in part order.  Checked against the
 fp64 oracle at the usual bounds (tests/gpu_util.py), run to run bitwise, and,
 where the split does not apply, bitwise against attn_bwd_gqa."""
 import numpy as np
@@ -23,6 +24,12 @@ def _gpu():
         pytest.skip("no GPU")
     import causal_attention_amd as ca
     ca.load_library()
+
+
+def units_of(B, H_kv, S, D):
+    """dK/dV workgroups of the unsplit grid: 64 keys each at D = 128, 128 below."""
+    bn = 64 if D == 128 else 128
+    return B * H_kv * ((S + bn - 1) // bn)
 
 
 def parts(G, units):
@@ -50,18 +57,21 @@ def workspace_for(x):
 
 
 CASES = [
-    ("bf16", 1, 8, 2, 600),   # G = 4: four parts
-    ("f16", 1, 16, 4, 300),   # G = 4, fp16 inputs
-    ("bf16", 2, 16, 2, 260),  # G = 8: eight parts, one head each
-    ("bf16", 1, 4, 2, 200),   # G = 2: two parts
-    ("bf16", 3, 12, 2, 190),  # G = 6: six parts (no divisor reaches 1024 units)
+    ("bf16", 1, 8, 2, 600, 128),   # G = 4: four parts
+    ("f16", 1, 16, 4, 300, 128),   # G = 4, fp16 inputs
+    ("bf16", 2, 16, 2, 260, 128),  # G = 8: eight parts, one head each
+    ("bf16", 1, 4, 2, 200, 128),   # G = 2: two parts
+    ("bf16", 3, 12, 2, 190, 128),  # G = 6: six parts (no divisor reaches 1024 units)
+    ("bf16", 1, 8, 1, 300, 64),    # D = 64, G = 8 (multi-query)
+    ("bf16", 2, 16, 1, 333, 64),   # D = 64, G = 16
+    ("f16", 2, 16, 2, 260, 32),    # D = 32, G = 8, fp16 inputs
 ]
 
 
-@pytest.mark.parametrize("dtype,B,H,H_kv,S", CASES)
-def test_parts_against_oracle(dtype, B, H, H_kv, S):
-    D, G = 128, H // H_kv
-    units = B * H_kv * ((S + 63) // 64)
+@pytest.mark.parametrize("dtype,B,H,H_kv,S,D", CASES)
+def test_parts_against_oracle(dtype, B, H, H_kv, S, D):
+    G = H // H_kv
+    units = units_of(B, H_kv, S, D)
     P = parts(G, units)
     x = gqa_inputs(dtype, B, H, H_kv, S, D, 1300 + H + S)
     ws, n = workspace_for(x)
@@ -85,8 +95,8 @@ def test_parts_packed_documents():
     compare(run_hip(x, workspace=ws), oracle(x), "bf16", tag="gqa ws packed H8/2 D128")
 
 
-@pytest.mark.parametrize("B,H,H_kv,S", [(1, 16, 4, 2048), (1, 16, 1, 1024)])
-def test_parts_sampled_groups(B, H, H_kv, S):
+@pytest.mark.parametrize("B,H,H_kv,S,D", [(1, 16, 4, 2048, 128), (1, 16, 1, 1024, 128), (2, 16, 1, 2048, 64)])
+def test_parts_sampled_groups(B, H, H_kv, S, D):
     """Sampled (batch, K/V head) slices against the oracle: each is an
     independent problem with G query heads.  Bounds: the fixed ones, or twice
     the 16-bit rounding model's error on the slice where that is larger (a
@@ -94,10 +104,10 @@ def test_parts_sampled_groups(B, H, H_kv, S):
     the fixed bound: B1 H16/1 S1024, model 1.99e-2, kernel 2.00e-2)."""
     from oracle import MASK_CAUSAL
     from tests.test_random_gpu import model_bounds
-    D, G = 128, H // H_kv
-    x = gqa_inputs("bf16", B, H, H_kv, S, D, 1350 + S)
+    G = H // H_kv
+    x = gqa_inputs("bf16", B, H, H_kv, S, D, 1350 + S + D)
     ws, n = workspace_for(x)
-    log(f"[gqa ws] B{B} H{H}/{H_kv} S{S} D{D}: {parts(G, B * H_kv * ((S + 63) // 64))} parts, {n} bytes")
+    log(f"[gqa ws] B{B} H{H}/{H_kv} S{S} D{D}: {parts(G, units_of(B, H_kv, S, D))} parts, {n} bytes")
     assert n > 0
     out = run_hip(x, workspace=ws)
     for b, j in [(0, 0), (B - 1, H_kv - 1)]:
@@ -112,7 +122,7 @@ def test_parts_sampled_groups(B, H, H_kv, S):
         ref = oracle(xs)
         c = dict(cu=None, dtype="bf16", rope=False)
         bounds = model_bounds(xs, xs["q"], xs["k"], ref, c, xs["scale"], MASK_CAUSAL, None)
-        compare(got, ref, "bf16", tag=f"gqa ws B{B} H{H}/{H_kv} S{S} slice ({b},{j})", bounds=bounds)
+        compare(got, ref, "bf16", tag=f"gqa ws B{B} H{H}/{H_kv} S{S} D{D} slice ({b},{j})", bounds=bounds)
 
 
 def test_parts_long_context_matches_the_chained_sum():
@@ -137,10 +147,11 @@ def test_parts_long_context_matches_the_chained_sum():
 
 
 @pytest.mark.parametrize("dtype,H,H_kv,S,D", [("bf16", 6, 2, 130, 128), ("bf16", 8, 2, 300, 64),
-                                              ("f32", 8, 2, 300, 128), ("bf16", 4, 4, 200, 128)])
+                                              ("f32", 8, 2, 300, 128), ("bf16", 4, 4, 200, 128),
+                                              ("f32", 8, 1, 300, 64)])
 def test_no_split_is_the_plain_call(dtype, H, H_kv, S, D):
-    """Odd groups, D = 64, fp32 inputs and plain heads need no workspace: the
-    call is attn_bwd_gqa, bitwise."""
+    """Odd groups at D = 128, groups under 8 at D <= 64, fp32 inputs and plain
+    heads need no workspace: the call is attn_bwd_gqa, bitwise."""
     x = gqa_inputs(dtype, 1, H, H_kv, S, D, 1370 + H + D)
     ws, n = workspace_for(x)
     log(f"[gqa ws] no split: {dtype} H{H}/{H_kv} S{S} D{D}")
