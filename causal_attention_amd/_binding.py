@@ -49,7 +49,8 @@ class AttnParams(ctypes.Structure):
                 ("dv", _P), ("delta", _P), ("B", _I), ("H", _I), ("H_kv", _I), ("S", _I), ("D", _I),
                 ("scale", _F), ("mask_mode", _I), ("cu_seqlens", _P), ("n_seqs", _I), ("max_seqlen", _I),
                 ("dtype", _I), ("out_dtype", _I), ("rope_table", _P), ("rope_npos", _I), ("q_rot", _P),
-                ("k_rot", _P), ("strides", (ctypes.c_int64 * 3) * 8)]
+                ("k_rot", _P), ("strides", (ctypes.c_int64 * 3) * 8), ("workspace", _P),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 STRIDE_SLOT = {"q": 0, "k": 1, "v": 2, "o": 3, "dO": 4, "dq": 5, "dk": 6, "dv": 7}
@@ -472,9 +473,11 @@ def attn_fwd_ex(q, k, v, o, lse, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=N
 
 
 def attn_bwd_ex(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=None,
-                n_seqs=None, max_seqlen=None, rope_table=None, q_rot=None, k_rot=None, stream=None):
+                n_seqs=None, max_seqlen=None, rope_table=None, q_rot=None, k_rot=None, stream=None, workspace=None):
     """Backward with every option (see attn_fwd_ex).  With RoPE the kernels read
-    q_rot, k_rot (q, k only give shapes); dq, dk, dv in o's dtype."""
+    q_rot, k_rot (q, k only give shapes); dq, dk, dv in o's dtype.  workspace:
+    None, or a device tensor of at least bwd_workspace_bytes(...) bytes with
+    which grouped heads split their dK/dV step."""
     p, (B, H, H_kv, S, D, dev) = _params(q, k, v, o, lse, scale, mask_mode, cu_seqlens, n_seqs, max_seqlen,
                                          rope_table, q_rot, k_rot)
     p.dO = _view(p, dO, "dO", (B, H, S, D), q.dtype, dev)
@@ -482,6 +485,9 @@ def attn_bwd_ex(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode=ATTN_MA
     p.dk = _view(p, dk, "dk", (B, H_kv, S, D), o.dtype, dev)
     p.dv = _view(p, dv, "dv", (B, H_kv, S, D), o.dtype, dev)
     p.delta = _ptr(delta, "delta", (B, H, S), _torch().float32, dev)
+    if workspace is not None:
+        p.workspace = _ptr(workspace, "workspace", device=dev)
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
     _check(load_library().attn_bwd_ex(ctypes.byref(p), _stream(stream)))
 
 
@@ -576,20 +582,20 @@ def backward(q, k, v, o, dO, lse, scale, mask_mode=ATTN_MASK_CAUSAL, cu_seqlens=
     dk = torch.empty(tuple(k.shape), dtype=o.dtype, device=q.device)
     dv = torch.empty_like(dk)
     delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    if o.dtype == torch.float32:
-        ws = None
-        if k.shape[1] != H and q.is_contiguous() and k.is_contiguous() and v.is_contiguous():
-            doc = mask_mode == ATTN_MASK_DOC_CAUSAL and cu_seqlens is not None and max_seqlen is not None
-            n_seqs = cu_seqlens.numel() - 1 if doc else 0
-            ms = int(max_seqlen) if doc else 0
-            nbytes = bwd_workspace_bytes(B, H, k.shape[1], S, D, q.dtype, mask_mode, n_seqs, ms)
-            if nbytes > 0:
-                ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    ws = None
+    if k.shape[1] != H:  # grouped heads: the workspace with which their dK/dV step may split
+        doc = mask_mode == ATTN_MASK_DOC_CAUSAL and cu_seqlens is not None and max_seqlen is not None
+        n_seqs = cu_seqlens.numel() - 1 if doc else 0
+        ms = int(max_seqlen) if doc else 0
+        nbytes = bwd_workspace_bytes(B, H, k.shape[1], S, D, q.dtype, mask_mode, n_seqs, ms)
+        if nbytes > 0:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if o.dtype == torch.float32 and q.is_contiguous() and k.is_contiguous() and v.is_contiguous():
         attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode, cu_seqlens, None, max_seqlen, stream,
                  workspace=ws)
     else:
         attn_bwd_ex(q, k, v, o, dO, lse, dq, dk, dv, delta, scale, mask_mode, cu_seqlens, None, max_seqlen,
-                    stream=stream)
+                    stream=stream, workspace=ws)
     return dq, dk, dv, delta
 
 

@@ -38,7 +38,7 @@ hipError_t launch_clock_probe(unsigned long long *out, unsigned long long ticks,
 
 namespace {
 
-constexpr int kAbiVersion = 191;  // 1.91: grouped-head backward with a workspace; 1.90: clock probe; grouped-query, decode, RoPE, fp16 inputs, attn_params calls (16-bit outputs,
+constexpr int kAbiVersion = 192;  // 1.92: attn_params.workspace; 1.91: grouped-head backward with a workspace; 1.90: clock probe; grouped-query, decode, RoPE, fp16 inputs, attn_params calls (16-bit outputs,
                                   // strides), the fused dQ + Delta stage, the build identifier, decode without allocation
 
 #ifndef ATTN_SOURCE_DIGEST
@@ -233,10 +233,7 @@ int bwd_all(const void *q, const void *k, const void *v, const void *o, const vo
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  // the parts' sum stores dK, dV as 16-byte vectors: with outputs not so
-  // aligned (never the case for whole allocations) the call runs unsplit
-  const bool aligned = reinterpret_cast<uintptr_t>(dk) % 16 == 0 && reinterpret_cast<uintptr_t>(dv) % 16 == 0;
-  const size_t need = with_ws && aligned ? attn::dkdv_workspace_bytes(a) : 0;
+  const size_t need = with_ws ? attn::dkdv_workspace_bytes(a) : 0;
   if (need > 0 && (ws == nullptr || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 16 != 0))
     return ATTN_ERR_WORKSPACE;
   hipError_t e = dq_delta_stage(a);
@@ -455,9 +452,11 @@ int attn_bwd_ex(const attn_params *p, void *stream) {
   if (p == nullptr) return ATTN_ERR_NULL;
   const int H_kv = p->H_kv == 0 ? p->H : p->H_kv;
   const bool rope = p->rope_table != nullptr;
+  // a workspace, when given, lets grouped heads split their dK/dV step (as attn_bwd_gqa_ws)
   return bwd_all(rope ? p->q_rot : p->q, rope ? p->k_rot : p->k, p->v, p->o, p->dO, p->lse, p->dq, p->dk, p->dv,
                  p->delta, rope, p->rope_table, p->rope_npos, p->B, p->H, H_kv, p->S, p->D, p->scale, p->mask_mode,
-                 p->cu_seqlens, p->n_seqs, p->max_seqlen, p->dtype, p->out_dtype, p->strides, stream);
+                 p->cu_seqlens, p->n_seqs, p->max_seqlen, p->dtype, p->out_dtype, p->strides, stream,
+                 p->workspace != nullptr, p->workspace, p->workspace_bytes);
 }
 
 size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int D, int max_len) {

@@ -1238,9 +1238,11 @@ hipError_t launch_bwd_dkdv(const Args &a) {
 // where G >= 8: the in-workgroup splits serve smaller groups better (the
 // parts' partial sums cost as much HBM traffic as G / P more K/V heads).
 // P is the smallest divisor of G that brings the grid to 1024 units, else G.
-// 16-bit inputs, fp32 contiguous outputs, no RoPE; 0 where it does not apply.
+// 16-bit inputs (any output type, strides, RoPE: the parts are fp32 and
+// contiguous, dK turned back by RoPE in each part, which is linear); 0 where
+// it does not apply.
 int dkdv_parts(const Args &a) {
-  if (!a.half() || a.out16 || a.rope != nullptr) return 0;
+  if (!a.half()) return 0;
   const int G = a.H / a.H_kv;
   if (a.D == 128 ? G % 2 != 0 : G < 8) return 0;
   const int bn = a.D == 128 ? 64 : 128;  // keys per workgroup
@@ -1257,11 +1259,14 @@ size_t dkdv_workspace_bytes(const Args &a) {
   return P == 0 ? 0 : (size_t)P * 2 * a.B * a.H_kv * a.S * a.D * sizeof(float);
 }
 
-// out[i] = ws[0][i] + ws[1][i] + ... + ws[P-1][i], in that order, over the
-// n4 float4s of dK (parts 0 .. P-1 of the workspace) and then of dV (parts
-// P .. 2P-1).
-__global__ __launch_bounds__(256) void attn_bwd_sum_parts_kernel(const f32x4 *__restrict__ ws, f32x4 *__restrict__ dk,
-                                                                  f32x4 *__restrict__ dv, int P, int64_t n4) {
+// out = ws[0] + ws[1] + ... + ws[P-1], in that order, four elements per
+// thread: over the n4 float4s of dK (parts 0 .. P-1 of the workspace, each a
+// contiguous [B, H_kv, S, D] set) and then of dV (parts P .. 2P-1), stored in
+// the output type through the outputs' layouts.
+template <typename OT, int D>
+__global__ __launch_bounds__(256) void attn_bwd_sum_parts_kernel(const f32x4 *__restrict__ ws, OT *__restrict__ dk,
+                                                                  OT *__restrict__ dv, int P, int64_t n4, int S,
+                                                                  int Hkv, Layout ldk, Layout ldv) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= 2 * n4) return;
   const bool second = i >= n4;
@@ -1269,7 +1274,31 @@ __global__ __launch_bounds__(256) void attn_bwd_sum_parts_kernel(const f32x4 *__
   const f32x4 *src = ws + (second ? (int64_t)P * n4 : 0) + j;
   f32x4 acc = src[0];
   for (int p = 1; p < P; ++p) acc += src[(int64_t)p * n4];
-  (second ? dv : dk)[j] = acc;
+  const int64_t r = j / (D / 4);  // row of the [B, H_kv, S, D] tensor
+  const int col = (int)(j - r * (D / 4)) * 4;
+  const int s = (int)(r % S);
+  const int bh = (int)(r / S);
+  const Layout &l = second ? ldv : ldk;
+  const GBuf g((second ? dv : dk) + panel_off(l, bh / Hkv, bh % Hkv), panel_bytes(l, S, D, sizeof(OT)));
+  store_out4<OT>(g, acc, (uint32_t)s * (uint32_t)l.ss + (uint32_t)col);
+}
+
+template <typename OT, int D>
+static hipError_t launch_sum_parts(const Args &a, const float *ws, int P, int64_t n) {
+  const int64_t n4 = n / 4;
+  hipLaunchKernelGGL((attn_bwd_sum_parts_kernel<OT, D>), dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256), 0,
+                     a.stream, reinterpret_cast<const f32x4 *>(ws), static_cast<OT *>(a.dk), static_cast<OT *>(a.dv),
+                     P, n4, a.S, a.H_kv, a.ldk, a.ldv);
+  return hipGetLastError();
+}
+
+template <typename OT>
+static hipError_t launch_sum_parts_d(const Args &a, const float *ws, int P, int64_t n) {
+  switch (a.D) {
+    case 32: return launch_sum_parts<OT, 32>(a, ws, P, n);
+    case 64: return launch_sum_parts<OT, 64>(a, ws, P, n);
+    default: return launch_sum_parts<OT, 128>(a, ws, P, n);
+  }
 }
 
 hipError_t launch_bwd_dkdv_parts(const Args &a, float *ws) {
@@ -1295,11 +1324,8 @@ hipError_t launch_bwd_dkdv_parts(const Args &a, float *ws) {
            : (a.doc ? launch_dkdv_split<f16, float, 32, true, 1>(a, P, wk, wv, n)
                     : launch_dkdv_split<f16, float, 32, false, 1>(a, P, wk, wv, n));
   if (e != hipSuccess) return e;
-  const int64_t n4 = n / 4;
-  hipLaunchKernelGGL(attn_bwd_sum_parts_kernel, dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256), 0, a.stream,
-                     reinterpret_cast<const f32x4 *>(ws), static_cast<f32x4 *>(a.dk), static_cast<f32x4 *>(a.dv), P,
-                     n4);
-  return hipGetLastError();
+  if (!a.out16) return launch_sum_parts_d<float>(a, ws, P, n);
+  return bf ? launch_sum_parts_d<bf16>(a, ws, P, n) : launch_sum_parts_d<f16>(a, ws, P, n);
 }
 
 hipError_t launch_bwd_dq(const Args &a) {

@@ -197,11 +197,10 @@ int attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o,
  * and the call is exactly attn_bwd_gqa.
  * workspace: caller-owned DEVICE memory, 16-byte aligned, of at least that
  * many bytes. Its contents on return are unspecified. It must not overlap
- * the other arguments. The split also needs dk and dv 16-byte aligned (as
- * whole allocations are); otherwise the call runs as attn_bwd_gqa and does
- * not touch the workspace. Arguments and errors as attn_bwd_gqa, plus
+ * the other arguments. Arguments and errors as attn_bwd_gqa, plus
  * ATTN_ERR_WORKSPACE if the workspace is needed and is NULL, misaligned or
- * too small.
+ * too small. attn_bwd_ex takes the same workspace in attn_params (with any
+ * output type, strides and RoPE; the size is the same).
  */
 size_t attn_bwd_gqa_workspace_bytes(int B, int H, int H_kv, int S, int D, int mask_mode,
                                     int n_seqs, int max_seqlen, int dtype);
@@ -365,6 +364,12 @@ int attn_bwd_rope(const void *q_rot, const void *k_rot, const void *v, const flo
  *                 bytes; else ATTN_ERR_STRIDE.  Inputs may overlap (a zero
  *                 head stride broadcasts one head); outputs must not overlap
  *                 one another or the inputs (not checked).
+ *   workspace,    attn_bwd_ex only: NULL (no workspace), or a device
+ *   workspace_bytes  workspace as for attn_bwd_gqa_ws, of at least
+ *                 attn_bwd_gqa_workspace_bytes(B, H, H_kv, S, D, mask_mode,
+ *                 n_seqs, max_seqlen, dtype) bytes, with which grouped heads
+ *                 split their dK/dV step (ATTN_ERR_WORKSPACE if too small or
+ *                 misaligned).  attn_fwd_ex ignores both.
  *
  * Errors, ownership and stream rules as the entry points above; a NULL
  * params pointer returns ATTN_ERR_NULL.
@@ -385,6 +390,8 @@ typedef struct attn_params {
   int rope_npos;
   void *q_rot, *k_rot;
   int64_t strides[8][3];
+  void *workspace;
+  size_t workspace_bytes;
 } attn_params;
 
 enum {

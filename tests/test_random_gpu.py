@@ -87,12 +87,46 @@ def _view(t, strided):
     return v
 
 
+def _parts(c):
+    """The workspace split the library takes for this mix (0: none): 16-bit
+    inputs, a group G even at D = 128 or >= 8 below, fewer than 1024 dK/dV
+    workgroups (64 keys each at D = 128, 128 below); P the smallest divisor
+    of G that brings them to 1024, else G."""
+    G = c["H"] // c["H_kv"]
+    if c["dtype"] == "f32" or (G % 2 if c["D"] == 128 else G < 8):
+        return 0
+    bn = 64 if c["D"] == 128 else 128
+    if c["cu"] is not None:
+        units = (len(c["cu"]) - 1) * c["H_kv"] * -(-int(np.diff(c["cu"]).max()) // bn)
+    else:
+        units = c["B"] * c["H_kv"] * -(-c["S"] // bn)
+    if units >= 1024:
+        return 0
+    return next((p for p in range(2, G) if G % p == 0 and units * p >= 1024), G)
+
+
+# the mixes whose grouped heads split their dK/dV step when given a workspace
+WS_CASES = [c for c in CASES if _parts(c)]
+
+
 @pytest.mark.parametrize("case", CASES, ids=[f"c{c['id']}" for c in CASES])
 def test_random_option_mix(case):
+    _run_case(case, with_ws=False)
+
+
+@pytest.mark.parametrize("case", WS_CASES, ids=[f"c{c['id']}" for c in WS_CASES])
+def test_random_option_mix_with_workspace(case):
+    """The same mix through attn_bwd_ex with a (NaN-filled) workspace: the
+    grouped heads' dK/dV in parts, summed in order, stored in the output type
+    through the output strides, turned back by RoPE in each part."""
+    _run_case(case, with_ws=True)
+
+
+def _run_case(case, with_ws):
     import torch
     import causal_attention_amd as ca
     c = case
-    log(f"[random] {c}")
+    log(f"[random{' ws' if with_ws else ''}] {c}")
     rng = np.random.default_rng(c["seed"])
     B, H, H_kv, S, D = c["B"], c["H"], c["H_kv"], c["S"], c["D"]
     # float32 draws rounded to the input dtype: the oracle sees exactly the kernel's inputs
@@ -119,8 +153,15 @@ def test_random_option_mix(case):
         kw["rope_table"] = ca.rope_table(kw.get("max_seqlen", S), D)
         kw["q_rot"] = torch.empty((B, H, S, D), dtype=tdt, device="cuda")
         kw["k_rot"] = torch.empty((B, H_kv, S, D), dtype=tdt, device="cuda")
+    ws = None
+    if with_ws:
+        n_seqs = len(c["cu"]) - 1 if c["cu"] is not None else 0
+        n = ca.bwd_workspace_bytes(B, H, H_kv, S, D, tdt, mode, n_seqs, kw.get("max_seqlen", 0))
+        assert n == 2 * _parts(c) * B * H_kv * S * D * 4, n
+        ws = torch.full((n // 4,), nan, dtype=torch.float32, device="cuda")
     ca.attn_fwd_ex(q, k, v, out["o"], out["lse"], scale, **kw)
-    ca.attn_bwd_ex(q, k, v, out["o"], do, out["lse"], out["dq"], out["dk"], out["dv"], out["delta"], scale, **kw)
+    ca.attn_bwd_ex(q, k, v, out["o"], do, out["lse"], out["dq"], out["dk"], out["dv"], out["delta"], scale,
+                   workspace=ws, **kw)
     torch.cuda.synchronize()
     if c["rope"]:
         # the rotation against the oracle's (one rounding apart at most,
