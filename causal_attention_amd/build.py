@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libcausal_attn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_rope.hip"]
+SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_doc.hip", "attn_decode.hip", "attn_rope.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -36,11 +36,14 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
-# Per-source flags.  The backward kernels are scheduled with the compiler's
-# iterative ILP strategy: measured on MI355X (backward, bitwise equal
-# results) ctx 1024 96.3 -> 93.4 us, ctx 512 37.6 -> 36.0, 4 K/V heads at
-# S = 8192 1.47 -> 1.40 ms, packed documents 84.4 -> 85.8; on the forward it
-# made no difference.
+# Per-source flags.  The causal backward kernels are scheduled with the
+# compiler's iterative ILP strategy: measured on MI355X (backward, bitwise
+# equal results) ctx 1024 96.3 -> 93.4 us, ctx 512 37.6 -> 36.0, 4 K/V heads
+# at S = 8192 1.47 -> 1.40 ms, packed documents 84.4 -> 85.8; on the forward
+# it made no difference.  The packed-document instantiations
+# (attn_bwd_doc.hip) keep the default strategy: with the work-ranked
+# document schedule the iterative one crashes this compiler's register
+# allocator on one of them, and it did not help packed documents before.
 FILE_FLAGS = {
     "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }

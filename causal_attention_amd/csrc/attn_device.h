@@ -845,17 +845,111 @@ __device__ __forceinline__ RowTile causal_tile(int bid, int nblocks, int ntiles,
   return t;
 }
 
-// Packed-document mode: 1-D grid of ntiles * n_seqs * H blocks, ntiles the
-// tile count of the longest document; unit = head * n_seqs + document.  Tiles
-// past a document's end are invalid (the workgroup exits at once).
+// Packed documents.  The tiles of one head are ranked by work across all of
+// its documents: a document of L rows has n = ceil(L / BM) tiles (at most
+// ntiles, the tile count of max_seqlen), and its tiles have the classes 1..n,
+// class c doing about c tiles' worth of work: query tile c - 1 (work grows
+// with the tile index: keys from the document start to the diagonal) or key
+// tile n - c (work shrinks with it: query rows from the tile to the
+// document end).  Rank k is the k-th tile in the order (class descending,
+// then document index), so the snake deal above pairs the heaviest tiles of
+// the longest documents with the lightest tiles, whatever the mix of lengths.
+// A head has at most doc_rank_slots() tiles; the grid holds that many blocks
+// per unit, and ranks past the head's actual tile count exit at once.  The
+// ranking is recomputed by every wave from cu_seqlens (lane j holds documents
+// j, j + 64, ...), which bounds it to kDocRankMax documents and tiles per
+// document; larger launches keep the per-document grid.
+constexpr int kDocRankMax = 4 * kWaveSize;
+__host__ __device__ __forceinline__ bool doc_ranked(int n_seqs, int ntiles) {
+  return n_seqs <= kDocRankMax && ntiles <= kDocRankMax;
+}
+// Upper bound on one head's tiles: n_seqs * ntiles, and, since the documents
+// cover the S rows, sum ceil(L_d / BM) <= (S + n_seqs * (BM - 1)) / BM.
+__host__ __device__ __forceinline__ int doc_rank_slots(int n_seqs, int ntiles, int S, int BM) {
+  const int64_t a = (int64_t)n_seqs * ntiles;
+  const int64_t b = ((int64_t)S + (int64_t)n_seqs * (BM - 1)) / BM;
+  return (int)(a < b ? a : b);
+}
+// Blocks per unit in packed mode; `rank` is the kernel's choice of the
+// ranked schedule (and it applies where doc_ranked allows it).
+__host__ __device__ __forceinline__ int doc_blocks_per_unit(int n_seqs, int ntiles, int S, int BM, bool rank) {
+  return rank && doc_ranked(n_seqs, ntiles) ? doc_rank_slots(n_seqs, ntiles, S, BM) : n_seqs * ntiles;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int x) {
+#pragma unroll
+  for (int o = 1; o < kWaveSize; o <<= 1) x += __shfl_xor(x, o, kWaveSize);
+  return x;
+}
+
+// Rank k of one head -> document * 2^32 + class, or -1 when the head has k
+// tiles or fewer.  Wave-uniform inputs and result: the classes are scanned
+// from the top, each taking as many ranks as there are documents with that
+// many tiles or more (ballot counts; at most kDocRankMax classes).
+__device__ __forceinline__ int64_t doc_rank_item(const int32_t *__restrict__ cu, int n_seqs, int ntiles, int BM,
+                                                 int k) {
+  constexpr int J = kDocRankMax / kWaveSize;
+  const int lane = threadIdx.x % kWaveSize;
+  int nd[J];  // tiles of documents lane + 64 j
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int d = lane + kWaveSize * j;
+    nd[j] = d < n_seqs ? min((cu[d + 1] - cu[d] + BM - 1) / BM, ntiles) : 0;
+  }
+  for (int c = ntiles; c >= 1; --c) {
+    uint64_t m[J];
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      m[j] = __ballot(nd[j] >= c);
+      cnt += __popcll(m[j]);
+    }
+    if (k < cnt) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int cj = __popcll(m[j]);
+        if (k < cj) {
+          uint64_t x = m[j];
+          for (int r = 0; r < k; ++r) x &= x - 1;
+          return (int64_t)(kWaveSize * j + __builtin_ctzll(x)) << 32 | c;
+        }
+        k -= cj;
+      }
+    }
+    k -= cnt;
+  }
+  return -1;
+}
+
+// Packed-document mode.  Ranked (doc_ranked): 1-D grid of units *
+// doc_rank_slots() blocks; unit = head.  Otherwise: units * n_seqs * ntiles
+// blocks, unit = head * n_seqs + document, tiles past a document's end exit
+// at once.  heavy_first as for causal_tile.
 __device__ __forceinline__ RowTile doc_tile(const int32_t *__restrict__ cu, int bid, int nblocks, int ntiles,
-                                            int n_seqs, int BM, bool heavy_first) {
+                                            int n_seqs, int BM, int S, bool heavy_first, bool rank) {
+  RowTile t;
+  if (rank && doc_ranked(n_seqs, ntiles)) {
+    const TileSlot sl = snake_slot(bid, nblocks, doc_rank_slots(n_seqs, ntiles, S, BM));
+    const int64_t item = doc_rank_item(cu, n_seqs, ntiles, BM, sl.rank);
+    t.valid = item >= 0;
+    if (!t.valid) return t;
+    const int doc = __builtin_amdgcn_readfirstlane((int)(item >> 32));
+    const int cls = __builtin_amdgcn_readfirstlane((int)item);
+    const int ds = cu[doc];
+    const int de = cu[doc + 1];
+    const int ti = heavy_first ? cls - 1 : min((de - ds + BM - 1) / BM, ntiles) - cls;
+    t.head = sl.unit;
+    t.r_start = ds + ti * BM;
+    t.r_end = min(t.r_start + BM, de);
+    t.seg_start = ds;
+    t.seg_end = de;
+    return t;
+  }
   const TileSlot sl = snake_slot(bid, nblocks, ntiles);
   const int doc = sl.unit % n_seqs;
   const int ds = cu[doc];
   const int de = cu[doc + 1];
   const int ti = heavy_first ? ntiles - 1 - sl.rank : sl.rank;
-  RowTile t;
   t.head = sl.unit / n_seqs;
   t.r_start = ds + ti * BM;
   t.r_end = min(t.r_start + BM, de);

@@ -76,6 +76,12 @@ int dkdv_parts(const Args &a);
 size_t dkdv_workspace_bytes(const Args &a);
 hipError_t launch_bwd_dkdv_parts(const Args &a, float *ws);
 hipError_t launch_bwd_dq(const Args &a);
+// Packed-document launches (attn_bwd_doc.hip): launch_bwd_dkdv,
+// launch_bwd_dq / launch_bwd_dq_delta (fuse_delta) and the parts step of
+// launch_bwd_dkdv_parts (P parts into wk, wv, n elements each), for a.doc.
+hipError_t launch_bwd_dkdv_doc(const Args &a);
+hipError_t launch_bwd_dq_doc(const Args &a, bool fuse_delta);
+hipError_t launch_bwd_dkdv_parts_doc(const Args &a, int P, float *wk, float *wv, int64_t n);
 // 16-bit inputs only: dQ that also computes Delta from O and dO (written to a.delta)
 hipError_t launch_bwd_dq_delta(const Args &a);
 // RoPE: the cos/sin table, and the rotation of a.q, a.k into q_rot, k_rot (table a.rope)
