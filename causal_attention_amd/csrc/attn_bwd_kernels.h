@@ -32,8 +32,8 @@ namespace attn {
 // Packed documents: the work-ranked schedule (attn_device.h, doc_tile) for
 // dK/dV's key tiles.  dQ keeps the per-document grid: measured on MI355X
 // (B1 H16, 8,192 tokens in documents of 32-1024, same-process A/B, backward
-// median) the ranked dK/dV took 85.2 -> 83.2 us, and ranking dQ as well made
-// it 88.5 (with either scheduling strategy).
+// median) the ranked dK/dV took 85.2 -> 83.2 us; ranking dQ as well made it
+// 88.5 with 64-key dQ tiles and gained nothing with 32-key ones.
 constexpr bool kRankDocsDq = false;
 constexpr bool kRankDocsDkdv = true;
 
@@ -1041,12 +1041,15 @@ template <typename T, int D> struct BwdCfg {
   static constexpr int MINB_DQ = 1;
   // dQ key tile: 32 keys leave the bf16 kernel enough registers for more
   // waves per SIMD (D = 64: 124 VGPRs, four; D = 128: two instead of one),
-  // measured 9 % (context 1024) and 26 % (S = 8192, D = 128) faster; packed
-  // documents at D <= 64 ran 12 % faster with 64, and a 32-row tile at D = 32
-  // is too small to split over four waves.
+  // measured 9 % (context 1024) and 26 % (S = 8192, D = 128) faster.  Packed
+  // documents at D = 64 had run 12 % faster with 64 under the per-document
+  // grid of every kernel; with the forward and dK/dV on the ranked schedule
+  // 32 is 2 % faster there (same-process A/B, backward 83.1 -> 81.6 us,
+  // bitwise equal: the key blocks are accumulated in the same order).  A
+  // 32-row tile at D = 32 is too small to split over four waves.
   template <bool DOC>
   static constexpr int dq_bn() {
-    return (sizeof(T) == 2 && D > 32 && !(DOC && D <= 64)) ? 32 : BN;
+    return (sizeof(T) == 2 && D > 32) ? 32 : BN;
   }
 };
 
