@@ -62,6 +62,25 @@ def test_more_than_256_documents_bitwise(dtype, D):
     _same(ranked, run_hip(y), f"{dtype} D{D}")
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("f32", 64)])
+def test_256_documents_bitwise(dtype, D):
+    """Exactly 256 documents (the ranked limit: every lane of the rank scan
+    holds four documents, so documents 64-255 exercise its later chunks),
+    some of them empty and a few of several tiles, against the same rows with
+    one more empty document (257: per-document grid)."""
+    lens = np.random.default_rng(256).integers(0, 24, 256)
+    lens[[3, 64, 130, 200, 255]] = 0
+    lens[[70, 150, 190, 250]] = [300, 140, 260, 129]  # several tiles, in the later chunks
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    log(f"[schedule] 256 documents ({int(cu[-1])} tokens) vs 257, {dtype} D={D}")
+    x = _inputs(dtype, D, cu, H=2, seed=9)
+    ranked = run_hip(x)
+    compare(ranked, oracle(x), dtype, tag=f"256 docs {dtype} D{D}")
+    y = dict(x)
+    y["cu_seqlens"] = np.concatenate([cu, [cu[-1]]]).astype(np.int32)
+    _same(ranked, run_hip(y), f"256 docs {dtype} D{D}")
+
+
 @pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128)])
 def test_max_seqlen_past_rank_limit_bitwise(dtype, D):
     """33,000 tokens in documents of at most 1,500: max_seqlen = the longest
