@@ -236,6 +236,7 @@ int bwd_all(const void *q, const void *k, const void *v, const void *o, const vo
   const size_t need = with_ws ? attn::dkdv_workspace_bytes(a) : 0;
   if (need > 0 && (ws == nullptr || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 16 != 0))
     return ATTN_ERR_WORKSPACE;
+  if (need == 0 && attn::bwd_small_applies(a)) return to_status(attn::launch_bwd_small(a));
   hipError_t e = dq_delta_stage(a);
   if (e == hipSuccess) e = need > 0 ? attn::launch_bwd_dkdv_parts(a, static_cast<float *>(ws)) : attn::launch_bwd_dkdv(a);
   return to_status(e);

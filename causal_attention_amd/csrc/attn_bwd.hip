@@ -128,6 +128,32 @@ hipError_t launch_bwd_dkdv_parts(const Args &a, float *ws) {
   return bf ? launch_sum_parts_d<bf16>(a, ws, P, n) : launch_sum_parts_d<f16>(a, ws, P, n);
 }
 
+// Small causal grids (attn_bwd_small_kernel): the grids of fewer than 768
+// workgroups on which dQ takes its 64-key tiles (launch_dq_t).
+bool bwd_small_applies(const Args &a) {
+  return a.half() && a.D == 64 && !a.doc && a.H_kv == a.H && (int64_t)a.B * a.H * ((a.S + 127) / 128) < 768;
+}
+
+template <typename T, typename OT>
+static hipError_t launch_bwd_small_t(const Args &a) {
+  const int ntiles = (a.S + 127) / 128;  // 128 keys per dK/dV workgroup, 128 queries per dQ workgroup
+  const int n = a.B * a.H * ntiles;
+  hipLaunchKernelGGL((attn_bwd_small_kernel<T, OT>), dim3(2 * n), dim3(256), 0, a.stream, static_cast<const T *>(a.q),
+                     static_cast<const T *>(a.k), static_cast<const T *>(a.v), static_cast<const T *>(a.dO),
+                     a.lse_in, a.delta_in, static_cast<OT *>(a.dq), static_cast<OT *>(a.dk), static_cast<OT *>(a.dv),
+                     a.S, a.scale * kLog2e, a.scale, ntiles, a.H, a.rope, a.rope_npos, a.lq, a.lk, a.lv, a.ldo,
+                     a.ldq, a.ldk, a.ldv, n);
+  return hipGetLastError();
+}
+
+// Delta by the preprocess kernel, then attn_bwd_small_kernel.
+hipError_t launch_bwd_small(const Args &a) {
+  hipError_t e = launch_bwd_preprocess(a);
+  if (e != hipSuccess) return e;
+  if (a.dtype == 1) return a.out16 ? launch_bwd_small_t<bf16, bf16>(a) : launch_bwd_small_t<bf16, float>(a);
+  return a.out16 ? launch_bwd_small_t<f16, f16>(a) : launch_bwd_small_t<f16, float>(a);
+}
+
 hipError_t launch_bwd_dq(const Args &a) {
   switch (a.dtype) {
     case 1: return a.out16 ? launch_dq_dt<bf16, bf16, false>(a) : launch_dq_dt<bf16, float, false>(a);

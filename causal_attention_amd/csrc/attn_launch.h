@@ -76,6 +76,10 @@ int dkdv_parts(const Args &a);
 size_t dkdv_workspace_bytes(const Args &a);
 hipError_t launch_bwd_dkdv_parts(const Args &a, float *ws);
 hipError_t launch_bwd_dq(const Args &a);
+// Small causal grids at D = 64 (16-bit inputs, H_kv == H): whether the
+// one-launch backward applies, and the backward itself (Delta, dK/dV, dQ).
+bool bwd_small_applies(const Args &a);
+hipError_t launch_bwd_small(const Args &a);
 // Packed-document launches (attn_bwd_doc.hip): launch_bwd_dkdv,
 // launch_bwd_dq / launch_bwd_dq_delta (fuse_delta) and the parts step of
 // launch_bwd_dkdv_parts (P parts into wk, wv, n elements each), for a.doc.
